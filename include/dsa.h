@@ -1,0 +1,183 @@
+/*
+ * dsa.h -- C ABI of libdsa, the MI355X (gfx950) DeepSeek-style sparse attention
+ * (DSA) hot path of the GLM-5 decoder:
+ *
+ *   1. a lightning indexer scores every earlier token of each query,
+ *   2. an exact top-k keeps the best k tokens (all of them below k tokens),
+ *   3. absorbed MLA attention runs over the compressed latent rows of only the
+ *      kept tokens.
+ *
+ * The operations are the ones the page "GLM on an A100, in Vx" defines in its
+ * section "The model" (latent K/V per token, an indexer that scores every
+ * earlier token, the best 2,048 kept, everything kept below 2,048 tokens) and in
+ * "How do we know it is right?" (ReLU per indexer head before the heads are
+ * combined; ties broken as a stable argsort of -scores).  The page
+ * "Self-contained GLM-5 serving stack" names the pieces (absorbed MLA decode,
+ * compressed request-local KV, full DSA indexer selection, fused GPU index-score
+ * kernel, split online-softmax compressed MLA).
+ *
+ * Conventions for every entry point:
+ *   - All array arguments are DEVICE pointers to caller-owned memory, except the
+ *     dsa_cache descriptor structs themselves, which live in host memory and
+ *     are read during the call only.  The library allocates nothing, frees
+ *     nothing and keeps no state between calls.
+ *   - Work is enqueued on `stream` (a hipStream_t; NULL is the null stream) and
+ *     the call returns after enqueue: no host<->device copies, no device reads
+ *     on the host, no synchronization.  Producers on other streams must be
+ *     ordered before the call by the caller (events).
+ *   - Arguments are validated on the host before any HIP call.  Sizes of 0 queries
+ *     return DSA_OK with no work.  Negative sizes, NULL required pointers, k < 1
+ *     or inconsistent strides return DSA_ERR_INVALID_ARGUMENT; shapes or dtypes
+ *     outside the supported set return DSA_ERR_UNSUPPORTED (there is no fallback
+ *     path); a workspace smaller than the matching *_workspace_size() returns
+ *     DSA_ERR_WORKSPACE_TOO_SMALL; a failed launch returns DSA_ERR_DEVICE.
+ *   - Values that live on the device (lengths, block tables, indices) are
+ *     trusted: an out-of-range value is undefined behaviour.
+ *   - Workspaces must be zero-filled before their first use (for example with
+ *     dsa_workspace_clear) and are left zero-filled in their control words by every
+ *     call, so one workspace can serve any number of consecutive calls on one
+ *     stream.  Calls that share a workspace must not overlap in time.
+ *   - Results are deterministic: the same inputs give the same bits on every run.
+ */
+#ifndef DSA_H_
+#define DSA_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  DSA_OK = 0,
+  DSA_ERR_INVALID_ARGUMENT = 1,
+  DSA_ERR_UNSUPPORTED = 2,
+  DSA_ERR_WORKSPACE_TOO_SMALL = 3,
+  DSA_ERR_DEVICE = 4
+} dsa_status;
+
+typedef enum {
+  DSA_F32 = 0,        /* IEEE binary32 */
+  DSA_BF16 = 1,       /* bfloat16, raw 16-bit patterns */
+  DSA_FP8_E4M3FN = 2  /* OCP float8 e4m3fn bytes (bias 7, no infinity, 0x7F/0xFF NaN) */
+} dsa_dtype;
+
+/*
+ * A per-token row cache in device memory ("compressed request-local KV").
+ * Token t of sequence b is stored at
+ *     rows + p * block_stride + (t % block_size) * row_stride          (bytes)
+ * where p = block_table ? block_table[b * max_blocks + t / block_size] : b.
+ *   - Contiguous caches: block_table = NULL and block_size = the capacity (rows
+ *     per sequence); p is then the sequence index.
+ *   - Paged caches: block_table is an int32 device array [batch][max_blocks]
+ *     and block_size a multiple of 32 (64 in the GLM-5 layout).  The key and
+ *     latent caches may share one table.
+ *   - fp8 rows carry one float32 scale per token (the dequantized value is
+ *     e4m3fn(byte) * scale), at scale[p * scale_block_stride + t % block_size];
+ *     scale is ignored for other dtypes.
+ *   - rows, row_stride and block_stride must be multiples of 16 bytes, and
+ *     row_stride >= width * element size.
+ */
+typedef struct {
+  const void *rows;
+  const float *scale;
+  int64_t row_stride;          /* bytes between consecutive tokens of a block */
+  int64_t block_stride;        /* bytes between blocks (or sequences) */
+  int64_t scale_block_stride;  /* floats between blocks of scales (fp8 only) */
+  const int32_t *block_table;  /* NULL: contiguous */
+  int32_t block_size;          /* tokens per block; contiguous: capacity */
+  int32_t max_blocks;          /* row length of block_table (paged only) */
+  int32_t width;               /* elements per row */
+  dsa_dtype dtype;
+} dsa_cache;
+
+/* dsa_topk flags */
+#define DSA_TOPK_ORDER_INDEX 0u  /* kept indices in ascending token order (the default) */
+
+/*
+ * Lightning-indexer scores.  For query i of sequence seq = q_seq ? q_seq[i] : 0
+ * that sees n = q_len[i] tokens (its own included), for every token s < n:
+ *     scores[i * ld_scores + s] = sum_h w[i * n_heads + h] * max(0, sum_d q[i][h][d] * khat[s][d])
+ * with khat = the key row (fp8: e4m3fn(byte) * scale[s]).  One key row of
+ * width keys->width is shared by all indexer heads.  Entries s >= n are not
+ * written.  Accumulation is float32.
+ *   q       [n_q][n_heads][keys->width], dtype q_dtype
+ *   w       [n_q][n_heads] float32 (any sign)
+ *   q_len   [n_q] int32, 0 <= q_len[i] <= max_len (device)
+ *   q_seq   [n_q] int32 or NULL (all queries in sequence 0)
+ * Supported: q f32 with f32 keys, or q bf16 with bf16 or fp8 keys;
+ *   width 32..128 in steps of 32 (bf16/fp8 keys: 64 or 128); 1 <= n_heads <= 64;
+ *   ld_scores >= max_len.
+ */
+dsa_status dsa_index_scores(float *scores, int64_t ld_scores, const void *q, dsa_dtype q_dtype, const float *w,
+                            const dsa_cache *keys, const int32_t *q_seq, const int32_t *q_len, int32_t n_q,
+                            int32_t n_heads, int32_t max_len, void *stream);
+
+/*
+ * Exact top-k.  For query i with n = q_len[i], keeps the first min(k, n)
+ * entries of a stable descending sort of scores[i * ld_scores + s], s < n:
+ * ties go to the lower token index, -0.0 equals +0.0, NaN ranks below every
+ * number.  indices [n_q][k] int32 receive the kept token indices in ascending
+ * order followed by -1 padding; counts [n_q] (nullable) receive min(k, n).
+ * Selection is integer-only on an order-preserving 32-bit image of each score,
+ * so the result is exact and deterministic.
+ * Supported: 1 <= k <= 2048, 1 <= max_len <= 262144, flags = DSA_TOPK_ORDER_INDEX.
+ */
+dsa_status dsa_topk(int32_t *indices, int32_t *counts, const float *scores, int64_t ld_scores,
+                    const int32_t *q_len, int32_t n_q, int32_t k, int32_t max_len, uint32_t flags,
+                    void *workspace, size_t workspace_bytes, void *stream);
+size_t dsa_topk_workspace_size(int32_t n_q, int32_t k, int32_t max_len);
+
+/*
+ * Sparse absorbed-MLA attention over kept latent rows.  For query i (sequence
+ * q_seq ? q_seq[i] : 0) and head h, over the slots j with indices[i * k + j] >= 0:
+ *     z_j = softmax_scale * sum_{c < W} q[i][h][c] * row_j[c]      (W = latent->width)
+ *     out[i][h][c] = sum_j softmax(z)_j * row_j[c],  c < kv_lora
+ *     lse[i][h]    = ln sum_j exp(z_j)
+ * The key is the whole latent row (kv_lora latent + rope), the value its
+ * first kv_lora entries.  No kept slot: out = 0, lse = -inf.
+ *   q       [n_q][n_heads][W], dtype q_dtype (same as latent->dtype)
+ *   out     [n_q][n_heads][kv_lora] float32;  lse [n_q][n_heads] float32 (nullable)
+ * Supported: bf16 with W = 576, kv_lora = 512, n_heads a multiple of 16 up to 128;
+ *   f32 with W <= 1024 a multiple of 4, kv_lora <= W a multiple of 4, n_heads <= 128;
+ *   1 <= k <= 2048.
+ */
+dsa_status mla_sparse_attend(float *out, float *lse, const void *q, dsa_dtype q_dtype, const dsa_cache *latent,
+                             int32_t kv_lora, const int32_t *indices, int32_t k, const int32_t *q_seq, int32_t n_q,
+                             int32_t n_heads, float softmax_scale, void *workspace, size_t workspace_bytes,
+                             void *stream);
+size_t mla_sparse_attend_workspace_size(int32_t n_q, int32_t n_heads, int32_t kv_lora, int32_t k);
+
+/*
+ * One fused DSA decode step for `batch` sequences: sequence b has seq_len[b]
+ * tokens and its newest token's query sees all of them.  Runs the indexer
+ * (scores), the exact top-k (ascending index order) and sparse MLA attention,
+ * stream-ordered, with the same definitions as the three calls above.
+ *   q_idx [batch][idx_heads][keys->width], w_idx [batch][idx_heads]
+ *   q_mla [batch][mla_heads][latent->width]
+ *   out [batch][mla_heads][kv_lora], lse [batch][mla_heads] (nullable)
+ *   scores_out [batch][max_len] float32 and indices_out [batch][k] int32 are
+ *   optional (NULL) copies of the intermediate scores and kept indices.
+ * Supported: the union of the constraints of the three calls.
+ */
+dsa_status dsa_decode_step(float *out, float *lse, const void *q_idx, dsa_dtype q_idx_dtype, const float *w_idx,
+                           const dsa_cache *keys, int32_t idx_heads, const void *q_mla, dsa_dtype q_mla_dtype,
+                           const dsa_cache *latent, int32_t kv_lora, int32_t mla_heads, const int32_t *seq_len,
+                           int32_t batch, int32_t max_len, int32_t k, float softmax_scale, float *scores_out,
+                           int32_t *indices_out, void *workspace, size_t workspace_bytes, void *stream);
+size_t dsa_decode_step_workspace_size(int32_t batch, int32_t max_len, int32_t k, int32_t mla_heads,
+                                      int32_t kv_lora);
+
+/* Zero-fill a workspace on `stream` with a fill kernel (no hipMemset node, so it
+ * may be captured in a graph).  bytes must be a multiple of 4. */
+dsa_status dsa_workspace_clear(void *workspace, size_t bytes, void *stream);
+
+/* Static description of a status code. */
+const char *dsa_status_string(dsa_status s);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* DSA_H_ */

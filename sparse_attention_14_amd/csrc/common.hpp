@@ -1,0 +1,128 @@
+// Device-side building blocks shared by the libdsa kernels (gfx950, wave64).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace dsa {
+
+typedef __attribute__((__vector_size__(8 * sizeof(__bf16)))) __bf16 bf16x8;
+typedef __attribute__((__vector_size__(2 * sizeof(__bf16)))) __bf16 bf16x2;
+typedef __attribute__((__vector_size__(4 * sizeof(float)))) float f32x4;
+typedef __attribute__((__vector_size__(16 * sizeof(float)))) float f32x16;
+typedef __attribute__((__vector_size__(4 * sizeof(uint32_t)))) uint32_t u32x4;
+
+constexpr int kWave = 64;
+constexpr int kHistBins = 4096;     // first radix level: top 12 bits of the ordered key
+constexpr int kHistShift = 20;
+
+// Cache descriptor as the kernels see it (mirrors dsa_cache; all byte strides).
+struct CacheDev {
+  const uint8_t *rows;
+  const float *scale;
+  int64_t row_stride;
+  int64_t block_stride;
+  int64_t scale_block_stride;
+  const int32_t *table;
+  int32_t block_size;
+  int32_t max_blocks;
+  int32_t width;
+};
+
+// Sequence of query qi: from q_seq, else qi itself (ident) or 0.
+__device__ __forceinline__ int seq_of(const int32_t *q_seq, int qi, int ident) {
+  return q_seq ? q_seq[qi] : (ident ? qi : 0);
+}
+
+// Physical block of token t of sequence seq and the token's slot inside it.
+__device__ __forceinline__ int64_t cache_block(const CacheDev &c, int seq, int t, int &slot) {
+  const int blk = t / c.block_size;
+  slot = t - blk * c.block_size;
+  return c.table ? (int64_t)c.table[(int64_t)seq * c.max_blocks + blk] : (int64_t)seq;
+}
+
+__device__ __forceinline__ const uint8_t *cache_row(const CacheDev &c, int64_t block, int slot) {
+  return c.rows + block * c.block_stride + (int64_t)slot * c.row_stride;
+}
+
+// Order-preserving 32-bit image of a float score: a > b as numbers <=> key(a) > key(b);
+// -0.0 and +0.0 share one key, every NaN maps to 0, below -inf (whose key is 0x007FFFFF).
+__device__ __forceinline__ uint32_t order_key(float f) {
+  uint32_t u = __float_as_uint(f);
+  if ((u & 0x7FFFFFFFu) == 0u) u = 0u;
+  if ((u & 0x7FFFFFFFu) > 0x7F800000u) return 0u;
+  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+
+// Two e4m3fn bytes (bits [15:0] or [31:16] of w) -> two bf16, exact: every
+// e4m3fn value, subnormals included, is representable in bf16.
+template <bool HI>
+__device__ __forceinline__ bf16x2 fp8x2_to_bf16x2(uint32_t w) {
+  return __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, HI);
+}
+
+// 8 e4m3fn bytes (two dwords) -> 8 bf16 MFMA operand elements in memory order.
+__device__ __forceinline__ bf16x8 fp8x8_to_bf16x8(uint32_t w0, uint32_t w1) {
+  bf16x2 a = fp8x2_to_bf16x2<false>(w0), b = fp8x2_to_bf16x2<true>(w0);
+  bf16x2 c = fp8x2_to_bf16x2<false>(w1), d = fp8x2_to_bf16x2<true>(w1);
+  bf16x8 r;
+  r[0] = a[0]; r[1] = a[1]; r[2] = b[0]; r[3] = b[1];
+  r[4] = c[0]; r[5] = c[1]; r[6] = d[0]; r[7] = d[1];
+  return r;
+}
+
+__device__ __forceinline__ float bf16_bits_to_float(uint16_t b) { return __uint_as_float((uint32_t)b << 16); }
+
+// Round-to-nearest-even float -> bf16 bits (finite inputs).
+__device__ __forceinline__ uint16_t float_to_bf16_bits(float f) {
+  uint32_t u = __float_as_uint(f);
+  u += 0x7FFFu + ((u >> 16) & 1u);
+  return (uint16_t)(u >> 16);
+}
+
+__device__ __forceinline__ bf16x8 as_bf16x8(u32x4 v) { return __builtin_bit_cast(bf16x8, v); }
+
+// 16-byte global load (the address must be 16-byte aligned).
+__device__ __forceinline__ u32x4 load16(const void *p) { return *reinterpret_cast<const u32x4 *>(p); }
+__device__ __forceinline__ u32x4 load16_nt(const void *p) {
+  return __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(p));
+}
+
+// Agent-scope release/acquire around the "last workgroup finishes" handshake.
+__device__ __forceinline__ void fence_release_agent() { __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent"); }
+__device__ __forceinline__ void fence_acquire_agent() { __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent"); }
+
+__device__ __forceinline__ uint32_t atomic_add_agent(uint32_t *p, uint32_t v) {
+  return __hip_atomic_fetch_add(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// Block-wide exclusive prefix sum of one uint32 per thread, in thread order.
+// scratch: >= blockDim.x / 64 + 1 words of LDS.  Returns the exclusive prefix;
+// *total receives the block sum.  All threads must call it.
+__device__ __forceinline__ uint32_t block_exclusive_scan(uint32_t v, uint32_t *scratch, uint32_t *total) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, nwaves = (blockDim.x + 63) >> 6;
+  uint32_t x = v;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    uint32_t y = __shfl_up(x, o, 64);
+    if (lane >= o) x += y;
+  }
+  if (lane == 63) scratch[wave] = x;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    uint32_t run = 0;
+    for (int i = 0; i < nwaves; ++i) {
+      uint32_t t = scratch[i];
+      scratch[i] = run;
+      run += t;
+    }
+    scratch[nwaves] = run;
+  }
+  __syncthreads();
+  uint32_t r = x - v + scratch[wave];
+  *total = scratch[nwaves];
+  __syncthreads();
+  return r;
+}
+
+}  // namespace dsa

@@ -1,0 +1,236 @@
+// C ABI of libdsa: host-side validation, workspace carving and launches.
+// Every check runs on the host before any HIP call; see include/dsa.h for the
+// contract of each entry point.
+#include "../../include/dsa.h"
+#include "kernels.hpp"
+
+using namespace dsa;
+
+namespace {
+
+constexpr int kMaxTopk = 2048;
+constexpr int kMaxLenTopk = 262144;
+
+int elem_bytes(dsa_dtype d) { return d == DSA_F32 ? 4 : (d == DSA_BF16 ? 2 : 1); }
+
+bool valid_dtype(int d) { return d == DSA_F32 || d == DSA_BF16 || d == DSA_FP8_E4M3FN; }
+
+bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+// Structural checks of a cache descriptor (no device reads).
+dsa_status check_cache(const dsa_cache *c) {
+  if (!c || !c->rows) return DSA_ERR_INVALID_ARGUMENT;
+  if (!valid_dtype(c->dtype)) return DSA_ERR_INVALID_ARGUMENT;
+  if (c->width <= 0 || c->block_size <= 0 || c->row_stride <= 0 || c->block_stride <= 0)
+    return DSA_ERR_INVALID_ARGUMENT;
+  if (c->row_stride < (int64_t)c->width * elem_bytes(c->dtype)) return DSA_ERR_INVALID_ARGUMENT;
+  if (c->block_stride < (int64_t)c->block_size * c->row_stride) return DSA_ERR_INVALID_ARGUMENT;
+  if (c->block_table && c->max_blocks <= 0) return DSA_ERR_INVALID_ARGUMENT;
+  if (c->dtype == DSA_FP8_E4M3FN && (!c->scale || c->scale_block_stride < c->block_size))
+    return DSA_ERR_INVALID_ARGUMENT;
+  if (!aligned16(c->rows) || (c->row_stride & 15) || (c->block_stride & 15)) return DSA_ERR_UNSUPPORTED;
+  if (c->block_table && (c->block_size & 31)) return DSA_ERR_UNSUPPORTED;
+  return DSA_OK;
+}
+
+CacheDev to_dev(const dsa_cache *c) {
+  CacheDev d{};
+  d.rows = static_cast<const uint8_t *>(c->rows);
+  d.scale = c->scale;
+  d.row_stride = c->row_stride;
+  d.block_stride = c->block_stride;
+  d.scale_block_stride = c->scale_block_stride;
+  d.table = c->block_table;
+  d.block_size = c->block_size;
+  d.max_blocks = c->max_blocks;
+  d.width = c->width;
+  return d;
+}
+
+dsa_status check_scores(const void *q, dsa_dtype q_dtype, const float *w, const dsa_cache *keys, int32_t n_heads) {
+  if (!q || !w) return DSA_ERR_INVALID_ARGUMENT;
+  if (!valid_dtype(q_dtype)) return DSA_ERR_INVALID_ARGUMENT;
+  dsa_status s = check_cache(keys);
+  if (s != DSA_OK) return s;
+  if (n_heads <= 0) return DSA_ERR_INVALID_ARGUMENT;
+  if (n_heads > 64) return DSA_ERR_UNSUPPORTED;
+  const int D = keys->width;
+  if (q_dtype == DSA_F32) {
+    if (keys->dtype != DSA_F32) return DSA_ERR_UNSUPPORTED;
+    if (D != 32 && D != 64 && D != 96 && D != 128) return DSA_ERR_UNSUPPORTED;
+  } else if (q_dtype == DSA_BF16) {
+    if (keys->dtype != DSA_BF16 && keys->dtype != DSA_FP8_E4M3FN) return DSA_ERR_UNSUPPORTED;
+    if (D != 64 && D != 128) return DSA_ERR_UNSUPPORTED;
+  } else {
+    return DSA_ERR_UNSUPPORTED;
+  }
+  if (!aligned16(q)) return DSA_ERR_UNSUPPORTED;
+  return DSA_OK;
+}
+
+dsa_status check_attend(const void *q, dsa_dtype q_dtype, const dsa_cache *latent, int32_t kv_lora, int32_t n_heads) {
+  if (!q) return DSA_ERR_INVALID_ARGUMENT;
+  if (!valid_dtype(q_dtype)) return DSA_ERR_INVALID_ARGUMENT;
+  dsa_status s = check_cache(latent);
+  if (s != DSA_OK) return s;
+  if (n_heads <= 0 || kv_lora <= 0 || kv_lora > latent->width) return DSA_ERR_INVALID_ARGUMENT;
+  if (q_dtype != latent->dtype) return DSA_ERR_UNSUPPORTED;
+  if (q_dtype == DSA_BF16) {
+    if (latent->width != 576 || kv_lora != 512 || (n_heads % 16) || n_heads > 128) return DSA_ERR_UNSUPPORTED;
+  } else if (q_dtype == DSA_F32) {
+    if (latent->width > 1024 || (latent->width & 3) || (kv_lora & 3) || n_heads > 128) return DSA_ERR_UNSUPPORTED;
+  } else {
+    return DSA_ERR_UNSUPPORTED;
+  }
+  if (!aligned16(q)) return DSA_ERR_UNSUPPORTED;
+  return DSA_OK;
+}
+
+dsa_status from_hip(hipError_t e) { return e == hipSuccess ? DSA_OK : DSA_ERR_DEVICE; }
+
+size_t round256(size_t b) { return (b + 255) / 256 * 256; }
+
+// Decode-step workspace: [scores][indices][topk][attend].
+struct StepLayout {
+  int64_t ld;
+  size_t off_scores, off_idx, off_topk, off_att, total;
+  TopkPlan tp;
+  AttendPlan ap;
+};
+
+StepLayout step_layout(int32_t batch, int32_t max_len, int32_t k, int32_t mla_heads, int32_t kv_lora,
+                       int latent_dt, int width) {
+  StepLayout L{};
+  L.ld = ((int64_t)max_len + 63) / 64 * 64;
+  L.tp = plan_topk(batch, k, max_len);
+  L.ap = plan_attend(batch, mla_heads, kv_lora, width, k, latent_dt);
+  size_t off = 0;
+  L.off_scores = off;
+  off += round256((size_t)batch * L.ld * 4);
+  L.off_idx = off;
+  off += round256((size_t)batch * k * 4);
+  L.off_topk = off;
+  off += round256(L.tp.total);
+  L.off_att = off;
+  off += round256(L.ap.total);
+  L.total = off;
+  return L;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char *dsa_status_string(dsa_status s) {
+  switch (s) {
+    case DSA_OK: return "ok";
+    case DSA_ERR_INVALID_ARGUMENT: return "invalid argument";
+    case DSA_ERR_UNSUPPORTED: return "unsupported shape or dtype";
+    case DSA_ERR_WORKSPACE_TOO_SMALL: return "workspace too small";
+    case DSA_ERR_DEVICE: return "device error";
+  }
+  return "unknown status";
+}
+
+dsa_status dsa_workspace_clear(void *workspace, size_t bytes, void *stream) {
+  if (bytes == 0) return DSA_OK;
+  if (!workspace || (bytes & 3)) return DSA_ERR_INVALID_ARGUMENT;
+  return from_hip(launch_fill_zero(static_cast<uint32_t *>(workspace), bytes / 4, static_cast<hipStream_t>(stream)));
+}
+
+dsa_status dsa_index_scores(float *scores, int64_t ld_scores, const void *q, dsa_dtype q_dtype, const float *w,
+                            const dsa_cache *keys, const int32_t *q_seq, const int32_t *q_len, int32_t n_q,
+                            int32_t n_heads, int32_t max_len, void *stream) {
+  if (n_q < 0 || max_len < 0) return DSA_ERR_INVALID_ARGUMENT;
+  if (n_q == 0) return DSA_OK;
+  if (!scores || !q_len || max_len < 1 || ld_scores < max_len) return DSA_ERR_INVALID_ARGUMENT;
+  dsa_status s = check_scores(q, q_dtype, w, keys, n_heads);
+  if (s != DSA_OK) return s;
+  return from_hip(launch_index_scores(scores, ld_scores, q, q_dtype, w, to_dev(keys), keys->dtype, q_seq, 0, q_len,
+                                      n_q, n_heads, max_len, nullptr, static_cast<hipStream_t>(stream)));
+}
+
+size_t dsa_topk_workspace_size(int32_t n_q, int32_t k, int32_t max_len) {
+  if (n_q <= 0 || k < 1 || max_len < 1) return 0;
+  return plan_topk(n_q, k, max_len).total;
+}
+
+dsa_status dsa_topk(int32_t *indices, int32_t *counts, const float *scores, int64_t ld_scores,
+                    const int32_t *q_len, int32_t n_q, int32_t k, int32_t max_len, uint32_t flags,
+                    void *workspace, size_t workspace_bytes, void *stream) {
+  if (n_q < 0 || max_len < 0) return DSA_ERR_INVALID_ARGUMENT;
+  if (n_q == 0) return DSA_OK;
+  if (!indices || !scores || !q_len || k < 1 || max_len < 1 || ld_scores < max_len) return DSA_ERR_INVALID_ARGUMENT;
+  if (flags != DSA_TOPK_ORDER_INDEX) return DSA_ERR_UNSUPPORTED;
+  if (k > kMaxTopk || max_len > kMaxLenTopk) return DSA_ERR_UNSUPPORTED;
+  const TopkPlan p = plan_topk(n_q, k, max_len);
+  if (p.total > 0 && (!workspace || workspace_bytes < p.total)) return DSA_ERR_WORKSPACE_TOO_SMALL;
+  return from_hip(launch_topk(indices, counts, scores, ld_scores, q_len, p, workspace, false,
+                              static_cast<hipStream_t>(stream)));
+}
+
+size_t mla_sparse_attend_workspace_size(int32_t n_q, int32_t n_heads, int32_t kv_lora, int32_t k) {
+  if (n_q <= 0 || n_heads <= 0 || kv_lora <= 0 || k < 1) return 0;
+  // The split plan is the bf16 one; the f32 path needs no workspace.
+  return plan_attend(n_q, n_heads, kv_lora, 576, k, kBF16).total;
+}
+
+dsa_status mla_sparse_attend(float *out, float *lse, const void *q, dsa_dtype q_dtype, const dsa_cache *latent,
+                             int32_t kv_lora, const int32_t *indices, int32_t k, const int32_t *q_seq, int32_t n_q,
+                             int32_t n_heads, float softmax_scale, void *workspace, size_t workspace_bytes,
+                             void *stream) {
+  if (n_q < 0) return DSA_ERR_INVALID_ARGUMENT;
+  if (n_q == 0) return DSA_OK;
+  if (!out || !indices || k < 1) return DSA_ERR_INVALID_ARGUMENT;
+  dsa_status s = check_attend(q, q_dtype, latent, kv_lora, n_heads);
+  if (s != DSA_OK) return s;
+  if (k > kMaxTopk) return DSA_ERR_UNSUPPORTED;
+  const AttendPlan p = plan_attend(n_q, n_heads, kv_lora, latent->width, k, q_dtype);
+  if (p.total > 0 && (!workspace || workspace_bytes < p.total)) return DSA_ERR_WORKSPACE_TOO_SMALL;
+  return from_hip(launch_attend(out, lse, q, q_dtype, to_dev(latent), kv_lora, indices, k, q_seq, 0, n_q, n_heads,
+                                softmax_scale, p, workspace, static_cast<hipStream_t>(stream)));
+}
+
+size_t dsa_decode_step_workspace_size(int32_t batch, int32_t max_len, int32_t k, int32_t mla_heads,
+                                      int32_t kv_lora) {
+  if (batch <= 0 || max_len < 1 || k < 1 || mla_heads <= 0 || kv_lora <= 0) return 0;
+  return step_layout(batch, max_len, k, mla_heads, kv_lora, kBF16, 576).total;
+}
+
+dsa_status dsa_decode_step(float *out, float *lse, const void *q_idx, dsa_dtype q_idx_dtype, const float *w_idx,
+                           const dsa_cache *keys, int32_t idx_heads, const void *q_mla, dsa_dtype q_mla_dtype,
+                           const dsa_cache *latent, int32_t kv_lora, int32_t mla_heads, const int32_t *seq_len,
+                           int32_t batch, int32_t max_len, int32_t k, float softmax_scale, float *scores_out,
+                           int32_t *indices_out, void *workspace, size_t workspace_bytes, void *stream) {
+  if (batch < 0 || max_len < 0) return DSA_ERR_INVALID_ARGUMENT;
+  if (batch == 0) return DSA_OK;
+  if (!out || !seq_len || k < 1 || max_len < 1) return DSA_ERR_INVALID_ARGUMENT;
+  dsa_status s = check_scores(q_idx, q_idx_dtype, w_idx, keys, idx_heads);
+  if (s != DSA_OK) return s;
+  s = check_attend(q_mla, q_mla_dtype, latent, kv_lora, mla_heads);
+  if (s != DSA_OK) return s;
+  if (k > kMaxTopk || max_len > kMaxLenTopk) return DSA_ERR_UNSUPPORTED;
+  // The workspace size query assumes the bf16 latent plan, which is the larger one.
+  const StepLayout L = step_layout(batch, max_len, k, mla_heads, kv_lora, kBF16, 576);
+  const StepLayout A = step_layout(batch, max_len, k, mla_heads, kv_lora, q_mla_dtype, latent->width);
+  if (!workspace || workspace_bytes < L.total) return DSA_ERR_WORKSPACE_TOO_SMALL;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  uint8_t *ws = static_cast<uint8_t *>(workspace);
+  float *scores = scores_out ? scores_out : reinterpret_cast<float *>(ws + L.off_scores);
+  const int64_t ld = scores_out ? (int64_t)max_len : L.ld;
+  int32_t *idx = indices_out ? indices_out : reinterpret_cast<int32_t *>(ws + L.off_idx);
+  void *ws_topk = ws + L.off_topk;
+  void *ws_att = ws + L.off_att;
+  uint32_t *hist = L.tp.chunks > 1 ? reinterpret_cast<uint32_t *>(static_cast<uint8_t *>(ws_topk) + L.tp.off_hist)
+                                   : nullptr;
+  hipError_t e = launch_index_scores(scores, ld, q_idx, q_idx_dtype, w_idx, to_dev(keys), keys->dtype, nullptr, 1,
+                                     seq_len, batch, idx_heads, max_len, hist, st);
+  if (e != hipSuccess) return DSA_ERR_DEVICE;
+  e = launch_topk(idx, nullptr, scores, ld, seq_len, L.tp, ws_topk, hist != nullptr, st);
+  if (e != hipSuccess) return DSA_ERR_DEVICE;
+  e = launch_attend(out, lse, q_mla, q_mla_dtype, to_dev(latent), kv_lora, idx, k, nullptr, 1, batch, mla_heads,
+                    softmax_scale, A.ap, ws_att, st);
+  return from_hip(e);
+}
+
+}  // extern "C"

@@ -1,0 +1,146 @@
+"""Helpers for the GPU parity tests: run the library through its C ABI on
+device copies of seeded inputs, and compare with the oracle under the stated
+tolerances.
+
+Tolerances (fp32 inputs 1e-5, bf16/fp8 inputs with fp32 accumulation 2e-3):
+  scores     |gpu - oracle| <= tol * sum_h |w_h| sum_d |q_hd khat_d| per token,
+             and an oracle score of exactly 0 must be exactly 0 on the GPU;
+  attention  ||gpu_o - oracle_o||_2 <= tol * ||oracle_o||_2 per (query, head),
+             |gpu_lse - oracle_lse| <= tol * max(1, |oracle_lse|);
+  indices    bit-exact against the oracle's top-k of the GPU's own scores.
+"""
+from __future__ import annotations
+
+import numpy as np
+import torch
+
+import oracle
+import sparse_attention_14_amd as dsa
+from sparse_attention_14_amd import device, inputs
+
+TOL = {"f32": 1e-5, "bf16": 2e-3, "e4m3fn": 2e-3}
+
+
+def decode_values(bits: np.ndarray, dtype: str) -> np.ndarray:
+    """Raw element bits -> float64 via torch's dtype casts."""
+    if dtype == "f32":
+        return bits.view(np.float32).astype(np.float64)
+    if dtype == "bf16":
+        return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(torch.bfloat16).double().numpy()
+    return torch.from_numpy(np.ascontiguousarray(bits).view(np.uint8)).view(torch.float8_e4m3fn).double().numpy()
+
+
+def logical_rows(cache: inputs.Cache, seq: int, n: int) -> np.ndarray:
+    """Decoded rows of tokens 0..n-1 of a sequence (float64 [n, width]), scale applied."""
+    eb = inputs.ELEM_BYTES[cache.dtype]
+    t = np.arange(n)
+    if cache.block_table is None:
+        blk = np.full(n, seq)
+        slot = t
+    else:
+        blk = cache.block_table[seq, t // cache.block_size]
+        slot = t % cache.block_size
+    raw = cache.storage[blk, slot]                       # [n, width * eb] uint8
+    elem = {1: np.uint8, 2: np.uint16, 4: np.uint32}[eb]
+    vals = decode_values(np.ascontiguousarray(raw).view(elem).reshape(n, cache.width), cache.dtype)
+    if cache.scale is not None:
+        vals = vals * cache.scale[blk, slot].astype(np.float64)[:, None]
+    return vals
+
+
+def score_condition(p: inputs.Problem, i: int) -> np.ndarray:
+    """sum_h |w_h| sum_d |q_hd khat_d| for every token of query i."""
+    n = int(p.q_len[i])
+    seq = int(p.q_seq[i])
+    k = np.abs(logical_rows(p.keys, seq, n))
+    q = np.abs(decode_values(p.q_idx[i].reshape(-1), p.q_idx_dtype).reshape(p.idx_heads, p.idx_dim))
+    return (np.abs(p.w_idx[i].astype(np.float64)) @ (q @ k.T)) if n else np.zeros(0)
+
+
+def check_scores(p, gpu: np.ndarray, ref: np.ndarray, rows=None, tol=None):
+    tol = TOL[p.keys.dtype] if tol is None else tol
+    rows = range(p.n_q) if rows is None else rows
+    worst = 0.0
+    for r, i in enumerate(rows):
+        n = int(p.q_len[i])
+        g = gpu[r, :n].astype(np.float64)
+        o = ref[r, :n]
+        cond = score_condition(p, i)
+        err = np.abs(g - o)
+        bound = tol * cond
+        bad = err > bound
+        assert not bad.any(), (f"query {i}: {bad.sum()} scores outside tolerance, worst err {err[bad].max():.3g} "
+                               f"vs bound {bound[bad][np.argmax(err[bad])]:.3g}")
+        assert np.all(g[o == 0.0] == 0.0), f"query {i}: exact zero scores are not zero"
+        if n:
+            worst = max(worst, float((err / np.maximum(cond, 1e-300)).max()))
+    return worst
+
+
+def check_attention(gpu_o, gpu_lse, ref_o, ref_lse, tol):
+    gpu_o = gpu_o.astype(np.float64)
+    num = np.linalg.norm(gpu_o - ref_o, axis=-1)
+    den = np.linalg.norm(ref_o, axis=-1)
+    zero = den == 0
+    assert np.all(num[zero] == 0), "output should be exactly 0 where no row is kept"
+    rel = num[~zero] / den[~zero]
+    worst = float(rel.max()) if rel.size else 0.0
+    assert worst <= tol, f"attention output relative error {worst:.3g} > {tol}"
+    if gpu_lse is not None:
+        g = gpu_lse.astype(np.float64)
+        inf = np.isneginf(ref_lse)
+        assert np.all(np.isneginf(g[inf])), "lse should be -inf where no row is kept"
+        d = np.abs(g[~inf] - ref_lse[~inf])
+        assert np.all(d <= tol * np.maximum(1.0, np.abs(ref_lse[~inf]))), f"lse error {d.max():.3g}"
+    return worst
+
+
+# ----------------------------------------------------------------- runners --
+
+def gpu_scores(dp, ld=None, use_seq=True):
+    p = dp.host
+    ld = max(p.max_len, 1) if ld is None else ld
+    scores = torch.full((p.n_q, ld), float("nan"), device="cuda")
+    dsa.dsa_index_scores(scores, dp.q_idx, p.q_idx_dtype, dp.w_idx, dp.keys, dp.q_len, p.idx_heads, p.max_len,
+                         q_seq=dp.q_seq if use_seq else None)
+    torch.cuda.synchronize()
+    return scores
+
+
+def gpu_topk(scores: torch.Tensor, q_len: torch.Tensor, k: int, max_len: int):
+    n_q = q_len.shape[0]
+    idx = torch.full((n_q, k), -7, dtype=torch.int32, device="cuda")
+    cnt = torch.full((n_q,), -7, dtype=torch.int32, device="cuda")
+    wsz = dsa.dsa_topk_workspace_size(n_q, k, max_len)
+    ws = torch.zeros(max(wsz, 1), dtype=torch.uint8, device="cuda")
+    dsa.dsa_topk(idx, cnt, scores, q_len, k, max_len, workspace=ws)
+    torch.cuda.synchronize()
+    return idx, cnt, ws
+
+
+def gpu_attend(dp, indices: torch.Tensor, use_seq=True):
+    p = dp.host
+    out = torch.full((p.n_q, p.mla_heads, p.kv_lora), float("nan"), device="cuda")
+    lse = torch.full((p.n_q, p.mla_heads), float("nan"), device="cuda")
+    wsz = dsa.mla_sparse_attend_workspace_size(p.n_q, p.mla_heads, p.kv_lora, indices.shape[1])
+    ws = torch.zeros(max(wsz, 1), dtype=torch.uint8, device="cuda")
+    dsa.mla_sparse_attend(out, lse, dp.q_mla, p.q_mla_dtype, dp.latent, p.kv_lora, indices, p.softmax_scale,
+                          q_seq=dp.q_seq if use_seq else None, workspace=ws)
+    torch.cuda.synchronize()
+    return out, lse
+
+
+def gpu_decode_step(dp, ws=None):
+    p = dp.host
+    B, H, L = p.n_q, p.mla_heads, p.kv_lora
+    out = torch.full((B, H, L), float("nan"), device="cuda")
+    lse = torch.full((B, H), float("nan"), device="cuda")
+    scores = torch.full((B, max(p.max_len, 1)), float("nan"), device="cuda")
+    idx = torch.full((B, p.topk), -7, dtype=torch.int32, device="cuda")
+    if ws is None:
+        ws = torch.zeros(dsa.dsa_decode_step_workspace_size(B, p.max_len, p.topk, H, L), dtype=torch.uint8,
+                         device="cuda")
+    dsa.dsa_decode_step(out, lse, dp.q_idx, p.q_idx_dtype, dp.w_idx, dp.keys, dp.q_mla, p.q_mla_dtype, dp.latent, L,
+                        dp.q_len, p.max_len, p.topk, p.softmax_scale, ws, scores_out=scores, indices_out=idx)
+    torch.cuda.synchronize()
+    return out, lse, scores, idx, ws

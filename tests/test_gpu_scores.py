@@ -1,0 +1,71 @@
+"""GPU parity: dsa_index_scores against the oracle's fp64 scores."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from sparse_attention_14_amd import device, inputs
+
+from gpu_util import check_scores, gpu_scores
+
+pytestmark = pytest.mark.gpu
+
+S = inputs.small
+CASES = {
+    "tiny_fp32_full": inputs.TINY_FP32,
+    "f32_ragged_d64": S(inputs.TINY_FP32, name="f32r", wid=201, batch=3, seq_len=(1, 700), idx_heads=5, idx_dim=64,
+                        capacity_pad=13),
+    "f32_d128_paged": S(inputs.TINY_FP32, name="f32p", wid=202, batch=2, seq_len=(300, 900), idx_heads=3,
+                        idx_dim=128, paged=True),
+    "bf16_decode": S(inputs.DECODE_8K, name="bf16", wid=203, batch=2, seq_len=(2000, 4100), capacity_pad=100),
+    "bf16_paged": S(inputs.PAGED_DECODE, name="bf16p", wid=204, batch=3, seq_len=(100, 5000)),
+    "fp8_ties": S(inputs.DECODE_128K_FP8, name="fp8", wid=205, batch=2, seq_len=(4000, 6000), tie_fraction=0.01),
+    "fp8_paged_d64_h48": S(inputs.DECODE_128K_FP8, name="fp8p", wid=206, batch=2, seq_len=(900, 3000), paged=True,
+                           idx_dim=64, idx_heads=48),
+    "bf16_h64": S(inputs.DECODE_8K, name="h64", wid=207, batch=1, seq_len=(2500, 2500), idx_heads=64),
+    "bf16_h7_signed_w": S(inputs.DECODE_8K, name="h7", wid=208, batch=2, seq_len=(50, 1500), idx_heads=7, w_lo=-1.0,
+                          w_hi=1.0),
+    "bf16_prefill_rows": S(inputs.PREFILL_64K, name="pre", wid=209, seq_len=(3000, 3000), prefill_queries=64),
+}
+
+
+@pytest.fixture(scope="module", params=sorted(CASES))
+def case(request):
+    p = inputs.make_problem(CASES[request.param])
+    return p, device.upload(p)
+
+
+def test_scores_match_oracle(case):
+    p, dp = case
+    print(f"case {p.name}: n_q={p.n_q} max_len={p.max_len} keys={p.keys.dtype} paged={p.keys.paged}", flush=True)
+    g = gpu_scores(dp).cpu().numpy()
+    ref = oracle.index_scores(p.q_idx, p.q_idx_dtype, p.w_idx, p.keys, p.q_seq, p.q_len)
+    worst = check_scores(p, g, ref)
+    print(f"  worst scaled error {worst:.3g}")
+    for i in range(p.n_q):
+        assert np.all(np.isnan(g[i, int(p.q_len[i]):])), "entries beyond q_len were written"
+
+
+def test_prefill_rows_without_q_seq(case):
+    p, dp = case
+    if p.decode:
+        pytest.skip("multi-query single-sequence case only")
+    g = gpu_scores(dp, use_seq=False).cpu().numpy()
+    ref = oracle.index_scores(p.q_idx, p.q_idx_dtype, p.w_idx, p.keys, None, p.q_len)
+    check_scores(p, g, ref)
+
+
+def test_copied_keys_score_bit_identically(case):
+    p, dp = case
+    if not p.meta["ties"]:
+        pytest.skip("no injected ties")
+    g = gpu_scores(dp).cpu().numpy()
+    for s, (dst, src) in p.meta["ties"].items():
+        assert np.array_equal(g[s, dst].view(np.uint32), g[s, src].view(np.uint32))
+
+
+def test_scores_are_deterministic(case):
+    p, dp = case
+    a = gpu_scores(dp).cpu().numpy()
+    b = gpu_scores(dp).cpu().numpy()
+    assert np.array_equal(a.view(np.uint32), b.view(np.uint32))

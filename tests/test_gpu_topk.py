@@ -1,0 +1,119 @@
+"""GPU parity: dsa_topk indices bit-exact against the oracle's top-k of the same
+score array (first min(k, n) of a stable argsort of -score, ascending output)."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+
+from gpu_util import gpu_topk
+
+pytestmark = pytest.mark.gpu
+
+
+def _run(scores_np: np.ndarray, lens, k: int):
+    scores_np = np.ascontiguousarray(scores_np, dtype=np.float32)
+    max_len = scores_np.shape[1]
+    s = torch.from_numpy(scores_np).cuda()
+    ql = torch.tensor(np.asarray(lens, np.int32)).cuda()
+    idx, cnt, ws = gpu_topk(s, ql, k, max_len)
+    ref_idx, ref_cnt = oracle.topk(scores_np.astype(np.float64), np.asarray(lens, np.int32), k)
+    gi, gc = idx.cpu().numpy(), cnt.cpu().numpy()
+    for i in range(len(lens)):
+        if not np.array_equal(gi[i], ref_idx[i]):
+            diff = np.nonzero(gi[i] != ref_idx[i])[0]
+            raise AssertionError(f"row {i} (n={lens[i]}, k={k}): {len(diff)} index slots differ, first at {diff[0]}: "
+                                 f"gpu {gi[i, diff[0]]} oracle {ref_idx[i, diff[0]]}")
+    assert np.array_equal(gc, ref_cnt)
+    return ws
+
+
+def test_random_long_rows_multi_workgroup():
+    rng = np.random.default_rng(1)
+    s = rng.standard_normal((4, 131072)).astype(np.float32) * 4 + 12
+    print("case: 4 x 131072 normal, k=2048", flush=True)
+    _run(s, [131072, 131072, 100000, 4097], 2048)
+
+
+def test_heavy_ties_take_lowest_indices():
+    rng = np.random.default_rng(2)
+    s = rng.integers(0, 6, size=(3, 40000)).astype(np.float32)   # six distinct values
+    print("case: 3 x 40000 six values, k=2048", flush=True)
+    _run(s, [40000, 39999, 20000], 2048)
+    _run(s, [40000, 39999, 20000], 17)
+
+
+def test_all_equal_overflows_candidates():
+    s = np.full((2, 50000), 0.75, np.float32)
+    print("case: all equal 2 x 50000", flush=True)
+    _run(s, [50000, 30000], 2048)
+    s = np.full((130, 9000), -3.5, np.float32)     # many rows: one workgroup per row
+    print("case: all equal 130 x 9000", flush=True)
+    _run(s, [9000] * 130, 2048)
+
+
+def test_relu_zero_ties():
+    rng = np.random.default_rng(3)
+    # about half the scores are exactly 0, so with n = 3000 the k = 2048 boundary
+    # falls inside the run of zeros and the tie quota decides
+    s = np.maximum(rng.standard_normal((2, 3000)), 0).astype(np.float32)
+    print("case: relu zeros", flush=True)
+    _run(s, [3000, 2900], 2048)
+    _run(s, [3000, 2900], 1000)
+
+
+def test_special_values():
+    rng = np.random.default_rng(4)
+    vals = np.array([np.nan, -np.nan, np.inf, -np.inf, 0.0, -0.0, 1.0, -1.0, 1e-40, -1e-40, 3.4e38, -3.4e38],
+                    np.float32)
+    s = vals[rng.integers(0, len(vals), size=(3, 9000))]
+    print("case: special values", flush=True)
+    _run(s, [9000, 5000, 8999], 2048)
+    _run(s, [9000, 5000, 8999], 5)
+
+
+@pytest.mark.parametrize("n", [1, 63, 64, 65, 2047, 2048, 2049])
+def test_context_at_most_k(n):
+    rng = np.random.default_rng(n)
+    s = rng.standard_normal((2, 5000)).astype(np.float32)
+    _run(s, [n, min(n + 1, 5000)], 2048)
+
+
+@pytest.mark.parametrize("k", [1, 17, 2048])
+def test_k_values_and_empty_rows(k):
+    rng = np.random.default_rng(k)
+    s = rng.standard_normal((5, 6000)).astype(np.float32)
+    _run(s, [6000, 0, 1, 3000, 5999], k)
+
+
+def test_exact_bin_boundary():
+    # k scores of 2.0 and the rest 1.0: the threshold bin is taken whole.
+    s = np.ones((2, 10000), np.float32)
+    rng = np.random.default_rng(5)
+    for r in range(2):
+        s[r, rng.choice(10000, 2048, replace=False)] = 2.0
+    _run(s, [10000, 10000], 2048)
+
+
+def test_many_rows_one_workgroup_each():
+    rng = np.random.default_rng(6)
+    s = (rng.standard_normal((200, 10000)) * 3).astype(np.float32)
+    lens = rng.integers(1, 10001, size=200)
+    _run(s, lens, 2048)
+
+
+def test_workspace_is_reusable():
+    rng = np.random.default_rng(7)
+    a = rng.standard_normal((4, 60000)).astype(np.float32)
+    b = np.round(rng.standard_normal((4, 60000)) * 2).astype(np.float32)
+    s = torch.from_numpy(a).cuda()
+    ql = torch.full((4,), 60000, dtype=torch.int32).cuda()
+    idx, cnt, ws = gpu_topk(s, ql, 2048, 60000)
+    import sparse_attention_14_amd as dsa
+    for arr in (b, a, b):
+        s2 = torch.from_numpy(arr).cuda()
+        idx2 = torch.empty(4, 2048, dtype=torch.int32, device="cuda")
+        dsa.dsa_topk(idx2, None, s2, ql, 2048, 60000, workspace=ws)
+        torch.cuda.synchronize()
+        ref, _ = oracle.topk(arr.astype(np.float64), [60000] * 4, 2048)
+        assert np.array_equal(idx2.cpu().numpy(), ref)
