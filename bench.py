@@ -1,0 +1,283 @@
+"""Benchmark of the DSA hot path on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu] [--no-prefill]
+
+Headline workload: long-context decode, 4 sequences x 131,072 tokens, 32 x 128
+fp8-e4m3fn indexer keys with per-token float32 scales, exact top-2048, 64-head
+absorbed MLA over bf16 576-wide latent rows ("decode_128k_fp8").  One step =
+indexer scores -> exact top-k -> sparse MLA for the 4 sequences
+(dsa_decode_step), replayed from a HIP graph.  Inputs are seeded synthetic
+caches already resident in HBM; the step rotates over several device copies of
+them (> the 256 MB last-level cache) so every step reads cold memory.
+
+value = algorithmic bytes per step / step time (GB/s); the same run also
+measures the dominant kernel (the indexer score kernel) with HIP events on its
+own stream, the chunked-prefill indexer (2,048 queries against a 65,536-token
+causal context) in TFLOP/s, and the CPU oracle on the host cores.
+Prints one JSON line.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "DSA decode µs/step & HBM GB/s at 128K ctx; prefill indexer TFLOP/s"
+HBM_PEAK_GBS = 8000.0
+BF16_PEAK_TFLOPS = 2500.0
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=400)
+    ap.add_argument("--warmup", type=int, default=40)
+    ap.add_argument("--copies", type=int, default=6, help="device copies of the caches rotated over")
+    ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    ap.add_argument("--no-prefill", action="store_true")
+    return ap.parse_args()
+
+
+def decode_algorithmic_bytes(p) -> int:
+    """Bytes the decode step must move: every visible key (+ fp8 scale), the kept
+    latent rows, the queries and head weights, and the outputs."""
+    eb = {"f32": 4, "bf16": 2, "e4m3fn": 1}
+    n_tok = int(p.q_len.astype("int64").sum())
+    kept = int(sum(min(int(n), p.topk) for n in p.q_len))
+    keys = n_tok * p.idx_dim * eb[p.keys.dtype] + (n_tok * 4 if p.keys.dtype == "e4m3fn" else 0)
+    latent = kept * (p.kv_lora + p.rope) * eb[p.latent.dtype]
+    q = p.q_idx.size * eb[p.q_idx_dtype] + p.w_idx.size * 4 + p.q_mla.size * eb[p.q_mla_dtype]
+    out = p.n_q * p.mla_heads * (p.kv_lora + 1) * 4
+    return keys + latent + q + out
+
+
+def score_kernel_bytes(p) -> int:
+    """Algorithmic bytes of one indexer-score launch: keys (+ scales), q, w."""
+    eb = {"f32": 4, "bf16": 2, "e4m3fn": 1}
+    n_tok = int(p.q_len.astype("int64").sum())
+    keys = n_tok * p.idx_dim * eb[p.keys.dtype] + (n_tok * 4 if p.keys.dtype == "e4m3fn" else 0)
+    return keys + p.q_idx.size * eb[p.q_idx_dtype] + p.w_idx.size * 4
+
+
+def prefill_indexer_flops(p) -> int:
+    """2 * heads * dim multiply-adds per visible (query, key) pair."""
+    return 2 * p.idx_heads * p.idx_dim * int(p.q_len.astype("int64").sum())
+
+
+def clone_cache(c):
+    from sparse_attention_14_amd.binding import DeviceCache
+    d = c.desc
+    return DeviceCache(c.rows.clone(), c.dtype, c.width, c.block_size, d.row_stride, d.block_stride,
+                       scale=None if c.scale is None else c.scale.clone(), scale_block_stride=d.scale_block_stride,
+                       block_table=None if c.block_table is None else c.block_table.clone())
+
+
+def read_traffic(kernel_tag: str):
+    """HBM traffic per launch from the committed PMC summary, if it was taken on
+    the current kernel source (its hash matches); else None."""
+    import hashlib
+    path = os.path.join(ROOT, "profiles", f"pmc_{kernel_tag}.txt")
+    if not os.path.exists(path):
+        return None
+    src = open(os.path.join(ROOT, "sparse_attention_14_amd", "csrc", "index_scores.hip"), "rb").read()
+    h = hashlib.sha256(src).hexdigest()[:16]
+    vals = {}
+    for line in open(path):
+        if ":" in line:
+            k, v = line.split(":", 1)
+            vals[k.strip()] = v.strip()
+    if vals.get("source_sha256_16") != h or "traffic_bytes_per_launch" not in vals:
+        return None
+    return float(vals["traffic_bytes_per_launch"])
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported (the path is single-GPU; "
+              "multi-GPU sharding is described in DESIGN.md but not built)", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import sparse_attention_14_amd as dsa
+    from sparse_attention_14_amd import device, inputs
+
+    dsa.load()
+    torch.cuda.init()
+    dev_name = torch.cuda.get_device_name(0)
+
+    # ------------------------------------------------------------ decode ---
+    wl = inputs.DECODE_128K_FP8
+    t0 = time.time()
+    p = inputs.make_problem(wl)
+    dp = device.upload(p)
+    print(f"[bench] generated and uploaded {wl.name} in {time.time() - t0:.1f}s", file=sys.stderr, flush=True)
+    B, H, L, k = p.n_q, p.mla_heads, p.kv_lora, p.topk
+    copies = [(dp.keys, dp.latent)] + [(clone_cache(dp.keys), clone_cache(dp.latent)) for _ in range(args.copies - 1)]
+    torch.cuda.synchronize()
+    out = torch.empty(B, H, L, device="cuda")
+    lse = torch.empty(B, H, device="cuda")
+    wsz = dsa.dsa_decode_step_workspace_size(B, p.max_len, k, H, L)
+    workspaces = [torch.zeros(wsz, dtype=torch.uint8, device="cuda") for _ in copies]
+
+    def step(ci, stream=None):
+        keys, lat = copies[ci]
+        dsa.dsa_decode_step(out, lse, dp.q_idx, p.q_idx_dtype, dp.w_idx, keys, dp.q_mla, p.q_mla_dtype, lat, L,
+                            dp.q_len, p.max_len, k, p.softmax_scale, workspaces[ci], stream=stream)
+
+    # eager warm-up and a sanity check
+    for i in range(3):
+        step(i % len(copies))
+    torch.cuda.synchronize()
+    assert torch.isfinite(out).all().item(), "non-finite decode output"
+
+    # graphs: one per input copy
+    side = torch.cuda.Stream()
+    graphs = []
+    for ci in range(len(copies)):
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g, stream=side):
+            step(ci)
+        graphs.append(g)
+    torch.cuda.synchronize()
+    for i in range(args.warmup):
+        graphs[i % len(graphs)].replay()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        graphs[i % len(graphs)].replay()
+    torch.cuda.synchronize()
+    t_step = (time.perf_counter() - t0) / args.steps
+
+    # eager (no graph) step time, for reference
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    n_eager = max(args.steps // 4, 10)
+    for i in range(n_eager):
+        step(i % len(copies))
+    torch.cuda.synchronize()
+    t_eager = (time.perf_counter() - t0) / n_eager
+
+    step_bytes = decode_algorithmic_bytes(p)
+    gbs = step_bytes / t_step / 1e9
+
+    # ----------------------------------- dominant kernel: indexer scores ---
+    # One dsa_index_scores call is exactly one launch of the score kernel; HIP
+    # events recorded on the stream it is launched on bracket the timed launches.
+    kstream = torch.cuda.Stream()
+    scores = torch.empty(B, p.max_len, device="cuda")
+    n_k = max(args.steps, 50)
+    with torch.cuda.stream(kstream):
+        for i in range(5):
+            keys, _ = copies[i % len(copies)]
+            dsa.dsa_index_scores(scores, dp.q_idx, p.q_idx_dtype, dp.w_idx, keys, dp.q_len, p.idx_heads, p.max_len)
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record(kstream)
+        for i in range(n_k):
+            keys, _ = copies[i % len(copies)]
+            dsa.dsa_index_scores(scores, dp.q_idx, p.q_idx_dtype, dp.w_idx, keys, dp.q_len, p.idx_heads, p.max_len)
+        e1.record(kstream)
+    e1.synchronize()
+    t_kernel = e0.elapsed_time(e1) / 1e3 / n_k
+    kbytes = score_kernel_bytes(p)
+    k_gbs = kbytes / t_kernel / 1e9
+    traffic = read_traffic("scores_decode_128k_fp8")
+    roofline = {"bound": "hbm", "achieved": round(k_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": round(k_gbs / HBM_PEAK_GBS, 4), "traffic": traffic,
+                "kernel": "scores_mfma_kernel (fp8 keys, 128-wide, 32 heads)", "bytes_per_launch": kbytes,
+                "avg_launch_us": round(t_kernel * 1e6, 3)}
+
+    # ----------------------------------------------------------- prefill ---
+    prefill = None
+    if not args.no_prefill:
+        del copies, workspaces, graphs
+        torch.cuda.empty_cache()
+        wp = inputs.PREFILL_64K
+        t0 = time.time()
+        pp = inputs.make_problem(wp)
+        dpp = device.upload(pp)
+        print(f"[bench] generated and uploaded {wp.name} in {time.time() - t0:.1f}s", file=sys.stderr, flush=True)
+        ps = torch.empty(pp.n_q, pp.max_len, device="cuda")
+        for _ in range(2):
+            dsa.dsa_index_scores(ps, dpp.q_idx, pp.q_idx_dtype, dpp.w_idx, dpp.keys, dpp.q_len, pp.idx_heads,
+                                 pp.max_len)
+        torch.cuda.synchronize()
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        reps = 5
+        e0.record()
+        for _ in range(reps):
+            dsa.dsa_index_scores(ps, dpp.q_idx, pp.q_idx_dtype, dpp.w_idx, dpp.keys, dpp.q_len, pp.idx_heads,
+                                 pp.max_len)
+        e1.record()
+        e1.synchronize()
+        t_pi = e0.elapsed_time(e1) / 1e3 / reps
+        flops = prefill_indexer_flops(pp)
+        # top-k and sparse attention of the chunk, reported
+        pidx = torch.empty(pp.n_q, pp.topk, dtype=torch.int32, device="cuda")
+        tws = torch.zeros(max(dsa.dsa_topk_workspace_size(pp.n_q, pp.topk, pp.max_len), 1), dtype=torch.uint8,
+                          device="cuda")
+        pout = torch.empty(pp.n_q, pp.mla_heads, pp.kv_lora, device="cuda")
+        plse = torch.empty(pp.n_q, pp.mla_heads, device="cuda")
+        aws = torch.zeros(max(dsa.mla_sparse_attend_workspace_size(pp.n_q, pp.mla_heads, pp.kv_lora, pp.topk), 1),
+                          dtype=torch.uint8, device="cuda")
+        dsa.dsa_topk(pidx, None, ps, dpp.q_len, pp.topk, pp.max_len, workspace=tws)
+        dsa.mla_sparse_attend(pout, plse, dpp.q_mla, pp.q_mla_dtype, dpp.latent, pp.kv_lora, pidx, pp.softmax_scale,
+                              workspace=aws)
+        torch.cuda.synchronize()
+        e0.record()
+        dsa.dsa_topk(pidx, None, ps, dpp.q_len, pp.topk, pp.max_len, workspace=tws)
+        e1.record()
+        e1.synchronize()
+        t_pt = e0.elapsed_time(e1) / 1e3
+        e0.record()
+        dsa.mla_sparse_attend(pout, plse, dpp.q_mla, pp.q_mla_dtype, dpp.latent, pp.kv_lora, pidx, pp.softmax_scale,
+                              workspace=aws)
+        e1.record()
+        e1.synchronize()
+        t_pa = e0.elapsed_time(e1) / 1e3
+        mla_flops = 0
+        for n in pp.q_len:
+            kept = min(int(n), pp.topk)
+            mla_flops += 2 * pp.mla_heads * kept * ((pp.kv_lora + pp.rope) + pp.kv_lora)
+        prefill = {"workload": wp.name, "queries": pp.n_q, "context": int(pp.max_len),
+                   "indexer_ms": round(t_pi * 1e3, 3), "indexer_tflops": round(flops / t_pi / 1e12, 1),
+                   "indexer_mfma_frac": round(flops / t_pi / 1e12 / BF16_PEAK_TFLOPS, 4),
+                   "topk_ms": round(t_pt * 1e3, 3), "sparse_mla_ms": round(t_pa * 1e3, 3),
+                   "sparse_mla_tflops": round(mla_flops / t_pa / 1e12, 1)}
+
+    # ------------------------------------------------------ CPU baseline ---
+    cpu = None
+    if not args.no_cpu:
+        import oracle
+        t0 = time.perf_counter()
+        oracle.decode_step(p)
+        t_cpu = time.perf_counter() - t0
+        cpu = {"value": round(step_bytes / t_cpu / 1e9, 3), "unit": "GB/s", "cores": oracle.num_threads(),
+               "kind": "oracle", "sample": f"one full decode step of {wl.name} (4 x 131072 tokens), fp64 oracle, "
+                                           f"{t_cpu:.2f} s"}
+
+    line = {
+        "metric": METRIC, "value": round(gbs, 1), "unit": "GB/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(t_step * 1e3, 5), "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": wl.name, "batch": B, "context": int(p.max_len), "topk": k,
+                   "indexer": f"{p.idx_heads}x{p.idx_dim} e4m3fn keys + f32 scale", "mla_heads": H,
+                   "latent": f"{L}+{p.rope} bf16", "graph": True, "cache_copies": args.copies},
+        "decode_us_per_step": round(t_step * 1e6, 2), "decode_us_per_step_eager": round(t_eager * 1e6, 2),
+        "decode_bytes_per_step": step_bytes, "decode_hbm_frac": round(gbs / HBM_PEAK_GBS, 4),
+        "roofline": roofline, "prefill": prefill, "cpu_baseline": cpu, "device": dev_name,
+    }
+    print(json.dumps(line))
+
+
+if __name__ == "__main__":
+    main()

@@ -96,33 +96,77 @@ __device__ __forceinline__ uint32_t atomic_add_agent(uint32_t *p, uint32_t v) {
   return __hip_atomic_fetch_add(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
+// Inclusive prefix sum over the 64 lanes of a wavefront with DPP moves (ALU
+// only): row_shr 1, 2, 4, 8 scans each 16-lane row, then row_bcast 15 and
+// row_bcast 31 carry the row totals forward.
+__device__ __forceinline__ uint32_t wave_inclusive_scan(uint32_t x) {
+  // dpp_ctrl: row_shr:n = 0x110 + n, row_bcast:15 = 0x142, row_bcast:31 = 0x143
+  x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x111, 0xF, 0xF, true);
+  x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x112, 0xF, 0xF, true);
+  x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x114, 0xF, 0xF, true);
+  x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x118, 0xF, 0xF, true);
+  x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x142, 0xA, 0xF, false);
+  x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x143, 0xC, 0xF, false);
+  return x;
+}
+
+__device__ __forceinline__ uint32_t wave_sum(uint32_t x) {
+  return (uint32_t)__builtin_amdgcn_readlane((int)wave_inclusive_scan(x), 63);
+}
+
+// Minimum / maximum over the lanes of a wavefront (DPP; result in every lane).
+__device__ __forceinline__ uint32_t wave_min_u32(uint32_t x) {
+  x = min(x, (uint32_t)__builtin_amdgcn_update_dpp(-1, (int)x, 0x111, 0xF, 0xF, false));
+  x = min(x, (uint32_t)__builtin_amdgcn_update_dpp(-1, (int)x, 0x112, 0xF, 0xF, false));
+  x = min(x, (uint32_t)__builtin_amdgcn_update_dpp(-1, (int)x, 0x114, 0xF, 0xF, false));
+  x = min(x, (uint32_t)__builtin_amdgcn_update_dpp(-1, (int)x, 0x118, 0xF, 0xF, false));
+  x = min(x, (uint32_t)__builtin_amdgcn_update_dpp(-1, (int)x, 0x142, 0xA, 0xF, false));
+  x = min(x, (uint32_t)__builtin_amdgcn_update_dpp(-1, (int)x, 0x143, 0xC, 0xF, false));
+  return (uint32_t)__builtin_amdgcn_readlane((int)x, 63);
+}
+__device__ __forceinline__ uint32_t wave_max_u32(uint32_t x) {
+  x = max(x, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x111, 0xF, 0xF, false));
+  x = max(x, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x112, 0xF, 0xF, false));
+  x = max(x, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x114, 0xF, 0xF, false));
+  x = max(x, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x118, 0xF, 0xF, false));
+  x = max(x, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x142, 0xA, 0xF, false));
+  x = max(x, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x143, 0xC, 0xF, false));
+  return (uint32_t)__builtin_amdgcn_readlane((int)x, 63);
+}
+
+// Largest key prefix T (the top `bits` bits; the rest zero) such that at least
+// `need` of the keys x[0..N) held by the lanes of one wavefront are >= T: a lower
+// bound on the need-th largest key.  Called by a whole wavefront.
+template <int N>
+__device__ __forceinline__ uint32_t wave_rank_bound(const uint32_t (&x)[N], uint32_t need, int bits) {
+  uint32_t T = 0;
+  for (int b = 31; b >= 32 - bits; --b) {
+    const uint32_t c = T | (1u << b);
+    uint32_t m = 0;
+#pragma unroll
+    for (int i = 0; i < N; ++i) m += x[i] >= c ? 1u : 0u;
+    if (wave_sum(m) >= need) T = c;
+  }
+  return T;
+}
+
 // Block-wide exclusive prefix sum of one uint32 per thread, in thread order.
 // scratch: >= blockDim.x / 64 + 1 words of LDS.  Returns the exclusive prefix;
 // *total receives the block sum.  All threads must call it.
 __device__ __forceinline__ uint32_t block_exclusive_scan(uint32_t v, uint32_t *scratch, uint32_t *total) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, nwaves = (blockDim.x + 63) >> 6;
-  uint32_t x = v;
-#pragma unroll
-  for (int o = 1; o < 64; o <<= 1) {
-    uint32_t y = __shfl_up(x, o, 64);
-    if (lane >= o) x += y;
-  }
+  const uint32_t x = wave_inclusive_scan(v);
   if (lane == 63) scratch[wave] = x;
   __syncthreads();
-  if (threadIdx.x == 0) {
-    uint32_t run = 0;
-    for (int i = 0; i < nwaves; ++i) {
-      uint32_t t = scratch[i];
-      scratch[i] = run;
-      run += t;
-    }
-    scratch[nwaves] = run;
+  uint32_t before = 0, all = 0;
+  for (int i = 0; i < nwaves; ++i) {
+    const uint32_t t = scratch[i];
+    before += i < wave ? t : 0u;
+    all += t;
   }
+  *total = all;
   __syncthreads();
-  uint32_t r = x - v + scratch[wave];
-  *total = scratch[nwaves];
-  __syncthreads();
-  return r;
+  return before + x - v;
 }
 
 }  // namespace dsa

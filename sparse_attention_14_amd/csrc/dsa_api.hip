@@ -90,10 +90,11 @@ dsa_status from_hip(hipError_t e) { return e == hipSuccess ? DSA_OK : DSA_ERR_DE
 
 size_t round256(size_t b) { return (b + 255) / 256 * 256; }
 
-// Decode-step workspace: [scores][indices][topk][attend].
+// Decode-step workspace: [scores][indices][score bounds][topk][attend].
 struct StepLayout {
   int64_t ld;
-  size_t off_scores, off_idx, off_topk, off_att, total;
+  int n_bounds;
+  size_t off_scores, off_idx, off_bounds, off_topk, off_att, total;
   TopkPlan tp;
   AttendPlan ap;
 };
@@ -109,6 +110,9 @@ StepLayout step_layout(int32_t batch, int32_t max_len, int32_t k, int32_t mla_he
   off += round256((size_t)batch * L.ld * 4);
   L.off_idx = off;
   off += round256((size_t)batch * k * 4);
+  L.n_bounds = score_groups_per_row(batch, max_len);
+  L.off_bounds = off;
+  off += round256((size_t)batch * L.n_bounds * 4);
   L.off_topk = off;
   off += round256(L.tp.total);
   L.off_att = off;
@@ -147,7 +151,8 @@ dsa_status dsa_index_scores(float *scores, int64_t ld_scores, const void *q, dsa
   dsa_status s = check_scores(q, q_dtype, w, keys, n_heads);
   if (s != DSA_OK) return s;
   return from_hip(launch_index_scores(scores, ld_scores, q, q_dtype, w, to_dev(keys), keys->dtype, q_seq, 0, q_len,
-                                      n_q, n_heads, max_len, nullptr, static_cast<hipStream_t>(stream)));
+                                      n_q, n_heads, max_len, ScoreBounds{nullptr, 0},
+                                      static_cast<hipStream_t>(stream)));
 }
 
 size_t dsa_topk_workspace_size(int32_t n_q, int32_t k, int32_t max_len) {
@@ -165,7 +170,7 @@ dsa_status dsa_topk(int32_t *indices, int32_t *counts, const float *scores, int6
   if (k > kMaxTopk || max_len > kMaxLenTopk) return DSA_ERR_UNSUPPORTED;
   const TopkPlan p = plan_topk(n_q, k, max_len);
   if (p.total > 0 && (!workspace || workspace_bytes < p.total)) return DSA_ERR_WORKSPACE_TOO_SMALL;
-  return from_hip(launch_topk(indices, counts, scores, ld_scores, q_len, p, workspace, false,
+  return from_hip(launch_topk(indices, counts, scores, ld_scores, q_len, p, workspace, nullptr, 0,
                               static_cast<hipStream_t>(stream)));
 }
 
@@ -221,12 +226,13 @@ dsa_status dsa_decode_step(float *out, float *lse, const void *q_idx, dsa_dtype 
   int32_t *idx = indices_out ? indices_out : reinterpret_cast<int32_t *>(ws + L.off_idx);
   void *ws_topk = ws + L.off_topk;
   void *ws_att = ws + L.off_att;
-  uint32_t *hist = L.tp.chunks > 1 ? reinterpret_cast<uint32_t *>(static_cast<uint8_t *>(ws_topk) + L.tp.off_hist)
-                                   : nullptr;
+  // bf16/fp8 keys: the score kernel also reports the top-k's candidate bounds
+  uint32_t *bounds = (L.tp.chunks > 1 && q_idx_dtype != DSA_F32)
+                         ? reinterpret_cast<uint32_t *>(ws + L.off_bounds) : nullptr;
   hipError_t e = launch_index_scores(scores, ld, q_idx, q_idx_dtype, w_idx, to_dev(keys), keys->dtype, nullptr, 1,
-                                     seq_len, batch, idx_heads, max_len, hist, st);
+                                     seq_len, batch, idx_heads, max_len, ScoreBounds{bounds, k}, st);
   if (e != hipSuccess) return DSA_ERR_DEVICE;
-  e = launch_topk(idx, nullptr, scores, ld, seq_len, L.tp, ws_topk, hist != nullptr, st);
+  e = launch_topk(idx, nullptr, scores, ld, seq_len, L.tp, ws_topk, bounds, L.n_bounds, st);
   if (e != hipSuccess) return DSA_ERR_DEVICE;
   e = launch_attend(out, lse, q_mla, q_mla_dtype, to_dev(latent), kv_lora, idx, k, nullptr, 1, batch, mla_heads,
                     softmax_scale, A.ap, ws_att, st);

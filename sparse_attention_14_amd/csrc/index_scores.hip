@@ -14,133 +14,190 @@
 // the same for every key, so byte-identical keys score bit-identically.
 //
 // The K dimension is permuted: lane half h (= lane / 32) holds dims
-// [h*D/2, (h+1)*D/2) of its key, which is one contiguous run of the key row, and
-// the q operand uses the same permutation, so the dot product is unchanged.
-//
-// Optionally the kernel also counts order_key(score) >> 20 per query into a
-// global histogram (the first radix level of the top-k), workgroup-local in
-// LDS first, then one atomic per non-empty bin.
+// [h*D/2, (h+1)*D/2) of its key, and the q operand uses the same permutation,
+// so the dot product is unchanged.  Keys are fetched with fully coalesced
+// loads and redistributed through a per-wavefront LDS tile.
 #include "kernels.hpp"
 
 namespace dsa {
 namespace {
 
-template <bool FP8, int D, int MT, bool HIST>
+constexpr int kMaxTilesPerWave = 8;
+
+template <bool FP8, int D, int MT>
 __global__ __launch_bounds__(256) void scores_mfma_kernel(float *__restrict__ scores, int64_t ld,
                                                           const uint16_t *__restrict__ q, const float *__restrict__ w,
                                                           CacheDev keys, const int32_t *__restrict__ q_seq,
                                                           int seq_ident, const int32_t *__restrict__ q_len,
-                                                          int n_heads, int tiles_per_wave,
-                                                          uint32_t *__restrict__ hist) {
-  constexpr int KS = D / 16;                 // 32x32x16 K-steps
-  constexpr int HALF = D / 2;                // dims held by one lane half
-  constexpr int EB = FP8 ? 1 : 2;            // key element bytes
-  __shared__ uint32_t lhist[HIST ? kHistBins : 1];
+                                                          int n_heads, int tiles_per_wave, uint32_t *__restrict__ bounds,
+                                                          int topk) {
+  constexpr int KS = D / 16;            // 32x32x16 K-steps
+  constexpr int HALF = D / 2;           // dims held by one lane half
+  constexpr int EB = FP8 ? 1 : 2;       // key element bytes
+  constexpr int ROWB = D * EB;          // key row bytes
+  constexpr int CPR = ROWB / 16;        // 16-byte chunks per row
+  constexpr int HALFC = CPR / 2;        // chunks per lane half
+  constexpr int TILEB = 32 * ROWB;      // bytes of a 32-key tile
+  constexpr int NLD = TILEB / 1024;     // 1 KB wavefront loads per tile
+  __shared__ __align__(16) uint8_t stage_all[4][TILEB];
 
   const int qi = blockIdx.y;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int half = lane >> 5, col = lane & 31;
   const int n = q_len[qi];
-  if (HIST) {
-    for (int i = threadIdx.x; i < kHistBins; i += 256) lhist[i] = 0;
-    __syncthreads();
-  }
   const int tile_begin = (blockIdx.x * 4 + wave) * tiles_per_wave;
   const int seq = seq_of(q_seq, qi, seq_ident);
+  uint8_t *stage = stage_all[wave];
+  uint32_t lane_max = 0;   // largest score key this lane wrote (bounds only)
 
   if (tile_begin * 32 < n) {
-    // q as the A operand: lane (col, half) holds head 32*mt + col, dims half*HALF + 8*ks + [0, 8).
-    bf16x8 a[MT][KS];
-    float wr[MT][16];
+  // q as the A operand: lane (col, half) holds head 32*mt + col, dims half*HALF + 8*ks + [0, 8).
+  bf16x8 a[MT][KS];
+  float wr[MT][16];
 #pragma unroll
-    for (int mt = 0; mt < MT; ++mt) {
-      const int head = 32 * mt + col;
-      const uint16_t *qrow = q + ((int64_t)qi * n_heads + (head < n_heads ? head : 0)) * D + half * HALF;
+  for (int mt = 0; mt < MT; ++mt) {
+    const int head = 32 * mt + col;
+    const uint16_t *qrow = q + ((int64_t)qi * n_heads + (head < n_heads ? head : 0)) * D + half * HALF;
 #pragma unroll
-      for (int ks = 0; ks < KS; ++ks) {
-        u32x4 v = load16(qrow + 8 * ks);
-        if (head >= n_heads) v = u32x4{0, 0, 0, 0};
-        a[mt][ks] = as_bf16x8(v);
-      }
-      // Accumulator element r of this lane is head 32*mt + 8*(r/4) + 4*half + r%4.
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int m = 32 * mt + 8 * (r >> 2) + 4 * half + (r & 3);
-        wr[mt][r] = m < n_heads ? w[(int64_t)qi * n_heads + m] : 0.0f;
-      }
+    for (int ks = 0; ks < KS; ++ks) {
+      u32x4 v = load16(qrow + 8 * ks);
+      if (head >= n_heads) v = u32x4{0, 0, 0, 0};
+      a[mt][ks] = as_bf16x8(v);
     }
-
-    for (int it = 0; it < tiles_per_wave; ++it) {
-      const int t0 = (tile_begin + it) * 32;
-      if (t0 >= n) break;
-      const int t = t0 + col;
-      const int tl = t < n ? t : n - 1;
-      const int bi = t0 / keys.block_size;   // a 32-token tile never straddles a block
-      const int64_t blk = keys.table ? (int64_t)keys.table[(int64_t)seq * keys.max_blocks + bi] : (int64_t)seq;
-      const int slot = tl - bi * keys.block_size;
-      const uint8_t *row = cache_row(keys, blk, slot) + half * HALF * EB;
-
-      bf16x8 b[KS];
-      if (FP8) {
+    // Accumulator element r of this lane is head 32*mt + 8*(r/4) + 4*half + r%4.
 #pragma unroll
-        for (int j = 0; j < HALF / 16; ++j) {
-          u32x4 v = load16_nt(row + 16 * j);
-          b[2 * j] = fp8x8_to_bf16x8(v[0], v[1]);
-          b[2 * j + 1] = fp8x8_to_bf16x8(v[2], v[3]);
-        }
-      } else {
-#pragma unroll
-        for (int ks = 0; ks < KS; ++ks) b[ks] = as_bf16x8(load16_nt(row + 16 * ks));
-      }
-      const float sc = FP8 ? keys.scale[blk * keys.scale_block_stride + slot] : 1.0f;
-
-      float s = 0.0f;
-#pragma unroll
-      for (int mt = 0; mt < MT; ++mt) {
-        f32x16 acc = {};
-#pragma unroll
-        for (int ks = 0; ks < KS; ++ks) acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[mt][ks], b[ks], acc, 0, 0, 0);
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          float v = FP8 ? acc[r] * sc : acc[r];
-          v = fmaxf(v, 0.0f);
-          s = fmaf(wr[mt][r], v, s);
-        }
-      }
-      s += __shfl_xor(s, 32, 64);
-      if (half == 0 && t < n) {
-        scores[(int64_t)qi * ld + t] = s;
-        if (HIST) atomicAdd(&lhist[order_key(s) >> kHistShift], 1u);
-      }
+    for (int r = 0; r < 16; ++r) {
+      const int m = 32 * mt + 8 * (r >> 2) + 4 * half + (r & 3);
+      wr[mt][r] = m < n_heads ? w[(int64_t)qi * n_heads + m] : 0.0f;
     }
   }
-  if (HIST) {
-    __syncthreads();
-    uint32_t *gh = hist + (int64_t)qi * kHistBins;
-    for (int i = threadIdx.x; i < kHistBins; i += 256) {
-      const uint32_t c = lhist[i];
-      if (c) atomic_add_agent(gh + i, c);
+
+  // Loads are coalesced: 16-byte piece j*64 + lane of the tile's rows (1 KB per
+  // wavefront instruction), i.e. key kk = (1024 j + 16 lane) / ROWB, chunk ch.
+  // They go through a wavefront-private LDS tile (chunk slots XOR-swizzled by
+  // the key index against bank conflicts) into the MFMA operand layout.
+  struct Raw {
+    u32x4 v[NLD];
+    float sc;
+  };
+  auto issue = [&](int tile, Raw &r) {
+    const int t0 = tile * 32;
+    const int bi = t0 / keys.block_size;   // a 32-token tile never straddles a block
+    const int64_t blk = keys.table ? (int64_t)keys.table[(int64_t)seq * keys.max_blocks + bi] : (int64_t)seq;
+    const int base_slot = t0 - bi * keys.block_size;
+    const int last = n - 1 - t0;           // clamp rows beyond the visible tokens
+#pragma unroll
+    for (int j = 0; j < NLD; ++j) {
+      const int byte = 1024 * j + 16 * lane;
+      const int kk = byte / ROWB, ch = (byte % ROWB) / 16;
+      const int kc = kk < last ? kk : last;
+      r.v[j] = load16(cache_row(keys, blk, base_slot + kc) + 16 * ch);
     }
+    if (FP8) {
+      const int kc = col < last ? col : last;
+      r.sc = keys.scale[blk * keys.scale_block_stride + base_slot + kc];
+    }
+  };
+  Raw cur, nxt;
+  issue(tile_begin, cur);
+  for (int it = 0; it < tiles_per_wave; ++it) {
+    const int t0 = (tile_begin + it) * 32;
+    if (t0 >= n) break;
+    const bool more = it + 1 < tiles_per_wave && t0 + 32 < n;
+    if (more) issue(tile_begin + it + 1, nxt);
+
+    // stage the tile, then read this lane's operand chunks back
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+#pragma unroll
+    for (int j = 0; j < NLD; ++j) {
+      const int byte = 1024 * j + 16 * lane;
+      const int kk = byte / ROWB, ch = (byte % ROWB) / 16;
+      *reinterpret_cast<u32x4 *>(stage + kk * ROWB + 16 * (ch ^ (kk & (CPR - 1)))) = cur.v[j];
+    }
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    bf16x8 b[KS];
+#pragma unroll
+    for (int j = 0; j < HALFC; ++j) {
+      const int ch = half * HALFC + j;
+      const u32x4 x = *reinterpret_cast<const u32x4 *>(stage + col * ROWB + 16 * (ch ^ (col & (CPR - 1))));
+      if (FP8) {
+        b[2 * j] = fp8x8_to_bf16x8(x[0], x[1]);
+        b[2 * j + 1] = fp8x8_to_bf16x8(x[2], x[3]);
+      } else {
+        b[j] = as_bf16x8(x);
+      }
+    }
+    const float sc = FP8 ? cur.sc : 1.0f;
+
+    float s = 0.0f;
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt) {
+      f32x16 acc = {};
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[mt][ks], b[ks], acc, 0, 0, 0);
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        float v = FP8 ? acc[r] * sc : acc[r];
+        v = fmaxf(v, 0.0f);
+        s = fmaf(wr[mt][r], v, s);
+      }
+    }
+    s += __shfl_xor(s, 32, 64);
+    const int t = t0 + col;
+    if (half == 0 && t < n) scores[(int64_t)qi * ld + t] = s;
+    if (half == 0 && t < n) lane_max = max(lane_max, order_key(s));
+    if (more) cur = nxt;
+  }
+  }
+
+  // Candidate bound for the top-k.  With G full wavefronts in the row (each
+  // covering tiles_per_wave * 32 tokens), a full wavefront reports the
+  // ceil(k / G)-th largest of its lanes' maxima: at least that many of its
+  // scores are >= it, so the row's minimum over full wavefronts leaves at least
+  // G * ceil(k / G) >= k scores at or above it.  Other wavefronts report
+  // 0xFFFFFFFF.
+  if (bounds) {
+    const int per_wave = tiles_per_wave * 32;
+    const int gfull = n / per_wave;
+    const int rank = gfull > 0 ? (topk + gfull - 1) / gfull : 0;
+    const int wid = blockIdx.x * 4 + wave;
+    uint32_t T = 0xFFFFFFFFu;
+    if ((wid + 1) * per_wave <= n && rank >= 1) {
+      if (rank <= 32) {
+        // rank-th largest of the 32 lane maxima (lanes 32..63 hold 0): extract
+        // the maximum rank times
+        uint32_t v = half == 0 ? lane_max : 0u;
+        for (int i = 0; i < rank; ++i) {
+          T = wave_max_u32(v);
+          const uint64_t hit = __ballot(v == T);
+          if (lane == __ffsll((unsigned long long)hit) - 1) v = 0;
+        }
+      } else {
+        T = 0;   // fewer than rank lane maxima: no useful bound from this wavefront
+      }
+    }
+    if (lane == 0) bounds[(int64_t)qi * gridDim.x * 4 + wid] = T;
   }
 }
 
 // fp32 queries and keys: one thread per key, fp32 FMA chains in a fixed order
 // (dims ascending, then heads ascending).
-template <int D, bool HIST>
+template <int D>
 __global__ __launch_bounds__(256) void scores_f32_kernel(float *__restrict__ scores, int64_t ld,
                                                          const float *__restrict__ q, const float *__restrict__ w,
                                                          CacheDev keys, const int32_t *__restrict__ q_seq,
                                                          int seq_ident, const int32_t *__restrict__ q_len,
-                                                         int n_heads, uint32_t *__restrict__ hist) {
+                                                         int n_heads) {
   __shared__ float lq[64 * D];
   __shared__ float lw[64];
-  __shared__ uint32_t lhist[HIST ? kHistBins : 1];
   const int qi = blockIdx.y;
   const int n = q_len[qi];
   for (int i = threadIdx.x; i < n_heads * D; i += 256) lq[i] = q[(int64_t)qi * n_heads * D + i];
   for (int i = threadIdx.x; i < n_heads; i += 256) lw[i] = w[(int64_t)qi * n_heads + i];
-  if (HIST)
-    for (int i = threadIdx.x; i < kHistBins; i += 256) lhist[i] = 0;
   __syncthreads();
   const int t = blockIdx.x * 256 + threadIdx.x;
   if (t < n) {
@@ -165,63 +222,50 @@ __global__ __launch_bounds__(256) void scores_f32_kernel(float *__restrict__ sco
       s = fmaf(lw[h], fmaxf(dot, 0.0f), s);
     }
     scores[(int64_t)qi * ld + t] = s;
-    if (HIST) atomicAdd(&lhist[order_key(s) >> kHistShift], 1u);
-  }
-  if (HIST) {
-    __syncthreads();
-    uint32_t *gh = hist + (int64_t)qi * kHistBins;
-    for (int i = threadIdx.x; i < kHistBins; i += 256) {
-      const uint32_t c = lhist[i];
-      if (c) atomic_add_agent(gh + i, c);
-    }
   }
 }
 
-template <bool FP8, int D, int MT, bool HIST>
+template <bool FP8, int D, int MT>
 hipError_t run_mfma(float *scores, int64_t ld, const void *q, const float *w, const CacheDev &keys,
                     const int32_t *q_seq, int seq_ident, const int32_t *q_len, int n_q, int n_heads, int max_len,
-                    uint32_t *hist, hipStream_t stream) {
+                    const ScoreBounds &sb, hipStream_t stream) {
   const int tiles = (max_len + 31) / 32;
-  // Aim at ~1024 workgroups of 4 wavefronts; each wavefront streams tiles_per_wave
-  // consecutive 32-key tiles so that its q fragment load is amortised.
-  const int64_t total = (int64_t)tiles * n_q;
-  int tpw = (int)((total + 4 * 1024 - 1) / (4 * 1024));
-  tpw = tpw < 1 ? 1 : (tpw > 64 ? 64 : tpw);
+  const int tpw = score_tiles_per_wave(n_q, max_len);
   const int gx = (tiles + 4 * tpw - 1) / (4 * tpw);
   dim3 grid(gx, n_q);
-  hipLaunchKernelGGL((scores_mfma_kernel<FP8, D, MT, HIST>), grid, dim3(256), 0, stream, scores, ld,
-                     static_cast<const uint16_t *>(q), w, keys, q_seq, seq_ident, q_len, n_heads, tpw, hist);
+  hipLaunchKernelGGL((scores_mfma_kernel<FP8, D, MT>), grid, dim3(256), 0, stream, scores, ld,
+                     static_cast<const uint16_t *>(q), w, keys, q_seq, seq_ident, q_len, n_heads, tpw, sb.bounds,
+                     sb.topk);
   return hipGetLastError();
 }
 
-template <int D, bool HIST>
+template <int D>
 hipError_t run_f32(float *scores, int64_t ld, const void *q, const float *w, const CacheDev &keys,
                    const int32_t *q_seq, int seq_ident, const int32_t *q_len, int n_q, int n_heads, int max_len,
-                   uint32_t *hist, hipStream_t stream) {
+                   hipStream_t stream) {
   dim3 grid((max_len + 255) / 256, n_q);
-  hipLaunchKernelGGL((scores_f32_kernel<D, HIST>), grid, dim3(256), 0, stream, scores, ld,
-                     static_cast<const float *>(q), w, keys, q_seq, seq_ident, q_len, n_heads, hist);
+  hipLaunchKernelGGL((scores_f32_kernel<D>), grid, dim3(256), 0, stream, scores, ld,
+                     static_cast<const float *>(q), w, keys, q_seq, seq_ident, q_len, n_heads);
   return hipGetLastError();
 }
 
-template <bool HIST>
 hipError_t dispatch(float *scores, int64_t ld, const void *q, int q_dt, const float *w, const CacheDev &keys,
                     int key_dt, const int32_t *q_seq, int seq_ident, const int32_t *q_len, int n_q, int n_heads,
-                    int max_len, uint32_t *hist, hipStream_t s) {
+                    int max_len, const ScoreBounds &sb, hipStream_t s) {
   const int D = keys.width;
   if (q_dt == kF32) {
     switch (D) {
-      case 32: return run_f32<32, HIST>(scores, ld, q, w, keys, q_seq, seq_ident, q_len, n_q, n_heads, max_len, hist, s);
-      case 64: return run_f32<64, HIST>(scores, ld, q, w, keys, q_seq, seq_ident, q_len, n_q, n_heads, max_len, hist, s);
-      case 96: return run_f32<96, HIST>(scores, ld, q, w, keys, q_seq, seq_ident, q_len, n_q, n_heads, max_len, hist, s);
-      case 128: return run_f32<128, HIST>(scores, ld, q, w, keys, q_seq, seq_ident, q_len, n_q, n_heads, max_len, hist, s);
+      case 32: return run_f32<32>(scores, ld, q, w, keys, q_seq, seq_ident, q_len, n_q, n_heads, max_len, s);
+      case 64: return run_f32<64>(scores, ld, q, w, keys, q_seq, seq_ident, q_len, n_q, n_heads, max_len, s);
+      case 96: return run_f32<96>(scores, ld, q, w, keys, q_seq, seq_ident, q_len, n_q, n_heads, max_len, s);
+      case 128: return run_f32<128>(scores, ld, q, w, keys, q_seq, seq_ident, q_len, n_q, n_heads, max_len, s);
       default: return hipErrorInvalidValue;
     }
   }
   const bool fp8 = key_dt == kFP8;
   const bool two = n_heads > 32;
 #define DSA_SC(F, DD, M)                                                                                    \
-  return run_mfma<F, DD, M, HIST>(scores, ld, q, w, keys, q_seq, seq_ident, q_len, n_q, n_heads, max_len, hist, s)
+  return run_mfma<F, DD, M>(scores, ld, q, w, keys, q_seq, seq_ident, q_len, n_q, n_heads, max_len, sb, s)
   if (D == 128) {
     if (fp8) { if (two) DSA_SC(true, 128, 2); DSA_SC(true, 128, 1); }
     if (two) DSA_SC(false, 128, 2);
@@ -240,13 +284,22 @@ hipError_t dispatch(float *scores, int64_t ld, const void *q, int q_dt, const fl
 
 hipError_t launch_index_scores(float *scores, int64_t ld, const void *q, int q_dt, const float *w,
                                const CacheDev &keys, int key_dt, const int32_t *q_seq, int seq_ident,
-                               const int32_t *q_len, int n_q, int n_heads, int max_len, uint32_t *hist,
+                               const int32_t *q_len, int n_q, int n_heads, int max_len, const ScoreBounds &sb,
                                hipStream_t stream) {
-  if (hist)
-    return dispatch<true>(scores, ld, q, q_dt, w, keys, key_dt, q_seq, seq_ident, q_len, n_q, n_heads, max_len, hist,
-                          stream);
-  return dispatch<false>(scores, ld, q, q_dt, w, keys, key_dt, q_seq, seq_ident, q_len, n_q, n_heads, max_len,
-                         nullptr, stream);
+  return dispatch(scores, ld, q, q_dt, w, keys, key_dt, q_seq, seq_ident, q_len, n_q, n_heads, max_len, sb, stream);
+}
+
+int score_tiles_per_wave(int n_q, int max_len) {
+  // ~512 workgroups of 4 wavefronts; each wavefront streams up to
+  // kMaxTilesPerWave consecutive 32-key tiles so its q fragment load is amortised.
+  const int64_t total = (int64_t)((max_len + 31) / 32) * n_q;
+  int tpw = (int)((total + 4 * 512 - 1) / (4 * 512));
+  return tpw < 1 ? 1 : (tpw > kMaxTilesPerWave ? kMaxTilesPerWave : tpw);
+}
+
+int score_groups_per_row(int n_q, int max_len) {
+  const int tpw = score_tiles_per_wave(n_q, max_len);
+  return 4 * (((max_len + 31) / 32 + 4 * tpw - 1) / (4 * tpw));
 }
 
 }  // namespace dsa

@@ -11,28 +11,40 @@ namespace dsa {
 enum DType { kF32 = 0, kBF16 = 1, kFP8 = 2 };
 
 // ---- indexer scores -------------------------------------------------------
-// hist (nullable): [n_q][kHistBins] uint32 counts of order_key(score) >> 20,
-// accumulated with atomics (must be zero on entry).
+// Optional candidate bounds for the top-k (bf16/fp8 keys only), one per
+// wavefront: bounds[q][g] <= the ceil(k / G)-th largest order_key of wavefront
+// g's scores (G = full wavefronts of the row), or 0xFFFFFFFF when wavefront
+// g's key range is not full.
+struct ScoreBounds {
+  uint32_t *bounds;  // [n_q][score_groups_per_row()] or nullptr
+  int topk;
+};
 hipError_t launch_index_scores(float *scores, int64_t ld, const void *q, int q_dt, const float *w,
                                const CacheDev &keys, int key_dt, const int32_t *q_seq, int seq_ident,
-                               const int32_t *q_len, int n_q, int n_heads, int max_len, uint32_t *hist,
+                               const int32_t *q_len, int n_q, int n_heads, int max_len, const ScoreBounds &sb,
                                hipStream_t stream);
+int score_tiles_per_wave(int n_q, int max_len);
+int score_groups_per_row(int n_q, int max_len);
 
 // ---- top-k ------------------------------------------------------------------
 struct TopkPlan {
   int n_q, k, max_len;
+  int groups;          // bound groups per row (bounds computed by the top-k itself)
+  int group;           // tokens per bound group
   int chunks;          // workgroups per query (1: each workgroup owns a whole row)
   int chunk;           // tokens per workgroup, multiple of 64
-  int words;           // 32-bit bitmap words per query (multiple of 2)
-  int cand_cap;        // candidate capacity per query
+  int words;           // 32-bit bitmap words per query in LDS (multiple of 4)
+  int cand_cap;        // candidate capacity per query in LDS
   size_t lds_bytes;    // dynamic LDS of the select kernel
-  // workspace carve-out (byte offsets)
-  size_t off_hist, off_ctrl, off_cand, off_sel, total;
+  // workspace carve-out (byte offsets; used when chunks > 1)
+  size_t off_ctrl, off_bounds, off_cand, total;
 };
 TopkPlan plan_topk(int n_q, int k, int max_len);
-// Builds the global histogram when plan.chunks > 1 and hist_ready is false.
+// bounds: per-row candidate bounds already computed (n_bounds per row), or
+// nullptr to compute them here.
 hipError_t launch_topk(int32_t *indices, int32_t *counts, const float *scores, int64_t ld, const int32_t *q_len,
-                       const TopkPlan &plan, void *workspace, bool hist_ready, hipStream_t stream);
+                       const TopkPlan &plan, void *workspace, const uint32_t *bounds, int n_bounds,
+                       hipStream_t stream);
 
 // ---- sparse MLA attention ---------------------------------------------------
 struct AttendPlan {

@@ -46,13 +46,38 @@ struct AttArgs {
   float scale_log2;  // softmax_scale * log2(e)
 };
 
+typedef __attribute__((__vector_size__(4 * sizeof(short)))) short i16x4;
+
+// Allreduce over the 16 lanes of a DPP row (row_ror 8, 4, 2, 1).
+__device__ __forceinline__ float row16_max(float x) {
+  x = fmaxf(x, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x128, 0xF, 0xF, false)));
+  x = fmaxf(x, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x124, 0xF, 0xF, false)));
+  x = fmaxf(x, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x122, 0xF, 0xF, false)));
+  x = fmaxf(x, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x121, 0xF, 0xF, false)));
+  return x;
+}
+__device__ __forceinline__ float row16_sum(float x) {
+  x += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x128, 0xF, 0xF, false));
+  x += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x124, 0xF, 0xF, false));
+  x += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x122, 0xF, 0xF, false));
+  x += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x121, 0xF, 0xF, false));
+  return x;
+}
+
+// Transposed LDS read (ds_read_b64_tr_b16): in each 16-lane group, lane p
+// names 4 bf16 of row base + p / 4 at columns col + 4 (p % 4); lane i of the
+// group receives rows base .. base + 3 of column col + i.
+__device__ __forceinline__ i16x4 lds_read_tr(const uint8_t *p) {
+  return __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+      (__attribute__((address_space(3))) i16x4 *)(reinterpret_cast<uintptr_t>(p)));
+}
+
 template <bool SPLIT>
 __global__ __launch_bounds__(256) void attend_bf16_kernel(AttArgs a) {
   __shared__ __align__(16) uint8_t lrows[kTile * kRowBytes];
   __shared__ __align__(16) uint16_t lp[2][kHG * kTile];  // P hi / lo, [head][row]
   __shared__ float red[2][4][kHG];
-  __shared__ const uint8_t *lptr[kTile];
-  __shared__ int lidx[kTile];
+  extern __shared__ __align__(16) const uint8_t *lptr[];  // [rows_per_split] row addresses (null: empty slot)
 
   // XCD-aware mapping: workgroup ids i, i+8, i+16, ... run on one XCD; give the
   // n_hg head groups of a (query, split) pair ids 8 apart.
@@ -70,6 +95,26 @@ __global__ __launch_bounds__(256) void attend_bf16_kernel(AttArgs a) {
   const int H = a.n_heads;
   const int h0 = hg * kHG;
   const int seq = seq_of(a.q_seq, qi, a.seq_ident);
+
+  const int j0 = sp * a.rows_per_split;
+  const int j1 = min(j0 + a.rows_per_split, a.k);
+  const int nrows = j1 - j0;
+  const int ntiles = (nrows + kTile - 1) / kTile;
+
+  // all row addresses of this split, once
+  {
+    const int32_t *idx_row = a.indices + (int64_t)qi * a.k + j0;
+    for (int r = tid; r < ntiles * kTile; r += 256) {
+      const int t = r < nrows ? idx_row[r] : -1;
+      const uint8_t *p = nullptr;
+      if (t >= 0) {
+        int slot;
+        const int64_t blk = cache_block(a.latent, seq, t, slot);
+        p = cache_row(a.latent, blk, slot);
+      }
+      lptr[r] = p;
+    }
+  }
 
   // q operand: head h0 + l16, dims 32*ks + 8*g4 + [0, 8)
   bf16x8 qa[kW / 32];
@@ -89,43 +134,30 @@ __global__ __launch_bounds__(256) void attend_bf16_kernel(AttArgs a) {
 #pragma unroll
   for (int nt = 0; nt < 8; ++nt) o[nt] = f32x4{0, 0, 0, 0};
 
-  const int j0 = sp * a.rows_per_split;
-  const int j1 = min(j0 + a.rows_per_split, a.k);
-  const int32_t *idx_row = a.indices + (int64_t)qi * a.k;
+  // gather: chunk c = tid + 256 i of the tile is row c / 72, bytes 16 (c % 72)
+  constexpr int kPer = kTile * kChunks / 256;  // 18
+  u32x4 v[kPer];
+  auto issue = [&](int tile) {
+#pragma unroll
+    for (int i = 0; i < kPer; ++i) {
+      const int c = tid + 256 * i;
+      const int r = c / kChunks, cc = c - r * kChunks;
+      const uint8_t *p = lptr[tile * kTile + r];
+      v[i] = p ? load16(p + cc * 16) : u32x4{0, 0, 0, 0};
+    }
+  };
+  __syncthreads();
+  if (ntiles > 0) issue(0);
 
-  for (int tb = j0; tb < j1; tb += kTile) {
-    if (tid < kTile) {
-      const int j = tb + tid;
-      const int t = j < j1 ? idx_row[j] : -1;
-      lidx[tid] = t;
-      const uint8_t *p = nullptr;
-      if (t >= 0) {
-        int slot;
-        const int64_t blk = cache_block(a.latent, seq, t, slot);
-        p = cache_row(a.latent, blk, slot);
-      }
-      lptr[tid] = p;
+  for (int tile = 0; tile < ntiles; ++tile) {
+#pragma unroll
+    for (int i = 0; i < kPer; ++i) {
+      const int c = tid + 256 * i;
+      const int r = c / kChunks, cc = c - r * kChunks;
+      *reinterpret_cast<u32x4 *>(lrows + r * kRowBytes + cc * 16) = v[i];
     }
     __syncthreads();
-    // gather the tile's rows into LDS (zeros for empty slots)
-    {
-      constexpr int kPer = kTile * kChunks / 256;  // 18
-      u32x4 v[kPer];
-#pragma unroll
-      for (int i = 0; i < kPer; ++i) {
-        const int c = tid + 256 * i;
-        const int r = c / kChunks, cc = c - r * kChunks;
-        const uint8_t *p = lptr[r];
-        v[i] = p ? load16(p + cc * 16) : u32x4{0, 0, 0, 0};
-      }
-#pragma unroll
-      for (int i = 0; i < kPer; ++i) {
-        const int c = tid + 256 * i;
-        const int r = c / kChunks, cc = c - r * kChunks;
-        *reinterpret_cast<u32x4 *>(lrows + r * kRowBytes + cc * 16) = v[i];
-      }
-    }
-    __syncthreads();
+    if (tile + 1 < ntiles) issue(tile + 1);   // in flight during this tile's math
 
     // QK^T: this wavefront's 16 rows
     const int row = wave * 16 + l16;
@@ -138,41 +170,33 @@ __global__ __launch_bounds__(256) void attend_bf16_kernel(AttArgs a) {
         sacc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qa[ks], b, sacc, 0, 0, 0);
       }
     }
-    const bool valid = lidx[row] >= 0;
+    const bool valid = lptr[tile * kTile + row] != nullptr;
     float z[4], mx[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       z[i] = valid ? sacc[i] * a.scale_log2 : -INFINITY;
-      mx[i] = z[i];
+      mx[i] = row16_max(z[i]);
     }
-#pragma unroll
-    for (int off = 1; off < 16; off <<= 1)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) mx[i] = fmaxf(mx[i], __shfl_xor(mx[i], off, 64));
     if (l16 == 0)
 #pragma unroll
       for (int i = 0; i < 4; ++i) red[0][wave][4 * g4 + i] = mx[i];
     __syncthreads();
 
-    float m_new[4], alpha[4], p[4], ps[4];
+    float m_new[4], alpha[4], ps[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int h = 4 * g4 + i;
-      float tm = fmaxf(fmaxf(red[0][0][h], red[0][1][h]), fmaxf(red[0][2][h], red[0][3][h]));
+      const float tm = fmaxf(fmaxf(red[0][0][h], red[0][1][h]), fmaxf(red[0][2][h], red[0][3][h]));
       m_new[i] = fmaxf(m_run[i], tm);
       const float mu = m_new[i] == -INFINITY ? 0.0f : m_new[i];
       alpha[i] = exp2f(m_run[i] - mu);
-      p[i] = exp2f(z[i] - mu);
-      const uint16_t hi = float_to_bf16_bits(p[i]);
-      const uint16_t lo = float_to_bf16_bits(p[i] - bf16_bits_to_float(hi));
+      const float p = exp2f(z[i] - mu);
+      const uint16_t hi = float_to_bf16_bits(p);
+      const uint16_t lo = float_to_bf16_bits(p - bf16_bits_to_float(hi));
       lp[0][h * kTile + row] = hi;
       lp[1][h * kTile + row] = lo;
-      ps[i] = p[i];
+      ps[i] = row16_sum(p);
     }
-#pragma unroll
-    for (int off = 1; off < 16; off <<= 1)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) ps[i] += __shfl_xor(ps[i], off, 64);
     if (l16 == 0)
 #pragma unroll
       for (int i = 0; i < 4; ++i) red[1][wave][4 * g4 + i] = ps[i];
@@ -189,22 +213,20 @@ __global__ __launch_bounds__(256) void attend_bf16_kernel(AttArgs a) {
 #pragma unroll
       for (int i = 0; i < 4; ++i) o[nt][i] *= alpha[i];
 
-    // PV: rows 32*ks2 + 8*g4 + e, columns 128*wave + 16*nt + l16
+    // PV: rows 32*ks2 + 8*g4 + e, columns 128*wave + 16*nt + l16; the V
+    // operand comes from two transposed LDS reads of 4 rows each
 #pragma unroll
     for (int ks2 = 0; ks2 < kTile / 32; ++ks2) {
       const bf16x8 ahi = as_bf16x8(*reinterpret_cast<const u32x4 *>(&lp[0][l16 * kTile + 32 * ks2 + 8 * g4]));
       const bf16x8 alo = as_bf16x8(*reinterpret_cast<const u32x4 *>(&lp[1][l16 * kTile + 32 * ks2 + 8 * g4]));
-      const uint8_t *vb = lrows + (32 * ks2 + 8 * g4) * kRowBytes + (128 * wave + l16) * 2;
+      const uint8_t *vb = lrows + (32 * ks2 + 8 * g4 + (l16 >> 2)) * kRowBytes + (128 * wave + 4 * (l16 & 3)) * 2;
 #pragma unroll
       for (int nt = 0; nt < 8; ++nt) {
-        uint32_t u[4];
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const uint32_t x0 = *reinterpret_cast<const uint16_t *>(vb + (2 * e) * kRowBytes + 32 * nt);
-          const uint32_t x1 = *reinterpret_cast<const uint16_t *>(vb + (2 * e + 1) * kRowBytes + 32 * nt);
-          u[e] = x0 | (x1 << 16);
-        }
-        const bf16x8 b = as_bf16x8(u32x4{u[0], u[1], u[2], u[3]});
+        const i16x4 v0 = lds_read_tr(vb + 32 * nt);
+        const i16x4 v1 = lds_read_tr(vb + 4 * kRowBytes + 32 * nt);
+        const bf16x8 b = __builtin_bit_cast(
+            bf16x8, (__attribute__((__vector_size__(8 * sizeof(short)))) short){v0[0], v0[1], v0[2], v0[3], v1[0],
+                                                                                 v1[1], v1[2], v1[3]});
         o[nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ahi, b, o[nt], 0, 0, 0);
         o[nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(alo, b, o[nt], 0, 0, 0);
       }
@@ -240,34 +262,53 @@ __global__ __launch_bounds__(256) void attend_bf16_kernel(AttArgs a) {
   }
 }
 
-// Combine split partials in split order.  One workgroup per (query, head).
+// Combine split partials in split order.  One workgroup per (query, head): one
+// wavefront turns the splits' (max, sum) into weights, then every thread sums
+// its 4 columns over the splits with all loads in flight.
+constexpr int kMaxSplits = 32;
 __global__ __launch_bounds__(128) void merge_kernel(float *__restrict__ out, float *__restrict__ lse,
                                                     const float *__restrict__ part_o,
                                                     const float *__restrict__ part_ml, int splits, int H, int L) {
-  const int qi = blockIdx.x / H, h = blockIdx.x - (blockIdx.x / H) * H;
-  float M = -INFINITY;
-  for (int s = 0; s < splits; ++s) M = fmaxf(M, part_ml[(((int64_t)qi * splits + s) * H + h) * 2]);
-  float *orow = out + ((int64_t)qi * H + h) * L;
-  if (M == -INFINITY) {
-    for (int c = threadIdx.x; c < L; c += 128) orow[c] = 0.0f;
-    if (threadIdx.x == 0 && lse) lse[(int64_t)qi * H + h] = -INFINITY;
-    return;
-  }
-  float Ls = 0.0f;
-  for (int s = 0; s < splits; ++s) {
-    const int64_t b = ((int64_t)qi * splits + s) * H + h;
-    Ls += exp2f(part_ml[b * 2] - M) * part_ml[b * 2 + 1];
-  }
-  const float inv = 1.0f / Ls;
-  for (int c = threadIdx.x; c < L; c += 128) {
-    float acc = 0.0f;
-    for (int s = 0; s < splits; ++s) {
-      const int64_t b = ((int64_t)qi * splits + s) * H + h;
-      acc += exp2f(part_ml[b * 2] - M) * part_o[b * L + c];
+  __shared__ float wgt[kMaxSplits];
+  __shared__ float tot[2];
+  const int qh = blockIdx.x;
+  const int qi = qh / H, h = qh - qi * H;
+  const int tid = threadIdx.x;
+  if (tid < 64) {
+    const bool ok = tid < splits;
+    const int64_t b = (((int64_t)qi * splits + (ok ? tid : 0)) * H + h) * 2;
+    const float m = ok ? part_ml[b] : -INFINITY;
+    const float l = ok ? part_ml[b + 1] : 0.0f;
+    float M = m;
+    for (int off = 32; off > 0; off >>= 1) M = fmaxf(M, __shfl_xor(M, off, 64));
+    const float w = (ok && M != -INFINITY) ? exp2f(m - M) : 0.0f;
+    float Ls = w * l;
+    for (int off = 32; off > 0; off >>= 1) Ls += __shfl_xor(Ls, off, 64);
+    if (ok) wgt[tid] = Ls > 0.0f ? w / Ls : 0.0f;
+    if (tid == 0) {
+      tot[0] = M;
+      tot[1] = Ls;
     }
-    orow[c] = acc * inv;
   }
-  if (threadIdx.x == 0 && lse) lse[(int64_t)qi * H + h] = (M + log2f(Ls)) * kLn2;
+  __syncthreads();
+  for (int c = tid * 4; c < L; c += 128 * 4) {
+    f32x4 v[kMaxSplits];
+#pragma unroll
+    for (int sp = 0; sp < kMaxSplits; ++sp)
+      if (sp < splits) v[sp] = *reinterpret_cast<const f32x4 *>(part_o + (((int64_t)qi * splits + sp) * H + h) * L + c);
+    f32x4 acc = {0, 0, 0, 0};
+#pragma unroll
+    for (int sp = 0; sp < kMaxSplits; ++sp)
+      if (sp < splits) {
+        const float w = wgt[sp];
+        acc[0] = fmaf(w, v[sp][0], acc[0]);
+        acc[1] = fmaf(w, v[sp][1], acc[1]);
+        acc[2] = fmaf(w, v[sp][2], acc[2]);
+        acc[3] = fmaf(w, v[sp][3], acc[3]);
+      }
+    *reinterpret_cast<f32x4 *>(out + (int64_t)qh * L + c) = acc;
+  }
+  if (tid == 0 && lse) lse[qh] = tot[1] > 0.0f ? (tot[0] + log2f(tot[1])) * kLn2 : -INFINITY;
 }
 
 // ------------------------------------------------------------------- f32 path
@@ -362,6 +403,7 @@ AttendPlan plan_attend(int n_q, int n_heads, int kv_lora, int width, int k, int 
     int s = (256 + n_q * n_hg - 1) / (n_q * n_hg);
     const int most = (tiles + 1) / 2;
     if (s > most) s = most;
+    if (s > kMaxSplits) s = kMaxSplits;
     if (s < 1) s = 1;
     const int tps = (tiles + s - 1) / s;
     p.rows_per_split = tps * kTile;
@@ -409,16 +451,17 @@ hipError_t launch_attend(float *out, float *lse, const void *q, int dt, const Ca
   uint8_t *ws = static_cast<uint8_t *>(workspace);
   const int groups = (a.pairs + 7) / 8;
   const dim3 grid(groups * 8 * a.n_hg);
+  const size_t lptr_bytes = (size_t)(plan.rows_per_split + kTile) * sizeof(void *);
   if (plan.splits > 1) {
     a.part_o = reinterpret_cast<float *>(ws + plan.off_part_o);
     a.part_ml = reinterpret_cast<float *>(ws + plan.off_part_ml);
-    hipLaunchKernelGGL(attend_bf16_kernel<true>, grid, dim3(256), 0, stream, a);
+    hipLaunchKernelGGL(attend_bf16_kernel<true>, grid, dim3(256), lptr_bytes, stream, a);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL(merge_kernel, dim3(n_q * n_heads), dim3(128), 0, stream, out, lse, a.part_o, a.part_ml,
                        plan.splits, n_heads, kv_lora);
   } else {
-    hipLaunchKernelGGL(attend_bf16_kernel<false>, grid, dim3(256), 0, stream, a);
+    hipLaunchKernelGGL(attend_bf16_kernel<false>, grid, dim3(256), lptr_bytes, stream, a);
   }
   return hipGetLastError();
 }

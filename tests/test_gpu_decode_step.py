@@ -20,6 +20,9 @@ CASES = {
     "bf16_paged": S(inputs.PAGED_DECODE, name="d2", wid=402, batch=4, seq_len=(100, 9000)),
     "fp8_ties": S(inputs.DECODE_128K_FP8, name="d3", wid=403, batch=2, seq_len=(10000, 10000)),
     "fp8_short": S(inputs.DECODE_128K_FP8, name="d4", wid=404, batch=3, seq_len=(1, 2100)),
+    # long enough (n > the 12288-candidate buffer) for the score kernel's bounds to filter
+    "fp8_long_bounded": S(inputs.DECODE_128K_FP8, name="d5", wid=405, batch=2, seq_len=(30000, 40000)),
+    "bf16_paged_long_bounded": S(inputs.PAGED_DECODE, name="d6", wid=406, batch=3, seq_len=(13000, 26000)),
 }
 
 
