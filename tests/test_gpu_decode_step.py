@@ -6,6 +6,8 @@ import numpy as np
 import pytest
 import torch
 
+import sparse_attention_14_amd as dsa
+
 import oracle
 from sparse_attention_14_amd import device, inputs
 
@@ -68,3 +70,64 @@ def test_decode_step_is_deterministic_and_workspace_reusable(case):
     b = gpu_decode_step(dp, ws=a[4])           # same workspace again
     for x, y in zip(a[:4], b[:4]):
         assert torch.equal(x.view(torch.int32), y.view(torch.int32))
+
+
+def test_key_ties_straddle_the_boundary():
+    """Copies of the rank-k token's key bytes and scale (rank by the oracle's
+    scores) are planted at 4 earlier and 4 later positions, so the GPU scores
+    them bit-identically and the boundary falls inside the tie group."""
+    wl = S(inputs.DECODE_128K_FP8, name="d7", wid=407, batch=2, seq_len=(20000, 30000), tie_fraction=0.0)
+    p = inputs.make_problem(wl)
+    ref = oracle.index_scores(p.q_idx, p.q_idx_dtype, p.w_idx, p.keys, p.q_seq, p.q_len)
+    rng = np.random.default_rng(9)
+    planted = {}
+    for b in range(p.n_q):
+        n = int(p.q_len[b])
+        order = np.argsort(-ref[b, :n], kind="stable")
+        t = int(order[p.topk - 1])
+        others = order[p.topk + 50:]       # overwrite only low-ranked tokens
+        dst = np.concatenate([rng.choice(others[others < t], 4, replace=False),
+                              rng.choice(others[others > t], 4, replace=False)])
+        for d in dst:
+            inputs.copy_token(p.keys, b, int(d), t)
+        planted[b] = (t, dst)
+    dp = device.upload(p)
+    print(f"case d7: planted boundary ties at {[(b, t) for b, (t, _) in planted.items()]}", flush=True)
+    out, lse, scores, idx, ws = gpu_decode_step(dp)
+    g_scores = scores.cpu().numpy()
+    for b, (t, dst) in planted.items():
+        assert np.all(g_scores[b, dst].view(np.uint32) == g_scores[b, t].view(np.uint32))
+        v = g_scores[b, t]
+        assert (g_scores[b, :p.q_len[b]] > v).sum() < p.topk < (g_scores[b, :p.q_len[b]] >= v).sum()
+    ref_idx, _ = oracle.topk(g_scores.astype(np.float64), p.q_len, p.topk)
+    assert np.array_equal(idx.cpu().numpy(), ref_idx)
+
+
+def test_decode_step_graph_replays_match_eager():
+    """The step captured in a HIP graph, replayed several times with other eager
+    work and synchronisations between replays, gives the eager result bit for bit."""
+    p = inputs.make_problem(CASES["fp8_long_bounded"])
+    dp = device.upload(p)
+    other = device.upload(inputs.make_problem(CASES["fp8_ties"]))
+    B, H, L = p.n_q, p.mla_heads, p.kv_lora
+    ref = gpu_decode_step(dp)
+    out = torch.empty(B, H, L, device="cuda")
+    lse = torch.empty(B, H, device="cuda")
+    idx = torch.empty(B, p.topk, dtype=torch.int32, device="cuda")
+    ws = torch.zeros(dsa.dsa_decode_step_workspace_size(B, p.max_len, p.topk, H, L), dtype=torch.uint8,
+                     device="cuda")
+    side = torch.cuda.Stream()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=side):
+        dsa.dsa_decode_step(out, lse, dp.q_idx, p.q_idx_dtype, dp.w_idx, dp.keys, dp.q_mla, p.q_mla_dtype,
+                            dp.latent, L, dp.q_len, p.max_len, p.topk, p.softmax_scale, ws, indices_out=idx)
+    torch.cuda.synchronize()
+    for rep in range(4):
+        out.fill_(float("nan"))
+        idx.fill_(-7)
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(idx, ref[3]), f"replay {rep}: indices differ"
+        assert torch.equal(out.view(torch.int32), ref[0].view(torch.int32)), f"replay {rep}: out differs"
+        assert torch.equal(lse.view(torch.int32), ref[1].view(torch.int32)), f"replay {rep}: lse differs"
+        gpu_decode_step(other)      # unrelated eager work between replays

@@ -117,3 +117,24 @@ def test_workspace_is_reusable():
         torch.cuda.synchronize()
         ref, _ = oracle.topk(arr.astype(np.float64), [60000] * 4, 2048)
         assert np.array_equal(idx2.cpu().numpy(), ref)
+
+
+def test_ties_straddle_the_boundary():
+    # The rank-k score is copied to 4 tokens before and 4 after the rank-k token,
+    # so a group of 9 equal scores straddles the boundary and the tie quota
+    # (lowest indices first) decides which of them are kept.
+    rng = np.random.default_rng(8)
+    n, k = 50000, 2048
+    s = rng.standard_normal((3, n)).astype(np.float32)
+    for r in range(3):
+        order = np.argsort(-s[r].astype(np.float64), kind="stable")
+        t = int(order[k - 1])
+        others = order[k + 50:]            # overwrite only low-ranked tokens
+        before = rng.choice(others[others < t], 4, replace=False)
+        after = rng.choice(others[others > t], 4, replace=False)
+        s[r, before] = s[r, t]
+        s[r, after] = s[r, t]
+        v = s[r, t]
+        assert (s[r] > v).sum() < k < (s[r] >= v).sum()
+    print("case: 9-way ties across the k boundary, 3 x 50000", flush=True)
+    _run(s, [n, n, n], k)
