@@ -150,6 +150,21 @@ __device__ __forceinline__ uint32_t wave_rank_bound(const uint32_t (&x)[N], uint
   return T;
 }
 
+// Candidate bounds for the top-k.  A row is cut into groups; each of its G
+// full groups reports a value with at least r distinct keys of the group at or
+// above it (r = bound_rank(k, G, most)), the rest report 0.  The ceil(k / r)-th
+// largest report then has at least k keys of the row at or above it.  r is half
+// again the smallest rank that would make the minimum report a bound, which
+// makes the chosen report a quantile of the groups instead of their minimum
+// (fewer candidates).  0: no bound (a group offers at most `most` ranks).
+__host__ __device__ inline int bound_rank(int k, int groups, int most) {
+  if (groups <= 0 || k <= 0) return 0;
+  const int base = (k + groups - 1) / groups;
+  if (base > most) return 0;
+  const int r = (3 * base + 1) / 2;
+  return r > most ? most : r;
+}
+
 // Block-wide exclusive prefix sum of one uint32 per thread, in thread order.
 // scratch: >= blockDim.x / 64 + 1 words of LDS.  Returns the exclusive prefix;
 // *total receives the block sum.  All threads must call it.

@@ -170,7 +170,7 @@ dsa_status dsa_topk(int32_t *indices, int32_t *counts, const float *scores, int6
   if (k > kMaxTopk || max_len > kMaxLenTopk) return DSA_ERR_UNSUPPORTED;
   const TopkPlan p = plan_topk(n_q, k, max_len);
   if (p.total > 0 && (!workspace || workspace_bytes < p.total)) return DSA_ERR_WORKSPACE_TOO_SMALL;
-  return from_hip(launch_topk(indices, counts, scores, ld_scores, q_len, p, workspace, nullptr, 0,
+  return from_hip(launch_topk(indices, counts, scores, ld_scores, q_len, p, workspace, nullptr, 0, 0,
                               static_cast<hipStream_t>(stream)));
 }
 
@@ -232,7 +232,8 @@ dsa_status dsa_decode_step(float *out, float *lse, const void *q_idx, dsa_dtype 
   hipError_t e = launch_index_scores(scores, ld, q_idx, q_idx_dtype, w_idx, to_dev(keys), keys->dtype, nullptr, 1,
                                      seq_len, batch, idx_heads, max_len, ScoreBounds{bounds, k}, st);
   if (e != hipSuccess) return DSA_ERR_DEVICE;
-  e = launch_topk(idx, nullptr, scores, ld, seq_len, L.tp, ws_topk, bounds, L.n_bounds, st);
+  e = launch_topk(idx, nullptr, scores, ld, seq_len, L.tp, ws_topk, bounds, L.n_bounds,
+                  score_group_tokens(batch, max_len), st);
   if (e != hipSuccess) return DSA_ERR_DEVICE;
   e = launch_attend(out, lse, q_mla, q_mla_dtype, to_dev(latent), kv_lora, idx, k, nullptr, 1, batch, mla_heads,
                     softmax_scale, A.ap, ws_att, st);

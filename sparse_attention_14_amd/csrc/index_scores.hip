@@ -154,30 +154,24 @@ __global__ __launch_bounds__(256) void scores_mfma_kernel(float *__restrict__ sc
   }
   }
 
-  // Candidate bound for the top-k.  With G full wavefronts in the row (each
-  // covering tiles_per_wave * 32 tokens), a full wavefront reports the
-  // ceil(k / G)-th largest of its lanes' maxima: at least that many of its
-  // scores are >= it, so the row's minimum over full wavefronts leaves at least
-  // G * ceil(k / G) >= k scores at or above it.  Other wavefronts report
-  // 0xFFFFFFFF.
+  // Candidate bound for the top-k: a full wavefront (all tiles_per_wave * 32
+  // of its tokens visible) reports the r-th largest of its lanes' maxima,
+  // r = bound_rank(k, G, 32) with G full wavefronts in the row; each lane
+  // maximum is the score of a distinct token.  Other wavefronts report 0.
   if (bounds) {
     const int per_wave = tiles_per_wave * 32;
     const int gfull = n / per_wave;
-    const int rank = gfull > 0 ? (topk + gfull - 1) / gfull : 0;
+    const int rank = bound_rank(topk, gfull, 32);
     const int wid = blockIdx.x * 4 + wave;
-    uint32_t T = 0xFFFFFFFFu;
+    uint32_t T = 0;
     if ((wid + 1) * per_wave <= n && rank >= 1) {
-      if (rank <= 32) {
-        // rank-th largest of the 32 lane maxima (lanes 32..63 hold 0): extract
-        // the maximum rank times
-        uint32_t v = half == 0 ? lane_max : 0u;
-        for (int i = 0; i < rank; ++i) {
-          T = wave_max_u32(v);
-          const uint64_t hit = __ballot(v == T);
-          if (lane == __ffsll((unsigned long long)hit) - 1) v = 0;
-        }
-      } else {
-        T = 0;   // fewer than rank lane maxima: no useful bound from this wavefront
+      // rank-th largest of the 32 lane maxima (lanes 32..63 hold 0): extract
+      // the maximum rank times
+      uint32_t v = half == 0 ? lane_max : 0u;
+      for (int i = 0; i < rank; ++i) {
+        T = wave_max_u32(v);
+        const uint64_t hit = __ballot(v == T);
+        if (lane == __ffsll((unsigned long long)hit) - 1) v = 0;
       }
     }
     if (lane == 0) bounds[(int64_t)qi * gridDim.x * 4 + wid] = T;
@@ -296,6 +290,8 @@ int score_tiles_per_wave(int n_q, int max_len) {
   int tpw = (int)((total + 4 * 512 - 1) / (4 * 512));
   return tpw < 1 ? 1 : (tpw > kMaxTilesPerWave ? kMaxTilesPerWave : tpw);
 }
+
+int score_group_tokens(int n_q, int max_len) { return 32 * score_tiles_per_wave(n_q, max_len); }
 
 int score_groups_per_row(int n_q, int max_len) {
   const int tpw = score_tiles_per_wave(n_q, max_len);

@@ -12,9 +12,9 @@ enum DType { kF32 = 0, kBF16 = 1, kFP8 = 2 };
 
 // ---- indexer scores -------------------------------------------------------
 // Optional candidate bounds for the top-k (bf16/fp8 keys only), one per
-// wavefront: bounds[q][g] <= the ceil(k / G)-th largest order_key of wavefront
-// g's scores (G = full wavefronts of the row), or 0xFFFFFFFF when wavefront
-// g's key range is not full.
+// wavefront of score_group_tokens() consecutive tokens: bounds[q][g] has at
+// least bound_rank(k, G, 32) of wavefront g's keys at or above it when the
+// wavefront's tokens are all visible (G such wavefronts in the row), else 0.
 struct ScoreBounds {
   uint32_t *bounds;  // [n_q][score_groups_per_row()] or nullptr
   int topk;
@@ -25,6 +25,7 @@ hipError_t launch_index_scores(float *scores, int64_t ld, const void *q, int q_d
                                hipStream_t stream);
 int score_tiles_per_wave(int n_q, int max_len);
 int score_groups_per_row(int n_q, int max_len);
+int score_group_tokens(int n_q, int max_len);
 
 // ---- top-k ------------------------------------------------------------------
 struct TopkPlan {
@@ -33,17 +34,16 @@ struct TopkPlan {
   int group;           // tokens per bound group
   int chunks;          // workgroups per query (1: each workgroup owns a whole row)
   int chunk;           // tokens per workgroup, multiple of 64
-  int words;           // 32-bit bitmap words per query in LDS (multiple of 4)
-  int cand_cap;        // candidate capacity per query in LDS
+  int local_cap;       // LDS candidates per row (one workgroup per row)
   size_t lds_bytes;    // dynamic LDS of the select kernel
   // workspace carve-out (byte offsets; used when chunks > 1)
-  size_t off_ctrl, off_bounds, off_cand, total;
+  size_t off_tlo, off_count, off_cmax, off_bounds, off_cand, total;
 };
 TopkPlan plan_topk(int n_q, int k, int max_len);
-// bounds: per-row candidate bounds already computed (n_bounds per row), or
-// nullptr to compute them here.
+// bounds: per-row candidate bounds already computed (n_bounds per row, each
+// over group_tokens tokens, see ScoreBounds), or nullptr to compute them here.
 hipError_t launch_topk(int32_t *indices, int32_t *counts, const float *scores, int64_t ld, const int32_t *q_len,
-                       const TopkPlan &plan, void *workspace, const uint32_t *bounds, int n_bounds,
+                       const TopkPlan &plan, void *workspace, const uint32_t *bounds, int n_bounds, int group_tokens,
                        hipStream_t stream);
 
 // ---- sparse MLA attention ---------------------------------------------------

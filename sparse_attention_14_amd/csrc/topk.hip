@@ -9,95 +9,78 @@
 // exact and deterministic.  Method:
 //  1. Candidate bound.  The row is cut into G groups; each full group reports a
 //     lower bound on its ceil(k / G)-th largest key (the score kernel does this
-//     as it writes the scores; otherwise bound_kernel does).  At least k keys of
-//     the row are >= T_lo = the minimum of these, and in practice only ~1.5-3 k.
-//     Rows that fit the candidate buffer use T_lo = 0 (every score).
-//  2. Filter.  The workgroups of a row scan their chunks, reserve room in the
-//     row's candidate array with one atomic each, and write the (key, token)
-//     pairs with key >= T_lo there.
-//  3. The last workgroup of the row (one atomic per workgroup) loads the
-//     candidates into registers and finds the exact k-th key T and the tie quota
-//     r = k - #(> T) with up to three 12-bit radix levels over a window that
-//     spans the candidates' keys.  If the candidates do not fit, the same
-//     selection runs over the whole row in memory instead: exact, slower.
-//  4. Ordered emission: candidates above T set a "sel" bit and candidates equal
-//     to T an "eq" bit in per-row LDS bitmaps; one pass over the bitmap words in
-//     token order keeps all sel bits and the first r eq bits (a block-wide
-//     prefix count of eq bits gives each word its quota).
-// When one workgroup owns a row (many rows, or short rows) it does all of this
-// alone, with candidates in LDS and no global state.  The last workgroup leaves
-// the row's counters zeroed for the next call.
+//     as it writes the scores; otherwise bound_kernel does, or one wavefront
+//     estimates it from strided samples).  With group bounds at least k keys of
+//     the row are >= T_lo = their minimum; a sampled estimate may miss, which
+//     only sends the row to the exact fallback below.  Rows that fit the
+//     candidate budget use T_lo = 0.
+//  2. Filter.  Workgroups scan the row in rounds of one score per thread and
+//     compact the (key, token) pairs with key >= T_lo in token order (wavefront
+//     ballots plus one prefix over the round totals).  For few long rows a
+//     filter kernel spreads each row over many workgroups, each writing its
+//     candidates and their count to a region of its own, and a finishing kernel
+//     takes over; otherwise one workgroup per row does both in LDS.
+//  3. Threshold.  Candidate j of the row (in token order) sits in thread
+//     j % NT, register slot j / NT.  12-bit radix levels over the window
+//     [T_lo, max key] give the exact k-th key T and the tie quota
+//     r = k - #(key > T).
+//  4. Ordered emission.  Keys > T, and the first r keys == T in token order,
+//     are kept; one prefix over (#>T, #==T) in candidate order gives every kept
+//     token its output slot.
+// Rows whose candidates do not fit (or a sampled bound that keeps fewer than k)
+// run steps 3-4 over the whole row in memory instead: exact, slower.
+//
+// The per-element code is branch-free (select instead of divergent branches,
+// a dump bin for histogram entries that do not count): with few wavefronts per
+// SIMD, divergent control flow per element costs far more than the arithmetic.
 #include "kernels.hpp"
 
 namespace dsa {
 namespace {
 
-constexpr int kSelThreads = 512;
-constexpr int kPerThread = 8;              // scores loaded per thread per pass
-constexpr int kCandPerThread = 24;         // candidates held per thread
-constexpr int kGroup = 1024;               // tokens per bound group (bound_kernel)
+constexpr int kRegCap = 12288;                  // candidates per row held in registers
+constexpr int kBins = kHistBins;                // 4096 (12-bit digits)
+constexpr int kCoarse = kBins + 64;             // 64 super-bins of 64 bins each; before them, per-lane
+                                                // dump slots for elements that do not count, after
+                                                // them the same for the super-bins
+constexpr int kHistWords = kCoarse + 128;
+constexpr int kGroup = 1024;                    // tokens per bound group (bound_kernel)
 constexpr int kSamples = 1024;
+constexpr int kMaxChunks = 256;
+constexpr int kFilterThreads = 512;
+constexpr int kPassRounds = 8;                  // filter rounds per pass
+constexpr int kPass = kFilterThreads * kPassRounds;   // 4096 scores per pass
+constexpr int kFinishThreads = 1024;            // finishing kernel of a spread row
+constexpr int kLocalThreads = 512;              // one workgroup per row
+constexpr int kLocalCap = 14 * kLocalThreads;   // LDS candidates of a one-workgroup row (7168)
 
-__device__ __forceinline__ uint32_t lowest_bits(uint32_t e, uint32_t take) {
-  uint32_t r = 0;
-  for (uint32_t i = 0; i < take; ++i) {
-    const uint32_t lb = e & (~e + 1u);
-    r |= lb;
-    e ^= lb;
-  }
-  return r;
-}
+// LDS carve-up (32-bit words), the same for every kernel.
+constexpr int kTotWords = 200;                  // >= rounds * waves + 1 for every use (192 + 1)
+constexpr int kOffHist = 0;
+constexpr int kOffScratch = kOffHist + kHistWords;
+constexpr int kOffShv = kOffScratch + 64;
+constexpr int kOffTot = kOffShv + 64;
+constexpr int kOffCpre = kOffTot + 2 * kTotWords;
+constexpr int kOffCmap = kOffCpre + kMaxChunks + 4;
+constexpr int kOffCand = (kOffCmap + kRegCap / 64 + 4 + 3) / 4 * 4;   // uint2 array, 16-byte aligned
+constexpr int kFixedWords = kOffCand;
 
-// One histogram increment; a wavefront whose active lanes all hit the same bin
-// (ties, narrow windows) adds once instead of serialising on one LDS address.
-__device__ __forceinline__ void hist_add(uint32_t *h, uint32_t bin) {
-  const uint64_t act = __ballot(1);
-  const uint32_t first = (uint32_t)__builtin_amdgcn_readfirstlane((int)bin);
-  if (__ballot(bin == first) == act) {
-    if ((int)(threadIdx.x & 63) == __ffsll((unsigned long long)act) - 1) atomicAdd(&h[first], (uint32_t)__popcll(act));
-  } else {
-    atomicAdd(&h[bin], 1u);
-  }
-}
+struct Lds {
+  uint32_t *hist, *scratch, *shv, *tot0, *tot1, *cpre, *cmap;
+  uint2 *cand;
+};
 
-// Among h[0..nbins), find the highest bin b whose suffix count (bins >= b)
-// reaches `need` (1 <= need <= total).  out[0] = b, out[1] = count of bins > b.
-__device__ void find_from_top(const uint32_t *h, int nbins, uint32_t need, uint32_t *scratch, uint32_t *out) {
-  const int per = nbins >= kSelThreads ? nbins / kSelThreads : 1;
-  const int t = threadIdx.x;
-  const bool owns = t * per < nbins;
-  const int hi = nbins - t * per;  // thread t owns bins [hi - per, hi), counted from the top
-  uint32_t hv[kHistBins / kSelThreads];
-  uint32_t local = 0;
-#pragma unroll
-  for (int j = 0; j < kHistBins / kSelThreads; ++j) {
-    hv[j] = (owns && j < per) ? h[hi - 1 - j] : 0u;
-    local += hv[j];
-  }
-  uint32_t tot;
-  const uint32_t before = block_exclusive_scan(local, scratch, &tot);
-  if (owns && before < need && before + local >= need) {
-    uint32_t run = before;
-#pragma unroll
-    for (int j = 0; j < kHistBins / kSelThreads; ++j) {
-      if (j < per && run < need && run + hv[j] >= need) {
-        out[0] = (uint32_t)(hi - 1 - j);
-        out[1] = run;
-      }
-      run += hv[j];
-    }
-  }
-  __syncthreads();
-}
-
-__device__ __forceinline__ uint32_t block_max(uint32_t v, uint32_t *scratch) {
-  const uint32_t m = wave_max_u32(v);
-  if ((threadIdx.x & 63) == 0) scratch[threadIdx.x >> 6] = m;
-  __syncthreads();
-  uint32_t r = 0;
-  for (int i = 0; i < (int)(blockDim.x >> 6); ++i) r = max(r, scratch[i]);
-  __syncthreads();
-  return r;
+__device__ __forceinline__ Lds carve(uint32_t *lds) {
+  Lds L;
+  L.hist = lds + kOffHist;
+  L.scratch = lds + kOffScratch;
+  L.shv = lds + kOffShv;
+  L.tot0 = lds + kOffTot;
+  L.tot1 = lds + kOffTot + kTotWords;
+  L.cpre = lds + kOffCpre;
+  L.cmap = lds + kOffCmap;
+  L.cand = reinterpret_cast<uint2 *>(lds + kOffCand);
+  return L;
 }
 
 struct SelectArgs {
@@ -109,151 +92,278 @@ struct SelectArgs {
   const uint32_t *bounds;  // [n_q][n_bounds] group bounds, or nullptr
   int n_bounds;
   int k;
-  int chunk;       // tokens per workgroup (multiple of 64)
-  int chunks;      // workgroups per row
-  int words;       // bitmap words allocated per row (LDS)
-  int cand_cap;    // candidate capacity per row
-  uint32_t *ctrl;  // [n_q][4]: done counter, candidate counter
-  uint2 *cand;     // [n_q][cand_cap]  (key, token)
+  int chunk;        // tokens per filter workgroup (<= kPass, multiple of 64)
+  int chunks;       // filter workgroups per row
+  int local_cap;    // LDS candidate capacity (one workgroup per row)
+  int group_tokens; // tokens per bound group
+  int bound_most;   // largest rank a bound group can report
+  uint32_t *ccount; // [n_q][chunks] candidates per chunk
+  uint32_t *cmax;   // [n_q][chunks] largest candidate key per chunk
+  uint32_t *tlo;    // [n_q] the row's candidate bound
+  uint2 *cand;      // [n_q][chunks][chunk] (key, token) per chunk
 };
 
-// Calls f(key, token) for every score of the row (the exact path when the
-// candidates do not fit); loads are issued kPerThread at a time.
-template <typename F>
-__device__ __forceinline__ void for_each_in_row(const float *row, int n, F &&f) {
-  for (int g0 = 0; g0 < n; g0 += kPerThread * kSelThreads) {
-    float v[kPerThread];
+// Number of set bits of `mask` below this lane.
+__device__ __forceinline__ uint32_t lanes_below(uint64_t mask) {
+  return __builtin_amdgcn_mbcnt_hi((uint32_t)(mask >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)mask, 0u));
+}
+
+// Order-preserving prefix over `rounds` (uniform, <= R) rounds of one element per
+// thread: element (m, tid) precedes (m', tid') when m < m' or (m == m' and
+// tid < tid').  flag(m) returns 1 (counted in the low half), 1 << 16 (high half)
+// or 0.  pre[m] receives the packed count of earlier elements (both halves); the
+// packed total is returned.  Each half must stay below 65536.  tot: LDS of
+// R * waves + 1 words, not written again before one more barrier.  Two barriers.
+template <int NT, int R, typename F>
+__device__ __forceinline__ uint32_t ordered_prefix(F &&flag, int rounds, uint32_t (&pre)[R], uint32_t *tot) {
+  constexpr int W = NT / 64;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  uint32_t totv = 0;   // lane m: packed total of round m in this wavefront
 #pragma unroll
-    for (int i = 0; i < kPerThread; ++i) {
-      const int t = g0 + threadIdx.x + kSelThreads * i;
-      v[i] = t < n ? row[t] : 0.0f;
+  for (int m = 0; m < R; ++m) {
+    if (m < rounds) {
+      const uint32_t v = flag(m);
+      const uint64_t lo = __ballot((v & 0xFFFFu) != 0u);
+      const uint64_t hi = __ballot((v >> 16) != 0u);
+      pre[m] = lanes_below(lo) | (lanes_below(hi) << 16);
+      const uint32_t t = (uint32_t)__popcll(lo) | ((uint32_t)__popcll(hi) << 16);
+      totv = lane == m ? t : totv;
     }
+  }
+  if (lane < rounds) tot[lane * W + wave] = totv;
+  __syncthreads();
+  if (wave == 0) {
+    const int E = rounds * W;
+    constexpr int PL = (R * W + 63) / 64;
+    uint32_t v[PL];
+    uint32_t s = 0;
 #pragma unroll
-    for (int i = 0; i < kPerThread; ++i) {
-      const int t = g0 + threadIdx.x + kSelThreads * i;
-      if (t < n) f(order_key(v[i]), (uint32_t)t);
+    for (int i = 0; i < PL; ++i) {
+      const int e = lane * PL + i;
+      v[i] = e < E ? tot[e] : 0u;
+      s += v[i];
     }
+    const uint32_t incl = wave_inclusive_scan(s);
+    uint32_t run = incl - s;
+#pragma unroll
+    for (int i = 0; i < PL; ++i) {
+      const int e = lane * PL + i;
+      if (e < E) tot[e] = run;
+      run += v[i];
+    }
+    if (lane == 63) tot[R * W] = incl;
+  }
+  __syncthreads();
+#pragma unroll
+  for (int m = 0; m < R; ++m)
+    if (m < rounds) pre[m] += tot[m * W + wave];
+  return tot[R * W];
+}
+
+template <int NT>
+__device__ __forceinline__ void zero_hist(uint32_t *h) {
+  uint4 *h4 = reinterpret_cast<uint4 *>(h);
+#pragma unroll
+  for (int i = 0; i < kBins / 4 / NT; ++i) h4[threadIdx.x + NT * i] = make_uint4(0, 0, 0, 0);
+  if (threadIdx.x < 64) h[kCoarse + threadIdx.x] = 0u;
+}
+
+// Highest bin b whose count of keys in bins >= b reaches `need` (1 <= need <=
+// total): the first wavefront scans the 64 super-bins from the top, then the 64
+// bins of the super-bin found.  Writes shv[0] = b, shv[1] = count in bins > b;
+// the caller synchronises before reading them.
+__device__ __forceinline__ void find_from_top(const uint32_t *h, uint32_t need, uint32_t *shv) {
+  if (threadIdx.x >= 64) return;
+  const int lane = threadIdx.x;
+  const uint32_t c = h[kCoarse + 63 - lane];   // lane 0: the highest super-bin
+  const uint32_t ci = wave_inclusive_scan(c);
+  const int l1 = __ffsll((unsigned long long)__ballot(ci >= need)) - 1;
+  const uint32_t sb = 63u - (uint32_t)l1;
+  const uint32_t above = (uint32_t)__builtin_amdgcn_readlane((int)(ci - c), l1);
+  const uint32_t f = h[sb * 64 + 63 - lane];
+  const uint32_t fi = wave_inclusive_scan(f) + above;
+  const int l2 = __ffsll((unsigned long long)__ballot(fi >= need)) - 1;
+  const uint32_t above2 = (uint32_t)__builtin_amdgcn_readlane((int)(fi - f), l2);
+  if (lane == 0) {
+    shv[0] = sb * 64 + 63u - (uint32_t)l2;
+    shv[1] = above2;
   }
 }
 
-// Exact selection of the k best, then emission of the ascending index list.
-// When `in_regs`, this thread's candidates are ck/ct[0..nc), every key >= the
-// k-th key of the row is among the block's candidates, and all of them are
-// >= lo; otherwise the whole row is read from memory (lo = 0).
-__device__ void finish_row(const SelectArgs &a, int qi, int n, bool in_regs, const uint32_t *ck, const uint32_t *ct,
-                           int nc, uint32_t lo, const float *row, uint32_t *lh, uint32_t *scratch, uint32_t *shv,
-                           uint32_t *sel_l, uint32_t *eq_l) {
-  const int tid = threadIdx.x;
-  const int k = a.k;
-  const int n_words = (n + 31) >> 5;
-  for (int w = tid; w < n_words; w += kSelThreads) {
-    sel_l[w] = 0;
-    eq_l[w] = 0;
-  }
-  auto visit = [&](auto &&f) {
-    if (in_regs) {
-#pragma unroll
-      for (int m = 0; m < kCandPerThread; ++m)
-        if (m < nc) f(ck[m], ct[m]);
-    } else {
-      for_each_in_row(row, n, f);
-    }
-  };
+template <int NT>
+__device__ __forceinline__ uint32_t block_max(uint32_t v, uint32_t *scratch) {
+  const uint32_t m = wave_max_u32(v);
+  if ((threadIdx.x & 63) == 0) scratch[threadIdx.x >> 6] = m;
+  __syncthreads();
   uint32_t r = 0;
-  if (n <= k) {
-    // every token is kept
-    for (int w = tid; w < n_words; w += kSelThreads) {
-      const int rem = n - 32 * w;
-      sel_l[w] = rem >= 32 ? 0xFFFFFFFFu : ((1u << rem) - 1u);
-    }
-    __syncthreads();
-  } else {
-    if (!in_regs) lo = 0;
-    // key window [lo, hi] of the source; levels of 12 bits from its top
-    uint32_t mx = 0;
-    visit([&](uint32_t key, uint32_t) { mx = max(mx, key); });
-    const uint32_t range = block_max(mx, scratch) - lo;
-    const int width = range ? 32 - __clz(range) : 0;   // bits of (key - lo)
-    // level i histograms bits [sh, prev) of (key - lo) among the keys whose
-    // bits >= prev match the prefix selected so far
-    int prev = 32;
-    int sh = width > 12 ? width - 12 : 0;
-    uint32_t base = 0;       // selected bits of (key - lo) at and above prev
-    uint32_t need = (uint32_t)k;
-    while (true) {
-      for (int i = tid; i < kHistBins; i += kSelThreads) lh[i] = 0;
-      __syncthreads();
-      const uint32_t mask = prev - sh >= 12 ? 0xFFFu : ((1u << (prev - sh)) - 1u);
-      visit([&](uint32_t key, uint32_t) {
-        const uint32_t off = key - lo;
-        if (prev == 32 || (off >> prev) == (base >> prev)) hist_add(lh, (off >> sh) & mask);
-      });
-      __syncthreads();
-      find_from_top(lh, kHistBins, need, scratch, shv);
-      base |= (shv[0] & 0xFFFu) << sh;
-      need -= shv[1];
-      __syncthreads();
-      if (sh == 0) break;
-      prev = sh;
-      sh = sh > 12 ? sh - 12 : 0;
-    }
-    const uint32_t T = lo + base;
-    r = need;
-    // classify
-    visit([&](uint32_t key, uint32_t t) {
-      if (key > T) atomicOr(&sel_l[t >> 5], 1u << (t & 31));
-      else if (key == T) atomicOr(&eq_l[t >> 5], 1u << (t & 31));
-    });
-    __syncthreads();
-  }
+#pragma unroll
+  for (int i = 0; i < NT / 64; ++i) r = max(r, scratch[i]);
+  __syncthreads();
+  return r;
+}
 
-  // ordered emission: all sel bits, and the first r eq bits in token order
-  constexpr int kWordsPerThread = 16;  // words <= 8192
-  const int per = (n_words + kSelThreads - 1) / kSelThreads;
-  const int w0 = min(tid * per, n_words), w1 = min(w0 + per, n_words);
-  uint32_t ev[kWordsPerThread], sv[kWordsPerThread];
-  uint32_t eqc = 0;
-#pragma unroll
-  for (int j = 0; j < kWordsPerThread; ++j) {
-    const bool ok = w0 + j < w1;
-    ev[j] = ok ? eq_l[w0 + j] : 0u;
-    sv[j] = ok ? sel_l[w0 + j] : 0u;
-    eqc += __popc(ev[j]);
+// Exact k-th largest key T and tie quota r = k - #(key > T) among the keys that
+// hist_pass(off_lo, himask, base, sh, mask) adds to L.hist (every thread its own
+// share: bin ((key - lo) >> sh) & mask of the keys whose (key - lo) agrees with
+// base on the bits in himask, the dump bin for the rest), all keys in [lo, mx],
+// at least k of them.  Radix levels of 12 bits from the top of the window.
+template <int NT, typename H>
+__device__ void radix_threshold(H &&hist_pass, uint32_t lo, uint32_t mx, uint32_t k, const Lds &L, uint32_t &T,
+                                uint32_t &r) {
+  const uint32_t range = mx - lo;
+  const int width = range ? 32 - __clz(range) : 0;   // bits of (key - lo)
+  // each level histograms bits [sh, prev) of (key - lo) among the keys whose
+  // bits >= prev equal the prefix chosen so far
+  int prev = 32;
+  int sh = width > 12 ? width - 12 : 0;
+  uint32_t base = 0;
+  uint32_t need = k;
+  while (true) {
+    zero_hist<NT>(L.hist);
+    __syncthreads();
+    const uint32_t mask = prev - sh >= 12 ? 0xFFFu : ((1u << (prev - sh)) - 1u);
+    const uint32_t himask = prev >= 32 ? 0u : (0xFFFFFFFFu << prev);
+    hist_pass(himask, base, sh, mask);
+    __syncthreads();
+    find_from_top(L.hist, need, L.shv);
+    __syncthreads();
+    base |= L.shv[0] << sh;
+    need -= L.shv[1];
+    if (sh == 0) break;
+    prev = sh;
+    sh = sh > 12 ? sh - 12 : 0;
   }
-  uint32_t dummy;
-  uint32_t eq_before = block_exclusive_scan(eqc, scratch, &dummy);
-  uint32_t cnt = 0;
+  T = lo + base;
+  r = need;
+}
+
+// Histogram increments of one key (branch-free): its bin and super-bin, or
+// this lane's dump slots when it does not count.
+__device__ __forceinline__ void hist_add(uint32_t *h, bool valid, uint32_t key, uint32_t lo, uint32_t himask,
+                                         uint32_t base, int sh, uint32_t mask) {
+  const uint32_t off = key - lo;
+  const bool in = valid && ((off ^ base) & himask) == 0u;
+  const uint32_t bin = (off >> sh) & mask;
+  const uint32_t lane = threadIdx.x & 63;
+  atomicAdd(&h[in ? bin : kBins + lane], 1u);
+  atomicAdd(&h[in ? kCoarse + (bin >> 6) : kCoarse + 64 + lane], 1u);
+}
+
+// Rows with n <= k keep every token.
+template <int NT>
+__device__ void emit_all(const SelectArgs &a, int qi, int n) {
+  int32_t *out = a.indices + (int64_t)qi * a.k;
+  for (int p = threadIdx.x; p < a.k; p += NT) out[p] = p < n ? p : -1;
+  if (threadIdx.x == 0 && a.counts) a.counts[qi] = n;
+}
+
+// Steps 3-4 on candidates held in registers: candidate j < C (token order) is
+// ck/ct[j / NT] of thread j % NT; all keys in [lo, mx], C >= k, and every key
+// of the row that ranks in the top k is among them.
+template <int NT, int R>
+__device__ void finish_regs(const SelectArgs &a, int qi, uint32_t C, uint32_t lo, uint32_t mx,
+                            const uint32_t (&ck)[R], const uint32_t (&ct)[R], const Lds &L) {
+  const int tid = threadIdx.x;
+  const int rounds = (int)((C + NT - 1) / NT);
+  uint32_t T, r;
+  radix_threshold<NT>(
+      [&](uint32_t himask, uint32_t base, int sh, uint32_t mask) {
 #pragma unroll
-  for (int j = 0; j < kWordsPerThread; ++j) {
-    const uint32_t pe = __popc(ev[j]);
-    // quota left for this word, clamped to [0, pe] in signed arithmetic (an
-    // unsigned "a >= b ? 0 : b - a" form has been folded into a wrapping subtract)
-    const int left = (int)r - (int)eq_before;
-    const uint32_t take = (uint32_t)min(max(left, 0), (int)pe);
-    eq_before += pe;
-    if (take) sv[j] |= lowest_bits(ev[j], take);
-    cnt += __popc(sv[j]);
-  }
-  uint32_t total;
-  uint32_t pos = block_exclusive_scan(cnt, scratch, &total);
-  int32_t *out = a.indices + (int64_t)qi * k;
+        for (int m = 0; m < R; ++m)
+          if (m < rounds)
+            hist_add(L.hist, (uint32_t)(tid + NT * m) < C, ck[m], lo, himask, base, sh, mask);
+      },
+      lo, mx, (uint32_t)a.k, L, T, r);
+  uint32_t pre[R];
+  ordered_prefix<NT, R>(
+      [&](int m) -> uint32_t {
+        const bool valid = (uint32_t)(tid + NT * m) < C;
+        return valid ? (ck[m] > T ? 1u : (ck[m] == T ? 0x10000u : 0u)) : 0u;
+      },
+      rounds, pre, L.tot0);
+  int32_t *out = a.indices + (int64_t)qi * a.k;
 #pragma unroll
-  for (int j = 0; j < kWordsPerThread; ++j) {
-    uint32_t f = sv[j];
-    while (f) {
-      const int b = __ffs(f) - 1;
-      if (pos < (uint32_t)k) out[pos] = (int32_t)((w0 + j) * 32 + b);
-      ++pos;
-      f &= f - 1;
+  for (int m = 0; m < R; ++m) {
+    if (m < rounds) {
+      const bool valid = (uint32_t)(tid + NT * m) < C;
+      const uint32_t sb = pre[m] & 0xFFFFu, eb = pre[m] >> 16;
+      const bool gt = valid && ck[m] > T;
+      const bool eq = valid && ck[m] == T && eb < r;
+      const uint32_t pos = sb + (gt ? min(eb, r) : eb);
+      if (gt || eq) out[pos] = (int32_t)ct[m];
     }
   }
-  for (int p = (int)total + tid; p < k; p += kSelThreads) out[p] = -1;
-  if (tid == 0 && a.counts) a.counts[qi] = (int32_t)(total < (uint32_t)k ? total : (uint32_t)k);
+  if (tid == 0 && a.counts) a.counts[qi] = a.k;
+}
+
+// Loads the rounds of scores of the pass at g0: token g0 + tid + NT i (< n).
+template <int NT, int RP>
+__device__ __forceinline__ void load_pass(const float *row, int g0, int n, float (&v)[RP]) {
+#pragma unroll
+  for (int i = 0; i < RP; ++i) {
+    const int t = g0 + (int)threadIdx.x + NT * i;
+    v[i] = t < n ? row[t] : 0.0f;
+  }
+}
+
+// Steps 3-4 over the whole row read from memory (n > k).
+template <int NT>
+__device__ void finish_row(const SelectArgs &a, int qi, int n, const float *row, const Lds &L) {
+  constexpr int RP = kPass / NT;
+  const int tid = threadIdx.x;
+  uint32_t mx = 0;
+  for (int g0 = 0; g0 < n; g0 += kPass) {
+    float v[RP];
+    load_pass<NT, RP>(row, g0, n, v);
+#pragma unroll
+    for (int i = 0; i < RP; ++i) mx = max(mx, g0 + tid + NT * i < n ? order_key(v[i]) : 0u);
+  }
+  mx = block_max<NT>(mx, L.scratch);
+  uint32_t T, r;
+  radix_threshold<NT>(
+      [&](uint32_t himask, uint32_t base, int sh, uint32_t mask) {
+        for (int g0 = 0; g0 < n; g0 += kPass) {
+          float v[RP];
+          load_pass<NT, RP>(row, g0, n, v);
+#pragma unroll
+          for (int i = 0; i < RP; ++i)
+            hist_add(L.hist, g0 + tid + NT * i < n, order_key(v[i]), 0u, himask, base, sh, mask);
+        }
+      },
+      0u, mx, (uint32_t)a.k, L, T, r);
+  int32_t *out = a.indices + (int64_t)qi * a.k;
+  uint32_t sel_base = 0, eq_base = 0;
+  int parity = 0;
+  for (int g0 = 0; g0 < n; g0 += kPass, parity ^= 1) {
+    float v[RP];
+    load_pass<NT, RP>(row, g0, n, v);
+    uint32_t key[RP];
+#pragma unroll
+    for (int i = 0; i < RP; ++i) key[i] = order_key(v[i]);
+    uint32_t pre[RP];
+    const uint32_t tot = ordered_prefix<NT, RP>(
+        [&](int i) -> uint32_t {
+          if (g0 + tid + NT * i >= n) return 0u;
+          return key[i] > T ? 1u : (key[i] == T ? 0x10000u : 0u);
+        },
+        RP, pre, parity ? L.tot1 : L.tot0);
+#pragma unroll
+    for (int i = 0; i < RP; ++i) {
+      const int t = g0 + tid + NT * i;
+      const uint32_t sb = sel_base + (pre[i] & 0xFFFFu), eb = eq_base + (pre[i] >> 16);
+      const bool gt = t < n && key[i] > T;
+      const bool eq = t < n && key[i] == T && eb < r;
+      const uint32_t pos = sb + (gt ? min(eb, r) : eb);
+      if (gt || eq) out[pos] = t;
+    }
+    sel_base += tot & 0xFFFFu;
+    eq_base += tot >> 16;
+  }
+  if (tid == 0 && a.counts) a.counts[qi] = a.k;
 }
 
 // Lower bound (top 16 bits) on the key of rank `need` among kSamples strided
-// samples of the row; used when one workgroup owns a row and no group bounds
-// were given.  Called by one whole wavefront.
+// samples of the row.  Called by one whole wavefront.
 __device__ uint32_t sample_bound_wave(const float *row, int n, uint32_t need) {
   const int lane = threadIdx.x & 63;
   uint32_t x[kSamples / 64];
@@ -262,179 +372,261 @@ __device__ uint32_t sample_bound_wave(const float *row, int n, uint32_t need) {
   return wave_rank_bound(x, need, 16);
 }
 
-template <bool LOCAL>
-__global__ __launch_bounds__(kSelThreads) void select_kernel(SelectArgs a) {
-  extern __shared__ __align__(16) uint32_t lds[];
-  uint32_t *lh = lds;                                   // [4096] histogram
-  uint32_t *scratch = lh + kHistBins;                   // [32]
-  uint32_t *shv = scratch + 32;                         // [32] shared scalars
-  uint32_t *sel_l = shv + 32;                           // [words]
-  uint32_t *eq_l = sel_l + a.words;                     // [words]
-  uint2 *cand_l = reinterpret_cast<uint2 *>(eq_l + a.words);  // [cand_cap]  (one workgroup per row only)
+// Candidate bound of a row from its group reports: with r = bound_rank(k, G,
+// most) for its G full groups, a lower bound (16-bit prefix) on the
+// ceil(k / r)-th largest report; 0 when there is no bound.  The first
+// wavefront computes it; the result is broadcast through LDS (one barrier).
+template <int N>
+__device__ __forceinline__ uint32_t report_quantile(const uint32_t *b, int nb, uint32_t need) {
+  const int lane = threadIdx.x & 63;
+  uint32_t x[N];
+#pragma unroll
+  for (int i = 0; i < N; ++i) {
+    const int g = lane + 64 * i;
+    x[i] = g < nb ? b[g] : 0u;
+  }
+  return wave_rank_bound(x, need, 16);
+}
 
+__device__ uint32_t row_bound(const SelectArgs &a, int qi, int n, const Lds &L) {
+  const int r = bound_rank(a.k, n / a.group_tokens, a.bound_most);
+  if (r == 0) return 0u;
+  const uint32_t need = (uint32_t)((a.k + r - 1) / r);
+  if (threadIdx.x < 64) {
+    const uint32_t *b = a.bounds + (int64_t)qi * a.n_bounds;
+    uint32_t t;
+    if (a.n_bounds <= 512) t = report_quantile<8>(b, a.n_bounds, need);
+    else t = report_quantile<32>(b, a.n_bounds, need);
+    if (threadIdx.x == 0) L.shv[6] = t;
+  }
+  __syncthreads();
+  return L.shv[6];
+}
+
+// One workgroup per row: filter into LDS, then finish.
+__global__ __launch_bounds__(kLocalThreads) void select_local_kernel(SelectArgs a) {
+  constexpr int NT = kLocalThreads;
+  extern __shared__ __align__(16) uint32_t lds[];
+  const Lds L = carve(lds);
   const int qi = blockIdx.y;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int n = a.q_len[qi];
   const int k = a.k;
+  if (n <= k) {
+    emit_all<NT>(a, qi, n);
+    return;
+  }
   const float *row = a.scores + (int64_t)qi * a.ld;
+  const uint32_t cap = (uint32_t)a.local_cap;
 
-  // ---- 1. candidate bound (identical in every workgroup of the row)
-  const bool bounded = n > k && n > a.cand_cap;
+  float v[kPassRounds];
+  load_pass<NT, kPassRounds>(row, 0, n, v);
   uint32_t t_lo = 0;
-  if (bounded) {
+  if ((uint32_t)n > cap) {
     if (a.bounds) {
-      uint32_t m = 0xFFFFFFFFu;
-      for (int g = lane; g < a.n_bounds; g += 64) m = min(m, a.bounds[(int64_t)qi * a.n_bounds + g]);
-      t_lo = wave_min_u32(m);
-      if (t_lo == 0xFFFFFFFFu) t_lo = 0;  // no full group: no bound
-    } else if (wave == 0) {
-      const uint64_t want = (uint64_t)5 * (uint64_t)k * kSamples / (2 * (uint64_t)n) + 4;
-      const uint32_t t = sample_bound_wave(row, n, (uint32_t)(want < kSamples ? want : kSamples));
-      if (lane == 0) shv[4] = t;
+      t_lo = row_bound(a, qi, n, L);
+    } else {
+      if (wave == 0) {
+        // about 2k candidates expected: rank 2 k S / n among S samples (+4)
+        const uint64_t want = (uint64_t)2 * (uint64_t)k * kSamples / (uint64_t)n + 4;
+        const uint32_t t = sample_bound_wave(row, n, (uint32_t)(want < kSamples ? want : kSamples));
+        if (lane == 0) L.shv[4] = t;
+      }
+      __syncthreads();
+      t_lo = L.shv[4];
     }
   }
 
-  // ---- 2. filter this workgroup's tokens into (key, token) candidates
-  const int c0 = LOCAL ? 0 : blockIdx.x * a.chunk;
-  const int c1 = LOCAL ? n : min(c0 + a.chunk, n);
-  uint32_t found = 0;
-  // first pass: count, to reserve room (multi-workgroup rows)
-  uint32_t key[kPerThread];
-  int g0 = c0;
-  bool loaded = false;
-  if (!LOCAL) {
-    // a chunk is at most kPerThread * kSelThreads tokens: one pass
-    float v[kPerThread];
+  uint32_t found = 0, mx = 0;
+  int parity = 0;
+  for (int g0 = 0; g0 < n; g0 += kPass, parity ^= 1) {
+    float nv[kPassRounds];
+    const bool more = g0 + kPass < n;
+    if (more) load_pass<NT, kPassRounds>(row, g0 + kPass, n, nv);
+    uint32_t key[kPassRounds];
 #pragma unroll
-    for (int i = 0; i < kPerThread; ++i) {
-      const int t = c0 + tid + kSelThreads * i;
-      v[i] = t < c1 ? row[t] : 0.0f;
+    for (int i = 0; i < kPassRounds; ++i) key[i] = order_key(v[i]);
+    uint32_t pre[kPassRounds];
+    const uint32_t tot = ordered_prefix<NT, kPassRounds>(
+        [&](int i) -> uint32_t { return (g0 + tid + NT * i < n && key[i] >= t_lo) ? 1u : 0u; }, kPassRounds, pre,
+        parity ? L.tot1 : L.tot0);
+#pragma unroll
+    for (int i = 0; i < kPassRounds; ++i) {
+      const int t = g0 + tid + NT * i;
+      const uint32_t p = found + pre[i];
+      if (t < n && key[i] >= t_lo && p < cap) L.cand[p] = make_uint2(key[i], (uint32_t)t);
+      mx = max(mx, t < n ? key[i] : 0u);
     }
+    found += tot;
+    if (more) {
 #pragma unroll
-    for (int i = 0; i < kPerThread; ++i) key[i] = order_key(v[i]);
-    loaded = true;
-  }
-  if (bounded && !a.bounds) {
-    __syncthreads();
-    t_lo = shv[4];
-  }
-  uint2 *gdst = nullptr;
-  if (!LOCAL) {
-    uint32_t mine = 0;
-#pragma unroll
-    for (int i = 0; i < kPerThread; ++i) mine += (c0 + tid + kSelThreads * i < c1 && key[i] >= t_lo) ? 1u : 0u;
-    uint32_t tot;
-    uint32_t pos = block_exclusive_scan(mine, scratch, &tot);
-    if (tid == 0) shv[5] = tot ? atomic_add_agent(&a.ctrl[qi * 4 + 1], tot) : 0u;
-    __syncthreads();
-    pos += shv[5];
-    found = tot;
-    gdst = a.cand + (int64_t)qi * a.cand_cap;
-#pragma unroll
-    for (int i = 0; i < kPerThread; ++i) {
-      const int t = c0 + tid + kSelThreads * i;
-      if (t < c1 && key[i] >= t_lo) {
-        if (pos < (uint32_t)a.cand_cap) {
-          // device-coherent store (written through to the coherence point), read
-          // by the row's last workgroup, which may sit on another XCD
-          const uint64_t pk = ((uint64_t)(uint32_t)t << 32) | key[i];
-          __hip_atomic_store(reinterpret_cast<uint64_t *>(gdst + pos), pk, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        }
-        ++pos;
-      }
-    }
-  } else {
-    for (; g0 < c1; g0 += kPerThread * kSelThreads) {
-      float v[kPerThread];
-#pragma unroll
-      for (int i = 0; i < kPerThread; ++i) {
-        const int t = g0 + tid + kSelThreads * i;
-        v[i] = t < c1 ? row[t] : 0.0f;
-      }
-      uint32_t mine = 0;
-#pragma unroll
-      for (int i = 0; i < kPerThread; ++i) {
-        key[i] = order_key(v[i]);
-        mine += (g0 + tid + kSelThreads * i < c1 && key[i] >= t_lo) ? 1u : 0u;
-      }
-      uint32_t tot;
-      uint32_t pos = found + block_exclusive_scan(mine, scratch, &tot);
-#pragma unroll
-      for (int i = 0; i < kPerThread; ++i) {
-        const int t = g0 + tid + kSelThreads * i;
-        if (t < c1 && key[i] >= t_lo) {
-          if (pos < (uint32_t)a.cand_cap) cand_l[pos] = make_uint2(key[i], (uint32_t)t);
-          ++pos;
-        }
-      }
-      found += tot;
+      for (int i = 0; i < kPassRounds; ++i) v[i] = nv[i];
     }
   }
-  (void)loaded;
+  mx = block_max<NT>(mx, L.scratch);   // (its barriers also publish L.cand)
+  if (found < (uint32_t)k || found > cap) {
+    finish_row<NT>(a, qi, n, row, L);
+    return;
+  }
+  constexpr int R = kRegCap / NT;
+  uint32_t ck[R], ct[R];
+#pragma unroll
+  for (int m = 0; m < R; ++m) {
+    const uint32_t j = tid + NT * m;
+    const uint2 c = j < found ? L.cand[j] : make_uint2(0u, 0u);
+    ck[m] = c.x;
+    ct[m] = c.y;
+  }
+  finish_regs<NT, R>(a, qi, found, t_lo, mx, ck, ct, L);
+}
 
-  uint32_t total = found;
-  if (!LOCAL) {
-    // ---- handshake: the last workgroup of the row finishes it.  Every store
-    // this workgroup made for the finisher is device-coherent and has completed
-    // (waitcnt 0) before the counter increment, so no L2 write-back is needed.
-    __builtin_amdgcn_s_waitcnt(0);
-    __syncthreads();
-    if (tid == 0) {
-      __builtin_amdgcn_s_waitcnt(0);
-      const uint32_t prev = __hip_atomic_fetch_add(&a.ctrl[qi * 4], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      const bool last = prev == (uint32_t)(a.chunks - 1);
-      shv[9] = last ? 1u : 0u;
-      if (last) {
-        // drop stale copies of other workgroups' lines from this L1/L2 once
-        // (agent-scope acquire), then read them with ordinary loads
-        fence_acquire_agent();
-        shv[10] = __hip_atomic_load(&a.ctrl[qi * 4 + 1], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      }
-    }
-    __syncthreads();
-    if (shv[9] == 0) return;
-    total = shv[10];
-  } else {
-    __syncthreads();
+// Few long rows, step 2: workgroup (chunk c, row) filters its chunk and writes
+// the candidates and their count to its own region.
+__global__ __launch_bounds__(kFilterThreads) void select_filter_kernel(SelectArgs a) {
+  constexpr int NT = kFilterThreads;
+  extern __shared__ __align__(16) uint32_t lds[];
+  const Lds L = carve(lds);
+  const int qi = blockIdx.y, c = blockIdx.x;
+  const int tid = threadIdx.x;
+  const int n = a.q_len[qi];
+  const int k = a.k;
+  if (n <= k) {
+    if (c == 0) emit_all<NT>(a, qi, n);
+    return;
   }
-
-  // ---- 3. this thread's candidates g = tid + 512 m, into registers
-  const bool in_regs = n <= k || (total >= (uint32_t)k && total <= (uint32_t)a.cand_cap);
-  uint32_t ck[kCandPerThread], ct[kCandPerThread];
-  int nc = 0;
-  if (in_regs && n > k) {
-    nc = total > (uint32_t)tid ? (int)((total - 1 - tid) / kSelThreads) + 1 : 0;
-    const uint2 *src = LOCAL ? cand_l : a.cand + (int64_t)qi * a.cand_cap;
-    uint2 c[kCandPerThread];
+  const float *row = a.scores + (int64_t)qi * a.ld;
+  const int c0 = c * a.chunk;
+  const int c1 = min(c0 + a.chunk, n);
+  float v[kPassRounds];
+  load_pass<NT, kPassRounds>(row, c0, c1, v);   // in flight while the bound is read
+  const uint32_t t_lo = n > kRegCap ? row_bound(a, qi, n, L) : 0u;
+  if (c == 0 && tid == 0) a.tlo[qi] = t_lo;
+  uint32_t key[kPassRounds];
+  uint32_t mx = 0;
 #pragma unroll
-    for (int m = 0; m < kCandPerThread; ++m)
-      if (m < nc) c[m] = src[tid + kSelThreads * m];
-#pragma unroll
-    for (int m = 0; m < kCandPerThread; ++m)
-      if (m < nc) {
-        ck[m] = c[m].x;
-        ct[m] = c[m].y;
-      }
+  for (int i = 0; i < kPassRounds; ++i) {
+    key[i] = order_key(v[i]);
+    mx = max(mx, c0 + tid + NT * i < c1 ? key[i] : 0u);
   }
-  finish_row(a, qi, n, in_regs, ck, ct, nc, t_lo, row, lh, scratch, shv, sel_l, eq_l);
-  if (!LOCAL && tid == 0) {
-    a.ctrl[qi * 4] = 0;       // leave the counters zeroed for the next call
-    a.ctrl[qi * 4 + 1] = 0;
+  mx = wave_max_u32(mx);
+  if ((tid & 63) == 0) L.scratch[40 + (tid >> 6)] = mx;   // read after the prefix's barriers
+  uint32_t pre[kPassRounds];
+  const uint32_t found = ordered_prefix<NT, kPassRounds>(
+      [&](int i) -> uint32_t { return (c0 + tid + NT * i < c1 && key[i] >= t_lo) ? 1u : 0u; }, kPassRounds, pre,
+      L.tot0);
+  uint2 *dst = a.cand + ((int64_t)qi * a.chunks + c) * a.chunk;
+#pragma unroll
+  for (int i = 0; i < kPassRounds; ++i) {
+    const int t = c0 + tid + NT * i;
+    if (t < c1 && key[i] >= t_lo) dst[pre[i]] = make_uint2(key[i], (uint32_t)t);
+  }
+  if (tid == 0) {
+    uint32_t m = 0;
+#pragma unroll
+    for (int w = 0; w < NT / 64; ++w) m = max(m, L.scratch[40 + w]);
+    a.ccount[(int64_t)qi * a.chunks + c] = found;
+    a.cmax[(int64_t)qi * a.chunks + c] = found ? m : 0u;
   }
 }
 
+// Few long rows, steps 3-4: one workgroup per row gathers the chunks'
+// candidates (in chunk order, i.e. token order) into registers and finishes.
+__global__ __launch_bounds__(kFinishThreads) void select_finish_kernel(SelectArgs a) {
+  constexpr int NT = kFinishThreads;
+  constexpr int R = kRegCap / NT;
+  extern __shared__ __align__(16) uint32_t lds[];
+  const Lds L = carve(lds);
+  const int qi = blockIdx.y;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int n = a.q_len[qi];
+  if (n <= a.k) return;   // the filter kernel emitted the row
+  const float *row = a.scores + (int64_t)qi * a.ld;
+  const int chunks = a.chunks;
+
+  // the first wavefront: chunk counts -> exclusive prefix cpre[0..chunks],
+  // cmap[b] = chunk of candidate 64 b, and the largest candidate key
+  if (wave == 0) {
+    constexpr int PL = kMaxChunks / 64;
+    uint32_t cc[PL];
+    uint32_t s = 0, m = 0;
+#pragma unroll
+    for (int i = 0; i < PL; ++i) {
+      const int ch = lane * PL + i;
+      cc[i] = ch < chunks ? a.ccount[(int64_t)qi * chunks + ch] : 0u;
+      m = max(m, ch < chunks ? a.cmax[(int64_t)qi * chunks + ch] : 0u);
+      s += cc[i];
+    }
+    const uint32_t incl = wave_inclusive_scan(s);
+    const bool fits = (uint32_t)__builtin_amdgcn_readlane((int)incl, 63) <= (uint32_t)kRegCap;
+    m = wave_max_u32(m);
+    uint32_t run = incl - s;
+#pragma unroll
+    for (int i = 0; i < PL; ++i) {
+      const int ch = lane * PL + i;
+      if (ch < chunks) {
+        L.cpre[ch] = run;
+        if (fits)
+          for (uint32_t b = (run + 63u) >> 6; (b << 6) < run + cc[i]; ++b) L.cmap[b] = (uint32_t)ch;
+      }
+      run += cc[i];
+    }
+    if (lane == 63) {
+      L.cpre[chunks] = incl;
+      if (fits) L.cmap[(incl + 63u) >> 6] = (uint32_t)(chunks - 1);
+      L.shv[1] = incl;
+      L.shv[2] = a.tlo[qi];
+      L.shv[3] = m;
+    }
+  }
+  __syncthreads();
+  const uint32_t C = L.shv[1];
+  const uint32_t t_lo = L.shv[2];
+  const uint32_t mx = L.shv[3];
+  if (C < (uint32_t)a.k || C > (uint32_t)kRegCap) {
+    finish_row<NT>(a, qi, n, row, L);
+    return;
+  }
+  const uint32_t nb = (C + 63u) >> 6;
+  // Candidates 64 b .. 64 b + 63 are one wavefront's round (b uniform per
+  // wavefront); their chunks lie in [cmap[b], cmap[b + 1]].
+  const uint2 *cand_row = a.cand + (int64_t)qi * chunks * a.chunk;
+  const int rounds = (int)((C + NT - 1) / NT);
+  uint2 cv[R];
+#pragma unroll
+  for (int m = 0; m < R; ++m) {
+    cv[m] = make_uint2(0u, 0u);
+    if (m < rounds) {
+      const uint32_t j = tid + NT * m;
+      const uint32_t b = j >> 6;   // uniform per wavefront
+      if (b < nb) {
+        const uint32_t c0 = L.cmap[b], c1 = L.cmap[b + 1];
+        uint32_t ch = c0;
+        for (uint32_t x = c0 + 1; x <= c1; ++x) ch += L.cpre[x] <= j ? 1u : 0u;
+        if (j < C) cv[m] = cand_row[(int64_t)ch * a.chunk + (j - L.cpre[ch])];
+      }
+    }
+  }
+  uint32_t ck[R], ct[R];
+#pragma unroll
+  for (int m = 0; m < R; ++m) {
+    ck[m] = cv[m].x;
+    ct[m] = cv[m].y;
+  }
+  finish_regs<NT, R>(a, qi, C, t_lo, mx, ck, ct, L);
+}
+
 // Group bounds from a score row (when the scores did not come with them): for
-// group g of kGroup tokens, a lower bound on its ceil(k / G)-th largest key
-// (G = full groups of the row), or 0xFFFFFFFF when the group is not full.
+// group g of kGroup tokens, a lower bound (16-bit prefix) on its r-th largest
+// key, r = bound_rank(k, G, kGroup) with G full groups in the row; 0 when the
+// group is not full.
 __global__ __launch_bounds__(256) void bound_kernel(const float *__restrict__ scores, int64_t ld,
                                                     const int32_t *__restrict__ q_len, int k,
                                                     uint32_t *__restrict__ bounds) {
   __shared__ uint32_t keys[kGroup];
   const int qi = blockIdx.y, g = blockIdx.x;
   const int n = q_len[qi];
-  const int gfull = n / kGroup;
-  const int rank = gfull > 0 ? (k + gfull - 1) / gfull : 0;
-  const bool full = (g + 1) * kGroup <= n && rank <= kGroup;
+  const int rank = bound_rank(k, n / kGroup, kGroup);
+  const bool full = (g + 1) * kGroup <= n && rank >= 1;
   if (full) {
     const float *row = scores + (int64_t)qi * ld + (int64_t)g * kGroup;
     float v[kGroup / 256];
@@ -448,7 +640,7 @@ __global__ __launch_bounds__(256) void bound_kernel(const float *__restrict__ sc
     uint32_t x[kGroup / 64];
 #pragma unroll
     for (int i = 0; i < kGroup / 64; ++i) x[i] = full ? keys[threadIdx.x + 64 * i] : 0u;
-    const uint32_t T = full ? wave_rank_bound(x, (uint32_t)rank, 16) : 0xFFFFFFFFu;
+    const uint32_t T = full ? wave_rank_bound(x, (uint32_t)rank, 16) : 0u;
     if (threadIdx.x == 0) bounds[(int64_t)qi * gridDim.x + g] = T;
   }
 }
@@ -461,14 +653,15 @@ TopkPlan plan_topk(int n_q, int k, int max_len) {
   p.k = k;
   p.max_len = max_len;
   // Many rows, or short rows: one workgroup per row.  Few long rows: spread each
-  // row over several workgroups (about 256 in all) so the whole chip takes part.
+  // row over several filter workgroups (about 256 in all) so the whole chip
+  // takes part, then one finishing workgroup per row.
   int chunks = 1;
   if (n_q < 128 && max_len > 8192) {
     chunks = 256 / (n_q > 0 ? n_q : 1);
-    const int fewest = (max_len + kPerThread * kSelThreads - 1) / (kPerThread * kSelThreads);
+    const int fewest = (max_len + kPass - 1) / kPass;
     const int most = (max_len + 1023) / 1024;
     if (chunks > most) chunks = most;
-    if (chunks < fewest) chunks = fewest;   // a chunk is one pass of kPerThread per thread
+    if (chunks < fewest) chunks = fewest;   // a chunk is one filter pass
     if (chunks < 2) chunks = 2;
   }
   int chunk = (max_len + chunks - 1) / chunks;
@@ -478,17 +671,8 @@ TopkPlan plan_topk(int n_q, int k, int max_len) {
   p.chunk = chunk;
   p.group = kGroup;
   p.groups = (max_len + kGroup - 1) / kGroup;
-  p.words = ((max_len + 31) / 32 + 3) / 4 * 4;
-  // LDS: 4096-word histogram + 64 words, two bitmaps, and (one workgroup per
-  // row) the candidate list, which takes what is left of 160 KiB.
-  const size_t fixed = (size_t)(kHistBins + 64) * 4 + (size_t)2 * p.words * 4;
-  size_t cap = (size_t)kCandPerThread * kSelThreads;  // 12288: the register budget
-  if (chunks == 1) {
-    const size_t room = fixed < 160 * 1024 ? (160 * 1024 - fixed) / 8 : 0;
-    if (room < cap) cap = room / kSelThreads * kSelThreads;
-  }
-  p.cand_cap = (int)cap;
-  p.lds_bytes = fixed + (chunks == 1 ? cap * 8 : 0);
+  p.local_cap = chunks == 1 ? kLocalCap : 0;
+  p.lds_bytes = (size_t)kFixedWords * 4 + (size_t)p.local_cap * 8;
   size_t off = 0;
   auto take = [&](size_t bytes) {
     size_t o = off;
@@ -496,9 +680,11 @@ TopkPlan plan_topk(int n_q, int k, int max_len) {
     return o;
   };
   if (chunks > 1) {
-    p.off_ctrl = take((size_t)n_q * 16);
+    p.off_tlo = take((size_t)n_q * 4);
+    p.off_count = take((size_t)n_q * chunks * 4);
+    p.off_cmax = take((size_t)n_q * chunks * 4);
     p.off_bounds = take((size_t)n_q * p.groups * 4);
-    p.off_cand = take((size_t)n_q * cap * 8);
+    p.off_cand = take((size_t)n_q * chunks * chunk * 8);
   }
   p.total = off;
   return p;
@@ -506,17 +692,15 @@ TopkPlan plan_topk(int n_q, int k, int max_len) {
 
 hipError_t launch_topk(int32_t *indices, int32_t *counts, const float *scores, int64_t ld, const int32_t *q_len,
                        const TopkPlan &plan, void *workspace, const uint32_t *bounds, int n_bounds,
-                       hipStream_t stream) {
-  // The select kernel uses up to 160 KiB of dynamic LDS.
+                       int group_tokens, hipStream_t stream) {
   static const bool lds_ok = [] {
     const int most = 160 * 1024;
-    return hipFuncSetAttribute(reinterpret_cast<const void *>(&select_kernel<true>),
-                               hipFuncAttributeMaxDynamicSharedMemorySize, most) == hipSuccess &&
-           hipFuncSetAttribute(reinterpret_cast<const void *>(&select_kernel<false>),
+    return hipFuncSetAttribute(reinterpret_cast<const void *>(&select_local_kernel),
                                hipFuncAttributeMaxDynamicSharedMemorySize, most) == hipSuccess;
   }();
   if (!lds_ok) return hipErrorInvalidConfiguration;
-  if (plan.lds_bytes > 160 * 1024 || plan.cand_cap < kSamples) return hipErrorInvalidValue;
+  if (plan.lds_bytes > 160 * 1024 || plan.chunks > kMaxChunks || (plan.chunks > 1 && plan.chunk > kPass))
+    return hipErrorInvalidValue;
   uint8_t *ws = static_cast<uint8_t *>(workspace);
   SelectArgs a{};
   a.indices = indices;
@@ -527,12 +711,15 @@ hipError_t launch_topk(int32_t *indices, int32_t *counts, const float *scores, i
   a.k = plan.k;
   a.chunk = plan.chunk;
   a.chunks = plan.chunks;
-  a.words = plan.words;
-  a.cand_cap = plan.cand_cap;
+  a.local_cap = plan.local_cap;
   a.bounds = bounds;
   a.n_bounds = n_bounds;
+  a.group_tokens = group_tokens > 0 ? group_tokens : 1;
+  a.bound_most = 32;
   if (plan.chunks > 1) {
-    a.ctrl = reinterpret_cast<uint32_t *>(ws + plan.off_ctrl);
+    a.tlo = reinterpret_cast<uint32_t *>(ws + plan.off_tlo);
+    a.ccount = reinterpret_cast<uint32_t *>(ws + plan.off_count);
+    a.cmax = reinterpret_cast<uint32_t *>(ws + plan.off_cmax);
     a.cand = reinterpret_cast<uint2 *>(ws + plan.off_cand);
     if (!bounds) {
       uint32_t *b = reinterpret_cast<uint32_t *>(ws + plan.off_bounds);
@@ -542,11 +729,17 @@ hipError_t launch_topk(int32_t *indices, int32_t *counts, const float *scores, i
       if (e != hipSuccess) return e;
       a.bounds = b;
       a.n_bounds = plan.groups;
+      a.group_tokens = kGroup;
+      a.bound_most = kGroup;
     }
-    hipLaunchKernelGGL(select_kernel<false>, dim3(plan.chunks, plan.n_q), dim3(kSelThreads), plan.lds_bytes, stream,
-                       a);
+    hipLaunchKernelGGL(select_filter_kernel, dim3(plan.chunks, plan.n_q), dim3(kFilterThreads),
+                       (size_t)kFixedWords * 4, stream, a);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(select_finish_kernel, dim3(1, plan.n_q), dim3(kFinishThreads), (size_t)kFixedWords * 4,
+                       stream, a);
   } else {
-    hipLaunchKernelGGL(select_kernel<true>, dim3(1, plan.n_q), dim3(kSelThreads), plan.lds_bytes, stream, a);
+    hipLaunchKernelGGL(select_local_kernel, dim3(1, plan.n_q), dim3(kLocalThreads), plan.lds_bytes, stream, a);
   }
   return hipGetLastError();
 }
