@@ -32,6 +32,9 @@ HBM_PEAK_GBS = 8000.0
 BF16_PEAK_TFLOPS = 2500.0
 
 
+COPY_PROBE_BYTES = 1 << 30
+
+
 def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -40,6 +43,8 @@ def parse():
     ap.add_argument("--copies", type=int, default=6, help="device copies of the caches rotated over")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--no-prefill", action="store_true")
+    ap.add_argument("--copy-probe", action="store_true",
+                    help="only run a plain 1 GiB device copy three times (calibrates HBM byte counters) and exit")
     return ap.parse_args()
 
 
@@ -109,6 +114,18 @@ def main():
     import sparse_attention_14_amd as dsa
     from sparse_attention_14_amd import device, inputs
 
+    if args.copy_probe:
+        # A plain copy kernel of known size: reads and writes COPY_PROBE_BYTES per
+        # launch, so profiler byte counters taken on it give their scale factor.
+        src = torch.empty(COPY_PROBE_BYTES, dtype=torch.uint8, device="cuda")
+        dst = torch.empty_like(src)
+        src.fill_(1)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_probe_bytes": COPY_PROBE_BYTES, "launches": 3}))
+        return
+
     dsa.load()
     torch.cuda.init()
     dev_name = torch.cuda.get_device_name(0)
@@ -177,13 +194,15 @@ def main():
     with torch.cuda.stream(kstream):
         for i in range(5):
             keys, _ = copies[i % len(copies)]
-            dsa.dsa_index_scores(scores, dp.q_idx, p.q_idx_dtype, dp.w_idx, keys, dp.q_len, p.idx_heads, p.max_len)
+            dsa.dsa_index_scores(scores, dp.q_idx, p.q_idx_dtype, dp.w_idx, keys, dp.q_len, p.idx_heads, p.max_len,
+                                 q_seq=dp.q_seq)
         e0 = torch.cuda.Event(enable_timing=True)
         e1 = torch.cuda.Event(enable_timing=True)
         e0.record(kstream)
         for i in range(n_k):
             keys, _ = copies[i % len(copies)]
-            dsa.dsa_index_scores(scores, dp.q_idx, p.q_idx_dtype, dp.w_idx, keys, dp.q_len, p.idx_heads, p.max_len)
+            dsa.dsa_index_scores(scores, dp.q_idx, p.q_idx_dtype, dp.w_idx, keys, dp.q_len, p.idx_heads, p.max_len,
+                                 q_seq=dp.q_seq)
         e1.record(kstream)
     e1.synchronize()
     t_kernel = e0.elapsed_time(e1) / 1e3 / n_k

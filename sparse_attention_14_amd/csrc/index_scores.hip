@@ -24,13 +24,17 @@ namespace {
 
 constexpr int kMaxTilesPerWave = 8;
 
-template <bool FP8, int D, int MT>
+// One wavefront scores TPW consecutive 32-key tiles.  The tile loop is fully
+// unrolled and every tile load is issued unconditionally (tiles past the row's
+// end reload its last tile and their scores are dropped), so the code is
+// straight-line and the compiler waits for exactly the tile it needs while the
+// next P tiles stay in flight.
+template <bool FP8, int D, int MT, int TPW>
 __global__ __launch_bounds__(256) void scores_mfma_kernel(float *__restrict__ scores, int64_t ld,
                                                           const uint16_t *__restrict__ q, const float *__restrict__ w,
                                                           CacheDev keys, const int32_t *__restrict__ q_seq,
                                                           int seq_ident, const int32_t *__restrict__ q_len,
-                                                          int n_heads, int tiles_per_wave, uint32_t *__restrict__ bounds,
-                                                          int topk) {
+                                                          int n_heads, uint32_t *__restrict__ bounds, int topk) {
   constexpr int KS = D / 16;            // 32x32x16 K-steps
   constexpr int HALF = D / 2;           // dims held by one lane half
   constexpr int EB = FP8 ? 1 : 2;       // key element bytes
@@ -39,130 +43,144 @@ __global__ __launch_bounds__(256) void scores_mfma_kernel(float *__restrict__ sc
   constexpr int HALFC = CPR / 2;        // chunks per lane half
   constexpr int TILEB = 32 * ROWB;      // bytes of a 32-key tile
   constexpr int NLD = TILEB / 1024;     // 1 KB wavefront loads per tile
+  constexpr int P = TPW < 2 ? TPW : 2;  // tiles in flight ahead of the one being scored
   __shared__ __align__(16) uint8_t stage_all[4][TILEB];
 
   const int qi = blockIdx.y;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int half = lane >> 5, col = lane & 31;
   const int n = q_len[qi];
-  const int tile_begin = (blockIdx.x * 4 + wave) * tiles_per_wave;
-  const int seq = seq_of(q_seq, qi, seq_ident);
-  uint8_t *stage = stage_all[wave];
+  const int ntile = (n + 31) / 32;
+  const int wid = blockIdx.x * 4 + wave;
+  const int tile_begin = wid * TPW;
   uint32_t lane_max = 0;   // largest score key this lane wrote (bounds only)
 
-  if (tile_begin * 32 < n) {
-  // q as the A operand: lane (col, half) holds head 32*mt + col, dims half*HALF + 8*ks + [0, 8).
-  bf16x8 a[MT][KS];
-  float wr[MT][16];
-#pragma unroll
-  for (int mt = 0; mt < MT; ++mt) {
-    const int head = 32 * mt + col;
-    const uint16_t *qrow = q + ((int64_t)qi * n_heads + (head < n_heads ? head : 0)) * D + half * HALF;
-#pragma unroll
-    for (int ks = 0; ks < KS; ++ks) {
-      u32x4 v = load16(qrow + 8 * ks);
-      if (head >= n_heads) v = u32x4{0, 0, 0, 0};
-      a[mt][ks] = as_bf16x8(v);
-    }
-    // Accumulator element r of this lane is head 32*mt + 8*(r/4) + 4*half + r%4.
-#pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      const int m = 32 * mt + 8 * (r >> 2) + 4 * half + (r & 3);
-      wr[mt][r] = m < n_heads ? w[(int64_t)qi * n_heads + m] : 0.0f;
-    }
-  }
-
-  // Loads are coalesced: 16-byte piece j*64 + lane of the tile's rows (1 KB per
-  // wavefront instruction), i.e. key kk = (1024 j + 16 lane) / ROWB, chunk ch.
-  // They go through a wavefront-private LDS tile (chunk slots XOR-swizzled by
-  // the key index against bank conflicts) into the MFMA operand layout.
-  struct Raw {
-    u32x4 v[NLD];
-    float sc;
-  };
-  auto issue = [&](int tile, Raw &r) {
-    const int t0 = tile * 32;
-    const int bi = t0 / keys.block_size;   // a 32-token tile never straddles a block
-    const int64_t blk = keys.table ? (int64_t)keys.table[(int64_t)seq * keys.max_blocks + bi] : (int64_t)seq;
-    const int base_slot = t0 - bi * keys.block_size;
-    const int last = n - 1 - t0;           // clamp rows beyond the visible tokens
-#pragma unroll
-    for (int j = 0; j < NLD; ++j) {
-      const int byte = 1024 * j + 16 * lane;
-      const int kk = byte / ROWB, ch = (byte % ROWB) / 16;
-      const int kc = kk < last ? kk : last;
-      r.v[j] = load16(cache_row(keys, blk, base_slot + kc) + 16 * ch);
-    }
-    if (FP8) {
-      const int kc = col < last ? col : last;
-      r.sc = keys.scale[blk * keys.scale_block_stride + base_slot + kc];
-    }
-  };
-  Raw cur, nxt;
-  issue(tile_begin, cur);
-  for (int it = 0; it < tiles_per_wave; ++it) {
-    const int t0 = (tile_begin + it) * 32;
-    if (t0 >= n) break;
-    const bool more = it + 1 < tiles_per_wave && t0 + 32 < n;
-    if (more) issue(tile_begin + it + 1, nxt);
-
-    // stage the tile, then read this lane's operand chunks back
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-    __builtin_amdgcn_wave_barrier();
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-#pragma unroll
-    for (int j = 0; j < NLD; ++j) {
-      const int byte = 1024 * j + 16 * lane;
-      const int kk = byte / ROWB, ch = (byte % ROWB) / 16;
-      *reinterpret_cast<u32x4 *>(stage + kk * ROWB + 16 * (ch ^ (kk & (CPR - 1)))) = cur.v[j];
-    }
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-    __builtin_amdgcn_wave_barrier();
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-    bf16x8 b[KS];
-#pragma unroll
-    for (int j = 0; j < HALFC; ++j) {
-      const int ch = half * HALFC + j;
-      const u32x4 x = *reinterpret_cast<const u32x4 *>(stage + col * ROWB + 16 * (ch ^ (col & (CPR - 1))));
-      if (FP8) {
-        b[2 * j] = fp8x8_to_bf16x8(x[0], x[1]);
-        b[2 * j + 1] = fp8x8_to_bf16x8(x[2], x[3]);
-      } else {
-        b[j] = as_bf16x8(x);
-      }
-    }
-    const float sc = FP8 ? cur.sc : 1.0f;
-
-    float s = 0.0f;
+  if (tile_begin < ntile) {
+    const int seq = seq_of(q_seq, qi, seq_ident);
+    uint8_t *stage = stage_all[wave];
+    // q as the A operand: lane (col, half) holds head 32*mt + col, dims half*HALF + 8*ks + [0, 8).
+    bf16x8 a[MT][KS];
+    float wr[MT][16];
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt) {
-      f32x16 acc = {};
+      const int head = 32 * mt + col;
+      const uint16_t *qrow = q + ((int64_t)qi * n_heads + (head < n_heads ? head : 0)) * D + half * HALF;
 #pragma unroll
-      for (int ks = 0; ks < KS; ++ks) acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[mt][ks], b[ks], acc, 0, 0, 0);
+      for (int ks = 0; ks < KS; ++ks) {
+        u32x4 v = load16(qrow + 8 * ks);
+        if (head >= n_heads) v = u32x4{0, 0, 0, 0};
+        a[mt][ks] = as_bf16x8(v);
+      }
+      // Accumulator element r of this lane is head 32*mt + 8*(r/4) + 4*half + r%4.
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
-        float v = FP8 ? acc[r] * sc : acc[r];
-        v = fmaxf(v, 0.0f);
-        s = fmaf(wr[mt][r], v, s);
+        const int m = 32 * mt + 8 * (r >> 2) + 4 * half + (r & 3);
+        wr[mt][r] = m < n_heads ? w[(int64_t)qi * n_heads + m] : 0.0f;
       }
     }
-    s += __shfl_xor(s, 32, 64);
-    const int t = t0 + col;
-    if (half == 0 && t < n) scores[(int64_t)qi * ld + t] = s;
-    if (half == 0 && t < n) lane_max = max(lane_max, order_key(s));
-    if (more) cur = nxt;
-  }
+    // Physical block of every tile of this wavefront, looked up once (a 32-key
+    // tile never straddles a block).
+    int64_t blk[TPW];
+    int bslot[TPW];
+#pragma unroll
+    for (int it = 0; it < TPW; ++it) {
+      int tile = tile_begin + it;
+      tile = tile < ntile ? tile : ntile - 1;
+      const int t0 = tile * 32;
+      const int bi = t0 / keys.block_size;
+      blk[it] = keys.table ? (int64_t)keys.table[(int64_t)seq * keys.max_blocks + bi] : (int64_t)seq;
+      bslot[it] = t0 - bi * keys.block_size;
+    }
+
+    // Loads are coalesced: 16-byte piece j*64 + lane of the tile's rows (1 KB per
+    // wavefront instruction), i.e. key kk = (1024 j + 16 lane) / ROWB, chunk ch.
+    // They go through a wavefront-private LDS tile (chunk slots XOR-swizzled by
+    // the key index against bank conflicts) into the MFMA operand layout.  Keys
+    // are read once per call: non-temporal loads.
+    struct Raw {
+      u32x4 v[NLD];
+      float sc;
+    };
+    auto issue = [&](int it, Raw &r) {
+      int tile = tile_begin + it;
+      tile = tile < ntile ? tile : ntile - 1;
+      const int last = n - 1 - tile * 32;    // clamp rows beyond the visible tokens
+#pragma unroll
+      for (int j = 0; j < NLD; ++j) {
+        const int byte = 1024 * j + 16 * lane;
+        const int kk = byte / ROWB, ch = (byte % ROWB) / 16;
+        const int kc = kk < last ? kk : last;
+        r.v[j] = load16_nt(cache_row(keys, blk[it], bslot[it] + kc) + 16 * ch);
+      }
+      if (FP8) {
+        const int kc = col < last ? col : last;
+        r.sc = keys.scale[blk[it] * keys.scale_block_stride + bslot[it] + kc];
+      }
+    };
+    Raw buf[P];
+#pragma unroll
+    for (int p = 0; p < P; ++p) issue(p, buf[p]);
+#pragma unroll
+    for (int it = 0; it < TPW; ++it) {
+      Raw &cur = buf[it % P];
+      // stage the tile, then read this lane's operand chunks back
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+      __builtin_amdgcn_wave_barrier();
+      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+#pragma unroll
+      for (int j = 0; j < NLD; ++j) {
+        const int byte = 1024 * j + 16 * lane;
+        const int kk = byte / ROWB, ch = (byte % ROWB) / 16;
+        *reinterpret_cast<u32x4 *>(stage + kk * ROWB + 16 * (ch ^ (kk & (CPR - 1)))) = cur.v[j];
+      }
+      const float sc = FP8 ? cur.sc : 1.0f;
+      if (it + P < TPW) issue(it + P, cur);
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+      __builtin_amdgcn_wave_barrier();
+      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+      bf16x8 b[KS];
+#pragma unroll
+      for (int j = 0; j < HALFC; ++j) {
+        const int ch = half * HALFC + j;
+        const u32x4 x = *reinterpret_cast<const u32x4 *>(stage + col * ROWB + 16 * (ch ^ (col & (CPR - 1))));
+        if (FP8) {
+          b[2 * j] = fp8x8_to_bf16x8(x[0], x[1]);
+          b[2 * j + 1] = fp8x8_to_bf16x8(x[2], x[3]);
+        } else {
+          b[j] = as_bf16x8(x);
+        }
+      }
+      // Epilogue.  fp8: ReLU(acc * sc) * w summed over heads equals
+      // sc * sum w * med3(acc, 0, +-inf) (the ReLU side flips with the sign of
+      // sc), with one multiply per key instead of one per head.
+      const float lim = sc >= 0.0f ? INFINITY : -INFINITY;
+      float s = 0.0f;
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt) {
+        f32x16 acc = {};
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[mt][ks], b[ks], acc, 0, 0, 0);
+#pragma unroll
+        for (int r = 0; r < 16; ++r)
+          s = fmaf(wr[mt][r], FP8 ? __builtin_amdgcn_fmed3f(acc[r], 0.0f, lim) : fmaxf(acc[r], 0.0f), s);
+      }
+      if (FP8) s *= sc;
+      s += __shfl_xor(s, 32, 64);
+      const int t = (tile_begin + it) * 32 + col;
+      const bool ok = half == 0 && t < n;
+      if (ok) scores[(int64_t)qi * ld + t] = s;
+      lane_max = max(lane_max, ok ? order_key(s) : 0u);
+    }
   }
 
-  // Candidate bound for the top-k: a full wavefront (all tiles_per_wave * 32
-  // of its tokens visible) reports the r-th largest of its lanes' maxima,
+  // Candidate bound for the top-k: a full wavefront (all TPW * 32 of its
+  // tokens visible) reports the r-th largest of its lanes' maxima,
   // r = bound_rank(k, G, 32) with G full wavefronts in the row; each lane
   // maximum is the score of a distinct token.  Other wavefronts report 0.
   if (bounds) {
-    const int per_wave = tiles_per_wave * 32;
+    constexpr int per_wave = TPW * 32;
     const int gfull = n / per_wave;
     const int rank = bound_rank(topk, gfull, 32);
-    const int wid = blockIdx.x * 4 + wave;
     uint32_t T = 0;
     if ((wid + 1) * per_wave <= n && rank >= 1) {
       // rank-th largest of the 32 lane maxima (lanes 32..63 hold 0): extract
@@ -227,9 +245,17 @@ hipError_t run_mfma(float *scores, int64_t ld, const void *q, const float *w, co
   const int tpw = score_tiles_per_wave(n_q, max_len);
   const int gx = (tiles + 4 * tpw - 1) / (4 * tpw);
   dim3 grid(gx, n_q);
-  hipLaunchKernelGGL((scores_mfma_kernel<FP8, D, MT>), grid, dim3(256), 0, stream, scores, ld,
-                     static_cast<const uint16_t *>(q), w, keys, q_seq, seq_ident, q_len, n_heads, tpw, sb.bounds,
-                     sb.topk);
+  const uint16_t *qb = static_cast<const uint16_t *>(q);
+#define DSA_SK(T)                                                                                            \
+  hipLaunchKernelGGL((scores_mfma_kernel<FP8, D, MT, T>), grid, dim3(256), 0, stream, scores, ld, qb, w, keys, \
+                     q_seq, seq_ident, q_len, n_heads, sb.bounds, sb.topk)
+  switch (tpw) {
+    case 1: DSA_SK(1); break;
+    case 2: DSA_SK(2); break;
+    case 4: DSA_SK(4); break;
+    default: DSA_SK(8); break;
+  }
+#undef DSA_SK
   return hipGetLastError();
 }
 
@@ -284,11 +310,13 @@ hipError_t launch_index_scores(float *scores, int64_t ld, const void *q, int q_d
 }
 
 int score_tiles_per_wave(int n_q, int max_len) {
-  // ~512 workgroups of 4 wavefronts; each wavefront streams up to
-  // kMaxTilesPerWave consecutive 32-key tiles so its q fragment load is amortised.
+  // ~512 workgroups of 4 wavefronts; each wavefront streams 1, 2, 4 or 8
+  // consecutive 32-key tiles so its q fragment load is amortised.
   const int64_t total = (int64_t)((max_len + 31) / 32) * n_q;
-  int tpw = (int)((total + 4 * 512 - 1) / (4 * 512));
-  return tpw < 1 ? 1 : (tpw > kMaxTilesPerWave ? kMaxTilesPerWave : tpw);
+  const int64_t want = (total + 4 * 512 - 1) / (4 * 512);
+  int tpw = 1;
+  while (tpw < kMaxTilesPerWave && tpw < want) tpw *= 2;
+  return tpw;
 }
 
 int score_group_tokens(int n_q, int max_len) { return 32 * score_tiles_per_wave(n_q, max_len); }
