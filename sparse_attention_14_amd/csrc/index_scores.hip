@@ -23,6 +23,7 @@ namespace dsa {
 namespace {
 
 constexpr int kMaxTilesPerWave = 8;
+constexpr int kPrefillMinQueries = 64;   // the GEMM-shaped kernel takes over from here
 
 // One wavefront scores TPW consecutive 32-key tiles.  The tile loop is fully
 // unrolled and every tile load is issued unconditionally (tiles past the row's
@@ -196,6 +197,162 @@ __global__ __launch_bounds__(256) void scores_mfma_kernel(float *__restrict__ sc
   }
 }
 
+// Many queries (chunked prefill), bf16 q and keys, 128-wide keys, up to 32
+// heads: a GEMM over (query, head) rows and key columns with K = 128.  A
+// workgroup owns kPQ consecutive queries and one range of keys; 64-key steps
+// are staged in LDS once and shared by its 8 wavefronts, each scoring 2
+// queries x 2 key tiles per step (8 MFMAs 32x32x16 per query and tile), so a
+// wavefront reads a key tile from LDS once for both of its queries.  Key steps
+// are loaded two steps ahead through a 3-slot LDS ring.  Queries of a block
+// that belong to different sequences are processed one sequence at a time.
+constexpr int kPQ = 16;            // queries per workgroup
+constexpr int kPStepKeys = 64;     // keys per step (two 32-key tiles)
+constexpr int kPThreads = 512;
+constexpr int kPRowB = 256;        // bf16 key row bytes (128 dims)
+
+__global__ __launch_bounds__(kPThreads) void scores_prefill_kernel(float *__restrict__ scores, int64_t ld,
+                                                                   const uint16_t *__restrict__ q,
+                                                                   const float *__restrict__ w, CacheDev keys,
+                                                                   const int32_t *__restrict__ q_seq,
+                                                                   const int32_t *__restrict__ q_len, int n_q,
+                                                                   int n_heads, int keys_per_split) {
+  constexpr int D = 128, KS = D / 16, HALF = D / 2, CPR = kPRowB / 16;   // 16 chunks per row
+  __shared__ __align__(16) uint8_t ring[3][kPStepKeys * kPRowB];            // 3 x 16 KB
+  __shared__ int32_t sseq[kPQ], slen[kPQ];
+  __shared__ int32_t groups[kPQ + 1];
+
+  const int qb = blockIdx.x, split = blockIdx.y;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int half = lane >> 5, col = lane & 31;
+  const int qbase = qb * kPQ;
+  if (tid < kPQ) {
+    const int qi = qbase + tid;
+    sseq[tid] = qi < n_q ? (q_seq ? q_seq[qi] : 0) : -1;
+    slen[tid] = qi < n_q ? q_len[qi] : 0;
+  }
+  __syncthreads();
+  if (tid == 0) {   // distinct sequences of the block, in order of first appearance
+    int ng = 0;
+    for (int i = 0; i < kPQ; ++i) {
+      if (sseq[i] < 0) continue;
+      bool seen = false;
+      for (int j = 0; j < i; ++j) seen = seen || sseq[j] == sseq[i];
+      if (!seen) groups[ng++] = sseq[i];
+    }
+    groups[kPQ] = ng;
+  }
+
+  // this wavefront's two queries: A operands (lane half h holds dims
+  // 64 h + 8 ks + [0, 8) of head col, the key operand uses the same order) and
+  // head weights (accumulator element r is head 8 (r / 4) + 4 half + r % 4)
+  bf16x8 a[2][KS];
+  float wr[2][16];
+  int qn[2], qs[2];
+#pragma unroll
+  for (int u = 0; u < 2; ++u) {
+    const int qi = qbase + 2 * wave + u;
+    const bool ok = qi < n_q;
+    const int head = col < n_heads ? col : 0;
+    const uint16_t *qrow = q + ((int64_t)(ok ? qi : 0) * n_heads + head) * D + half * HALF;
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      u32x4 v = load16(qrow + 8 * ks);
+      if (!ok || col >= n_heads) v = u32x4{0, 0, 0, 0};
+      a[u][ks] = as_bf16x8(v);
+    }
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int m = 8 * (r >> 2) + 4 * half + (r & 3);
+      wr[u][r] = (ok && m < n_heads) ? w[(int64_t)qi * n_heads + m] : 0.0f;
+    }
+  }
+  __syncthreads();
+#pragma unroll
+  for (int u = 0; u < 2; ++u) {
+    qn[u] = slen[2 * wave + u];
+    qs[u] = sseq[2 * wave + u];
+  }
+  const int ngroups = groups[kPQ];
+
+  for (int gi = 0; gi < ngroups; ++gi) {
+    const int seq = groups[gi];
+    int nmax = 0;
+    for (int i = 0; i < kPQ; ++i) nmax = sseq[i] == seq ? max(nmax, slen[i]) : nmax;
+    const int k0 = split * keys_per_split;
+    const int k1 = min(k0 + keys_per_split, nmax);
+    if (k0 >= k1) continue;   // uniform over the workgroup
+    const int nsteps = (k1 - k0 + kPStepKeys - 1) / kPStepKeys;
+
+    // key step loads: thread t takes 16-byte chunks t and t + 512 of the step's
+    // 64 rows (row = c / 16, chunk = c % 16); rows past k1 are clamped to k1 - 1
+    auto load_step = [&](int st, u32x4 (&r)[2]) {
+      const int sc = st < nsteps ? st : nsteps - 1;
+#pragma unroll
+      for (int x = 0; x < 2; ++x) {
+        const int c = tid + kPThreads * x;
+        const int row = c / CPR, ch = c % CPR;
+        int t = k0 + sc * kPStepKeys + row;
+        t = t < k1 ? t : k1 - 1;
+        int slot;
+        const int64_t blk = cache_block(keys, seq, t, slot);
+        r[x] = load16_nt(cache_row(keys, blk, slot) + 16 * ch);
+      }
+    };
+    auto store_step = [&](int st, const u32x4 (&r)[2]) {
+      uint8_t *buf = ring[st % 3];
+#pragma unroll
+      for (int x = 0; x < 2; ++x) {
+        const int c = tid + kPThreads * x;
+        const int row = c / CPR, ch = c % CPR;
+        *reinterpret_cast<u32x4 *>(buf + row * kPRowB + 16 * (ch ^ (row & (CPR - 1)))) = r[x];
+      }
+    };
+    auto compute_step = [&](int st) {
+      const uint8_t *buf = ring[st % 3];
+      const int kb = k0 + st * kPStepKeys;
+#pragma unroll
+      for (int tl = 0; tl < 2; ++tl) {
+        const int row = tl * 32 + col;
+        bf16x8 b[KS];
+#pragma unroll
+        for (int j = 0; j < KS; ++j) {
+          const int ch = half * (CPR / 2) + j;
+          b[j] = as_bf16x8(*reinterpret_cast<const u32x4 *>(buf + row * kPRowB + 16 * (ch ^ (row & (CPR - 1)))));
+        }
+        const int key = kb + row;
+#pragma unroll
+        for (int u = 0; u < 2; ++u) {
+          f32x16 acc = {};
+#pragma unroll
+          for (int ks = 0; ks < KS; ++ks) acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[u][ks], b[ks], acc, 0, 0, 0);
+          float s = 0.0f;
+#pragma unroll
+          for (int r = 0; r < 16; ++r) s = fmaf(wr[u][r], fmaxf(acc[r], 0.0f), s);
+          s += __shfl_xor(s, 32, 64);
+          const int qi = qbase + 2 * wave + u;
+          if (half == 0 && qs[u] == seq && key < qn[u] && key < k1) scores[(int64_t)qi * ld + key] = s;
+        }
+      }
+    };
+
+    u32x4 ra[2], rb[2];
+    load_step(0, ra);
+    load_step(1, rb);
+    store_step(0, ra);
+    __syncthreads();
+    for (int st = 0; st < nsteps; st += 2) {
+      load_step(st + 2, ra);
+      compute_step(st);
+      store_step(st + 1, rb);
+      __syncthreads();
+      load_step(st + 3, rb);
+      if (st + 1 < nsteps) compute_step(st + 1);
+      store_step(st + 2, ra);
+      __syncthreads();
+    }
+  }
+}
+
 // fp32 queries and keys: one thread per key, fp32 FMA chains in a fixed order
 // (dims ascending, then heads ascending).
 template <int D>
@@ -284,6 +441,17 @@ hipError_t dispatch(float *scores, int64_t ld, const void *q, int q_dt, const fl
   }
   const bool fp8 = key_dt == kFP8;
   const bool two = n_heads > 32;
+  if (!fp8 && D == 128 && !two && n_q >= kPrefillMinQueries && !sb.bounds && !seq_ident) {
+    const int blocks = (n_q + kPQ - 1) / kPQ;
+    // split the keys so that about 256 workgroups run
+    int splits = (256 + blocks - 1) / blocks;
+    int per = (max_len + splits - 1) / splits;
+    per = (per + kPStepKeys - 1) / kPStepKeys * kPStepKeys;
+    splits = (max_len + per - 1) / per;
+    hipLaunchKernelGGL(scores_prefill_kernel, dim3(blocks, splits), dim3(kPThreads), 0, s, scores, ld,
+                       static_cast<const uint16_t *>(q), w, keys, q_seq, q_len, n_q, n_heads, per);
+    return hipGetLastError();
+  }
 #define DSA_SC(F, DD, M)                                                                                    \
   return run_mfma<F, DD, M>(scores, ld, q, w, keys, q_seq, seq_ident, q_len, n_q, n_heads, max_len, sb, s)
   if (D == 128) {

@@ -26,6 +26,11 @@ CASES = {
     "bf16_h7_signed_w": S(inputs.DECODE_8K, name="h7", wid=208, batch=2, seq_len=(50, 1500), idx_heads=7, w_lo=-1.0,
                           w_hi=1.0),
     "bf16_prefill_rows": S(inputs.PREFILL_64K, name="pre", wid=209, seq_len=(3000, 3000), prefill_queries=64),
+    # many queries: the GEMM-shaped kernel, with a ragged last block and fewer heads
+    "bf16_prefill_ragged_h20": S(inputs.PREFILL_64K, name="pre2", wid=211, seq_len=(5000, 5000), prefill_queries=100,
+                                 idx_heads=20),
+    # many queries of different (paged) sequences: blocks mix sequences
+    "bf16_many_sequences": S(inputs.PAGED_DECODE, name="ms", wid=210, batch=70, seq_len=(40, 700)),
 }
 
 
