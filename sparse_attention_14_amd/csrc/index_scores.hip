@@ -284,18 +284,31 @@ __global__ __launch_bounds__(kPThreads) void scores_prefill_kernel(float *__rest
     const int nsteps = (k1 - k0 + kPStepKeys - 1) / kPStepKeys;
 
     // key step loads: thread t takes 16-byte chunks t and t + 512 of the step's
-    // 64 rows (row = c / 16, chunk = c % 16); rows past k1 are clamped to k1 - 1
+    // 64 rows (row = c / 16, chunk = c % 16); rows past k1 are clamped to
+    // k1 - 1.  A step starts on a multiple of 64 tokens, so with blocks of a
+    // multiple of 64 tokens (or a contiguous cache) it lies in one block: one
+    // lookup per step.
+    const bool one_block = keys.block_size % kPStepKeys == 0;
     auto load_step = [&](int st, u32x4 (&r)[2]) {
       const int sc = st < nsteps ? st : nsteps - 1;
+      const int t0 = k0 + sc * kPStepKeys;
+      int64_t blk0 = 0;
+      int slot0 = 0;
+      if (one_block) blk0 = cache_block(keys, seq, t0, slot0);
 #pragma unroll
       for (int x = 0; x < 2; ++x) {
         const int c = tid + kPThreads * x;
         const int row = c / CPR, ch = c % CPR;
-        int t = k0 + sc * kPStepKeys + row;
-        t = t < k1 ? t : k1 - 1;
-        int slot;
-        const int64_t blk = cache_block(keys, seq, t, slot);
-        r[x] = load16_nt(cache_row(keys, blk, slot) + 16 * ch);
+        const int t = t0 + row < k1 ? t0 + row : k1 - 1;
+        const uint8_t *src;
+        if (one_block) {
+          src = cache_row(keys, blk0, slot0 + (t - t0));
+        } else {
+          int slot;
+          const int64_t blk = cache_block(keys, seq, t, slot);
+          src = cache_row(keys, blk, slot);
+        }
+        r[x] = load16_nt(src + 16 * ch);
       }
     };
     auto store_step = [&](int st, const u32x4 (&r)[2]) {
@@ -307,31 +320,40 @@ __global__ __launch_bounds__(kPThreads) void scores_prefill_kernel(float *__rest
         *reinterpret_cast<u32x4 *>(buf + row * kPRowB + 16 * (ch ^ (row & (CPR - 1)))) = r[x];
       }
     };
+    auto epilogue = [&](const f32x16 &acc, int u, int key) {
+      float s = 0.0f;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) s = fmaf(wr[u][r], fmaxf(acc[r], 0.0f), s);
+      s += __shfl_xor(s, 32, 64);
+      const int qi = qbase + 2 * wave + u;
+      if (half == 0 && qs[u] == seq && key < qn[u] && key < k1) scores[(int64_t)qi * ld + key] = s;
+    };
+    // Per step: 4 (tile, query) combinations; the MFMAs of one overlap the
+    // epilogue (ReLU, head weights, head sum) of the previous one.
     auto compute_step = [&](int st) {
       const uint8_t *buf = ring[st % 3];
       const int kb = k0 + st * kPStepKeys;
+      bf16x8 b[2][KS];
 #pragma unroll
       for (int tl = 0; tl < 2; ++tl) {
         const int row = tl * 32 + col;
-        bf16x8 b[KS];
 #pragma unroll
         for (int j = 0; j < KS; ++j) {
           const int ch = half * (CPR / 2) + j;
-          b[j] = as_bf16x8(*reinterpret_cast<const u32x4 *>(buf + row * kPRowB + 16 * (ch ^ (row & (CPR - 1)))));
+          b[tl][j] = as_bf16x8(*reinterpret_cast<const u32x4 *>(buf + row * kPRowB + 16 * (ch ^ (row & (CPR - 1)))));
         }
-        const int key = kb + row;
+      }
+      f32x16 prev = {};
 #pragma unroll
-        for (int u = 0; u < 2; ++u) {
-          f32x16 acc = {};
+      for (int c = 0; c <= 4; ++c) {
+        f32x16 acc = {};
+        if (c < 4) {
+          const int tl = c >> 1, u = c & 1;
 #pragma unroll
-          for (int ks = 0; ks < KS; ++ks) acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[u][ks], b[ks], acc, 0, 0, 0);
-          float s = 0.0f;
-#pragma unroll
-          for (int r = 0; r < 16; ++r) s = fmaf(wr[u][r], fmaxf(acc[r], 0.0f), s);
-          s += __shfl_xor(s, 32, 64);
-          const int qi = qbase + 2 * wave + u;
-          if (half == 0 && qs[u] == seq && key < qn[u] && key < k1) scores[(int64_t)qi * ld + key] = s;
+          for (int ks = 0; ks < KS; ++ks) acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[u][ks], b[tl][ks], acc, 0, 0, 0);
         }
+        if (c > 0) epilogue(prev, (c - 1) & 1, kb + ((c - 1) >> 1) * 32 + col);
+        prev = acc;
       }
     };
 
@@ -443,8 +465,8 @@ hipError_t dispatch(float *scores, int64_t ld, const void *q, int q_dt, const fl
   const bool two = n_heads > 32;
   if (!fp8 && D == 128 && !two && n_q >= kPrefillMinQueries && !sb.bounds && !seq_ident) {
     const int blocks = (n_q + kPQ - 1) / kPQ;
-    // split the keys so that about 256 workgroups run
-    int splits = (256 + blocks - 1) / blocks;
+    // split the keys so that about 512 workgroups run
+    int splits = (512 + blocks - 1) / blocks;
     int per = (max_len + splits - 1) / splits;
     per = (per + kPStepKeys - 1) / kPStepKeys * kPStepKeys;
     splits = (max_len + per - 1) / per;
