@@ -32,6 +32,7 @@ constexpr float kLn2 = 0.6931471805599453f;
 constexpr int kW = 576, kL = 512, kTile = 64, kHG = 16;
 constexpr int kRowBytes = kW * 2 + 16;          // padded LDS row
 constexpr int kChunks = kW * 2 / 16;            // 16-byte chunks per row (72)
+constexpr int kMaxSplits = 32;
 
 struct AttArgs {
   float *out;
@@ -72,12 +73,20 @@ __device__ __forceinline__ i16x4 lds_read_tr(const uint8_t *p) {
       (__attribute__((address_space(3))) i16x4 *)(reinterpret_cast<uintptr_t>(p)));
 }
 
+// Two teams of four wavefronts: per step the workgroup gathers 128 kept rows
+// (thread t copies 18 16-byte chunks of row t / 4 from one base address), and
+// team t scores rows [64 t, 64 t + 64) with its own online softmax; the teams'
+// states are combined at the end.
+constexpr int kTeams = 2;
+constexpr int kStepRows = kTile * kTeams;    // 128
+constexpr int kAttThreads = 256 * kTeams;    // 512
+
 template <bool SPLIT>
-__global__ __launch_bounds__(256) void attend_bf16_kernel(AttArgs a) {
-  __shared__ __align__(16) uint8_t lrows[kTile * kRowBytes];
-  __shared__ __align__(16) uint16_t lp[2][kHG * kTile];  // P hi / lo, [head][row]
-  __shared__ float red[2][4][kHG];
-  extern __shared__ __align__(16) const uint8_t *lptr[];  // [rows_per_split] row addresses (null: empty slot)
+__global__ __launch_bounds__(kAttThreads) void attend_bf16_kernel(AttArgs a) {
+  __shared__ __align__(16) uint8_t lrows[kTeams][kTile * kRowBytes];
+  __shared__ __align__(16) uint16_t lp[kTeams][2][kHG * kTile];  // P hi / lo, [head][row]
+  __shared__ float red[kTeams][2][4][kHG];
+  __shared__ uint8_t lvalid[kStepRows];
 
   // XCD-aware mapping: workgroup ids i, i+8, i+16, ... run on one XCD; give the
   // n_hg head groups of a (query, split) pair ids 8 apart.
@@ -91,6 +100,7 @@ __global__ __launch_bounds__(256) void attend_bf16_kernel(AttArgs a) {
   const int sp = pair - qi * a.splits;
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int team = wave >> 2, tw = wave & 3;
   const int l16 = lane & 15, g4 = lane >> 4;
   const int H = a.n_heads;
   const int h0 = hg * kHG;
@@ -98,31 +108,7 @@ __global__ __launch_bounds__(256) void attend_bf16_kernel(AttArgs a) {
 
   const int j0 = sp * a.rows_per_split;
   const int j1 = min(j0 + a.rows_per_split, a.k);
-  const int nrows = j1 - j0;
-  const int ntiles = (nrows + kTile - 1) / kTile;
-
-  // all row addresses of this split, once
-  {
-    const int32_t *idx_row = a.indices + (int64_t)qi * a.k + j0;
-    for (int r = tid; r < ntiles * kTile; r += 256) {
-      const int t = r < nrows ? idx_row[r] : -1;
-      const uint8_t *p = nullptr;
-      if (t >= 0) {
-        int slot;
-        const int64_t blk = cache_block(a.latent, seq, t, slot);
-        p = cache_row(a.latent, blk, slot);
-      }
-      lptr[r] = p;
-    }
-  }
-
-  // q operand: head h0 + l16, dims 32*ks + 8*g4 + [0, 8)
-  bf16x8 qa[kW / 32];
-  {
-    const uint16_t *qr = a.q + ((int64_t)qi * H + h0 + l16) * kW + 8 * g4;
-#pragma unroll
-    for (int ks = 0; ks < kW / 32; ++ks) qa[ks] = as_bf16x8(load16(qr + 32 * ks));
-  }
+  const int nsteps = (j1 - j0 + kStepRows - 1) / kStepRows;
 
   float m_run[4], l_run[4];
 #pragma unroll
@@ -134,43 +120,56 @@ __global__ __launch_bounds__(256) void attend_bf16_kernel(AttArgs a) {
 #pragma unroll
   for (int nt = 0; nt < 8; ++nt) o[nt] = f32x4{0, 0, 0, 0};
 
-  // gather: chunk c = tid + 256 i of the tile is row c / 72, bytes 16 (c % 72)
-  constexpr int kPer = kTile * kChunks / 256;  // 18
-  u32x4 v[kPer];
-  auto issue = [&](int tile) {
-#pragma unroll
-    for (int i = 0; i < kPer; ++i) {
-      const int c = tid + 256 * i;
-      const int r = c / kChunks, cc = c - r * kChunks;
-      const uint8_t *p = lptr[tile * kTile + r];
-      v[i] = p ? load16(p + cc * 16) : u32x4{0, 0, 0, 0};
-    }
-  };
-  __syncthreads();
-  if (ntiles > 0) issue(0);
+  // q operand (head h0 + l16, dims 32*ks + 8*g4 + [0, 8)): loaded after the
+  // first step's index and row loads are issued, so those are not queued
+  // behind it
+  bf16x8 qa[kW / 32];
+  const uint16_t *qr = a.q + ((int64_t)qi * H + h0 + l16) * kW + 8 * g4;
 
-  for (int tile = 0; tile < ntiles; ++tile) {
+  uint8_t *my_rows = lrows[team];
+  uint16_t *my_p = lp[team][0];
+  // gather role: row gr = tid / 4 of the step, chunks gq + 4 j (j < 18)
+  const int gr = tid >> 2, gq = tid & 3;
+  constexpr int kPer = kChunks / 4;   // 18
+
+  for (int step = 0; step < nsteps; ++step) {
+    {
+      const int j = j0 + step * kStepRows + gr;
+      const int t = j < j1 ? a.indices[(int64_t)qi * a.k + j] : -1;
+      u32x4 v[kPer];
+      if (t >= 0) {
+        int slot;
+        const int64_t blk = cache_block(a.latent, seq, t, slot);
+        const uint8_t *p = cache_row(a.latent, blk, slot) + 16 * gq;
 #pragma unroll
-    for (int i = 0; i < kPer; ++i) {
-      const int c = tid + 256 * i;
-      const int r = c / kChunks, cc = c - r * kChunks;
-      *reinterpret_cast<u32x4 *>(lrows + r * kRowBytes + cc * 16) = v[i];
+        for (int i = 0; i < kPer; ++i) v[i] = load16(p + 64 * i);
+      } else {
+#pragma unroll
+        for (int i = 0; i < kPer; ++i) v[i] = u32x4{0, 0, 0, 0};
+      }
+      if (step == 0) {
+#pragma unroll
+        for (int ks = 0; ks < kW / 32; ++ks) qa[ks] = as_bf16x8(load16(qr + 32 * ks));
+      }
+      if (gq == 0) lvalid[gr] = t >= 0 ? 1 : 0;
+      uint8_t *dst = lrows[gr / kTile] + (gr % kTile) * kRowBytes + 16 * gq;
+#pragma unroll
+      for (int i = 0; i < kPer; ++i) *reinterpret_cast<u32x4 *>(dst + 64 * i) = v[i];
     }
     __syncthreads();
-    if (tile + 1 < ntiles) issue(tile + 1);   // in flight during this tile's math
 
-    // QK^T: this wavefront's 16 rows
-    const int row = wave * 16 + l16;
+    // QK^T: this wavefront's 16 rows of its team's tile
+    const int row = tw * 16 + l16;
     f32x4 sacc = {0, 0, 0, 0};
     {
-      const uint8_t *rp = lrows + row * kRowBytes + 16 * g4;
+      const uint8_t *rp = my_rows + row * kRowBytes + 16 * g4;
 #pragma unroll
       for (int ks = 0; ks < kW / 32; ++ks) {
         const bf16x8 b = as_bf16x8(*reinterpret_cast<const u32x4 *>(rp + 64 * ks));
         sacc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qa[ks], b, sacc, 0, 0, 0);
       }
     }
-    const bool valid = lptr[tile * kTile + row] != nullptr;
+    const bool valid = lvalid[team * kTile + row] != 0;
     float z[4], mx[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
@@ -179,32 +178,33 @@ __global__ __launch_bounds__(256) void attend_bf16_kernel(AttArgs a) {
     }
     if (l16 == 0)
 #pragma unroll
-      for (int i = 0; i < 4; ++i) red[0][wave][4 * g4 + i] = mx[i];
+      for (int i = 0; i < 4; ++i) red[team][0][tw][4 * g4 + i] = mx[i];
     __syncthreads();
 
     float m_new[4], alpha[4], ps[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int h = 4 * g4 + i;
-      const float tm = fmaxf(fmaxf(red[0][0][h], red[0][1][h]), fmaxf(red[0][2][h], red[0][3][h]));
+      const float tm =
+          fmaxf(fmaxf(red[team][0][0][h], red[team][0][1][h]), fmaxf(red[team][0][2][h], red[team][0][3][h]));
       m_new[i] = fmaxf(m_run[i], tm);
       const float mu = m_new[i] == -INFINITY ? 0.0f : m_new[i];
       alpha[i] = exp2f(m_run[i] - mu);
       const float p = exp2f(z[i] - mu);
       const uint16_t hi = float_to_bf16_bits(p);
       const uint16_t lo = float_to_bf16_bits(p - bf16_bits_to_float(hi));
-      lp[0][h * kTile + row] = hi;
-      lp[1][h * kTile + row] = lo;
+      my_p[h * kTile + row] = hi;
+      my_p[kHG * kTile + h * kTile + row] = lo;
       ps[i] = row16_sum(p);
     }
     if (l16 == 0)
 #pragma unroll
-      for (int i = 0; i < 4; ++i) red[1][wave][4 * g4 + i] = ps[i];
+      for (int i = 0; i < 4; ++i) red[team][1][tw][4 * g4 + i] = ps[i];
     __syncthreads();
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int h = 4 * g4 + i;
-      const float tsum = ((red[1][0][h] + red[1][1][h]) + red[1][2][h]) + red[1][3][h];
+      const float tsum = ((red[team][1][0][h] + red[team][1][1][h]) + red[team][1][2][h]) + red[team][1][3][h];
       l_run[i] = l_run[i] * alpha[i] + tsum;
       m_run[i] = m_new[i];
     }
@@ -213,13 +213,14 @@ __global__ __launch_bounds__(256) void attend_bf16_kernel(AttArgs a) {
 #pragma unroll
       for (int i = 0; i < 4; ++i) o[nt][i] *= alpha[i];
 
-    // PV: rows 32*ks2 + 8*g4 + e, columns 128*wave + 16*nt + l16; the V
-    // operand comes from two transposed LDS reads of 4 rows each
+    // PV: rows 32*ks2 + 8*g4 + e, columns 128*tw + 16*nt + l16; the V operand
+    // comes from two transposed LDS reads of 4 rows each
 #pragma unroll
     for (int ks2 = 0; ks2 < kTile / 32; ++ks2) {
-      const bf16x8 ahi = as_bf16x8(*reinterpret_cast<const u32x4 *>(&lp[0][l16 * kTile + 32 * ks2 + 8 * g4]));
-      const bf16x8 alo = as_bf16x8(*reinterpret_cast<const u32x4 *>(&lp[1][l16 * kTile + 32 * ks2 + 8 * g4]));
-      const uint8_t *vb = lrows + (32 * ks2 + 8 * g4 + (l16 >> 2)) * kRowBytes + (128 * wave + 4 * (l16 & 3)) * 2;
+      const bf16x8 ahi = as_bf16x8(*reinterpret_cast<const u32x4 *>(&my_p[l16 * kTile + 32 * ks2 + 8 * g4]));
+      const bf16x8 alo =
+          as_bf16x8(*reinterpret_cast<const u32x4 *>(&my_p[kHG * kTile + l16 * kTile + 32 * ks2 + 8 * g4]));
+      const uint8_t *vb = my_rows + (32 * ks2 + 8 * g4 + (l16 >> 2)) * kRowBytes + (128 * tw + 4 * (l16 & 3)) * 2;
 #pragma unroll
       for (int nt = 0; nt < 8; ++nt) {
         const i16x4 v0 = lds_read_tr(vb + 32 * nt);
@@ -234,16 +235,46 @@ __global__ __launch_bounds__(256) void attend_bf16_kernel(AttArgs a) {
     __syncthreads();
   }
 
-  // epilogue: lane holds heads h0 + 4*g4 + i, columns 128*wave + 16*nt + l16
+  // combine the teams: team 1 hands its state to team 0 through LDS
+  float *xo = reinterpret_cast<float *>(lrows[1]);              // [16 heads][512]
+  float *xml = reinterpret_cast<float *>(lrows[1]) + kHG * kL;  // [16 heads][2]
+  if (team == 1) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int h = 4 * g4 + i;
+#pragma unroll
+      for (int nt = 0; nt < 8; ++nt) xo[h * kL + 128 * tw + 16 * nt + l16] = o[nt][i];
+      if (tw == 0 && l16 == 0) {
+        xml[2 * h] = m_run[i];
+        xml[2 * h + 1] = l_run[i];
+      }
+    }
+  }
+  __syncthreads();
+  if (team == 1) return;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int h = 4 * g4 + i;
+    const float m1 = xml[2 * h], l1 = xml[2 * h + 1];
+    const float m = fmaxf(m_run[i], m1);
+    const float mu = m == -INFINITY ? 0.0f : m;
+    const float a0 = exp2f(m_run[i] - mu), a1 = exp2f(m1 - mu);
+    l_run[i] = a0 * l_run[i] + a1 * l1;
+    m_run[i] = m;
+#pragma unroll
+    for (int nt = 0; nt < 8; ++nt) o[nt][i] = a0 * o[nt][i] + a1 * xo[h * kL + 128 * tw + 16 * nt + l16];
+  }
+
+  // epilogue: lane holds heads h0 + 4*g4 + i, columns 128*tw + 16*nt + l16
   if (!SPLIT) {
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int head = h0 + 4 * g4 + i;
       const float inv = l_run[i] > 0.0f ? 1.0f / l_run[i] : 0.0f;
-      float *orow = a.out + ((int64_t)qi * H + head) * kL + 128 * wave + l16;
+      float *orow = a.out + ((int64_t)qi * H + head) * kL + 128 * tw + l16;
 #pragma unroll
       for (int nt = 0; nt < 8; ++nt) orow[16 * nt] = o[nt][i] * inv;
-      if (wave == 0 && l16 == 0 && a.lse)
+      if (tw == 0 && l16 == 0 && a.lse)
         a.lse[(int64_t)qi * H + head] = l_run[i] > 0.0f ? (m_run[i] + log2f(l_run[i])) * kLn2 : -INFINITY;
     }
   } else {
@@ -251,10 +282,10 @@ __global__ __launch_bounds__(256) void attend_bf16_kernel(AttArgs a) {
     for (int i = 0; i < 4; ++i) {
       const int head = h0 + 4 * g4 + i;
       const int64_t base = ((int64_t)(qi * a.splits + sp) * H + head);
-      float *orow = a.part_o + base * kL + 128 * wave + l16;
+      float *orow = a.part_o + base * kL + 128 * tw + l16;
 #pragma unroll
       for (int nt = 0; nt < 8; ++nt) orow[16 * nt] = o[nt][i];
-      if (wave == 0 && l16 == 0) {
+      if (tw == 0 && l16 == 0) {
         a.part_ml[base * 2 + 0] = m_run[i];
         a.part_ml[base * 2 + 1] = l_run[i];
       }
@@ -265,7 +296,6 @@ __global__ __launch_bounds__(256) void attend_bf16_kernel(AttArgs a) {
 // Combine split partials in split order.  One workgroup per (query, head): one
 // wavefront turns the splits' (max, sum) into weights, then every thread sums
 // its 4 columns over the splits with all loads in flight.
-constexpr int kMaxSplits = 32;
 __global__ __launch_bounds__(128) void merge_kernel(float *__restrict__ out, float *__restrict__ lse,
                                                     const float *__restrict__ part_o,
                                                     const float *__restrict__ part_ml, int splits, int H, int L) {
@@ -394,20 +424,18 @@ AttendPlan plan_attend(int n_q, int n_heads, int kv_lora, int width, int k, int 
   p.width = width;
   p.k = k;
   p.splits = 1;
-  p.rows_per_split = (k + kTile - 1) / kTile * kTile;
+  p.rows_per_split = (k + kStepRows - 1) / kStepRows * kStepRows;
   if (dtype == kBF16 && n_heads >= kHG) {
     const int n_hg = n_heads / kHG;
-    const int tiles = (k + kTile - 1) / kTile;
-    // ~256 workgroups, but at least two tiles per split so the partial outputs
-    // (H x L floats per split) stay below the rows they summarise.
+    const int steps = (k + kStepRows - 1) / kStepRows;
+    // ~256 workgroups; each split is a whole number of 128-row steps
     int s = (256 + n_q * n_hg - 1) / (n_q * n_hg);
-    const int most = (tiles + 1) / 2;
-    if (s > most) s = most;
+    if (s > steps) s = steps;
     if (s > kMaxSplits) s = kMaxSplits;
     if (s < 1) s = 1;
-    const int tps = (tiles + s - 1) / s;
-    p.rows_per_split = tps * kTile;
-    p.splits = (tiles + tps - 1) / tps;
+    const int sps = (steps + s - 1) / s;
+    p.rows_per_split = sps * kStepRows;
+    p.splits = (steps + sps - 1) / sps;
   }
   size_t off = 0;
   auto take = [&](size_t bytes) {
@@ -451,17 +479,16 @@ hipError_t launch_attend(float *out, float *lse, const void *q, int dt, const Ca
   uint8_t *ws = static_cast<uint8_t *>(workspace);
   const int groups = (a.pairs + 7) / 8;
   const dim3 grid(groups * 8 * a.n_hg);
-  const size_t lptr_bytes = (size_t)(plan.rows_per_split + kTile) * sizeof(void *);
   if (plan.splits > 1) {
     a.part_o = reinterpret_cast<float *>(ws + plan.off_part_o);
     a.part_ml = reinterpret_cast<float *>(ws + plan.off_part_ml);
-    hipLaunchKernelGGL(attend_bf16_kernel<true>, grid, dim3(256), lptr_bytes, stream, a);
+    hipLaunchKernelGGL(attend_bf16_kernel<true>, grid, dim3(kAttThreads), 0, stream, a);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL(merge_kernel, dim3(n_q * n_heads), dim3(128), 0, stream, out, lse, a.part_o, a.part_ml,
                        plan.splits, n_heads, kv_lora);
   } else {
-    hipLaunchKernelGGL(attend_bf16_kernel<false>, grid, dim3(256), lptr_bytes, stream, a);
+    hipLaunchKernelGGL(attend_bf16_kernel<false>, grid, dim3(kAttThreads), 0, stream, a);
   }
   return hipGetLastError();
 }
