@@ -22,6 +22,22 @@
 namespace dsa {
 namespace {
 
+// max(x, 0) / min(x, 0) on the bits: IEEE floats order like sign-magnitude
+// integers, so a signed-integer clamp is the float clamp (-0 becomes +0), in one
+// instruction.  lim = INT_MAX keeps the positive side, INT_MIN the negative one.
+__device__ __forceinline__ float relu_side(float x, int lim) {
+  const int b = __float_as_int(x);
+  return __int_as_float(lim >= 0 ? min(max(b, 0), lim) : max(min(b, 0), lim));
+}
+__device__ __forceinline__ float relu(float x) { return __int_as_float(max(__float_as_int(x), 0)); }
+
+// Sum of a value over lanes l and l ^ 32, the same in both lanes and formed in
+// the same order (lower half first) in both.
+__device__ __forceinline__ float halves_sum(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
 constexpr int kMaxTilesPerWave = 8;
 constexpr int kPrefillMinQueries = 64;   // the GEMM-shaped kernel takes over from here
 
@@ -152,9 +168,9 @@ __global__ __launch_bounds__(256) void scores_mfma_kernel(float *__restrict__ sc
         }
       }
       // Epilogue.  fp8: ReLU(acc * sc) * w summed over heads equals
-      // sc * sum w * med3(acc, 0, +-inf) (the ReLU side flips with the sign of
-      // sc), with one multiply per key instead of one per head.
-      const float lim = sc >= 0.0f ? INFINITY : -INFINITY;
+      // sc * sum w * (acc clamped to the side of 0 that the sign of sc keeps),
+      // with one multiply per key instead of one per head.
+      const int lim = sc >= 0.0f ? 0x7FFFFFFF : (int)0x80000000;
       float s = 0.0f;
 #pragma unroll
       for (int mt = 0; mt < MT; ++mt) {
@@ -162,11 +178,10 @@ __global__ __launch_bounds__(256) void scores_mfma_kernel(float *__restrict__ sc
 #pragma unroll
         for (int ks = 0; ks < KS; ++ks) acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[mt][ks], b[ks], acc, 0, 0, 0);
 #pragma unroll
-        for (int r = 0; r < 16; ++r)
-          s = fmaf(wr[mt][r], FP8 ? __builtin_amdgcn_fmed3f(acc[r], 0.0f, lim) : fmaxf(acc[r], 0.0f), s);
+        for (int r = 0; r < 16; ++r) s = fmaf(wr[mt][r], FP8 ? relu_side(acc[r], lim) : relu(acc[r]), s);
       }
       if (FP8) s *= sc;
-      s += __shfl_xor(s, 32, 64);
+      s = halves_sum(s);
       const int t = (tile_begin + it) * 32 + col;
       const bool ok = half == 0 && t < n;
       if (ok) scores[(int64_t)qi * ld + t] = s;
@@ -209,6 +224,7 @@ constexpr int kPQ = 16;            // queries per workgroup
 constexpr int kPStepKeys = 64;     // keys per step (two 32-key tiles)
 constexpr int kPThreads = 512;
 constexpr int kPRowB = 256;        // bf16 key row bytes (128 dims)
+constexpr int kPLdsRow = kPRowB + 16;   // padded LDS row: conflict-free 16-byte operand reads
 
 __global__ __launch_bounds__(kPThreads) void scores_prefill_kernel(float *__restrict__ scores, int64_t ld,
                                                                    const uint16_t *__restrict__ q,
@@ -217,7 +233,7 @@ __global__ __launch_bounds__(kPThreads) void scores_prefill_kernel(float *__rest
                                                                    const int32_t *__restrict__ q_len, int n_q,
                                                                    int n_heads, int keys_per_split) {
   constexpr int D = 128, KS = D / 16, HALF = D / 2, CPR = kPRowB / 16;   // 16 chunks per row
-  __shared__ __align__(16) uint8_t ring[3][kPStepKeys * kPRowB];            // 3 x 16 KB
+  __shared__ __align__(16) uint8_t ring[3][kPStepKeys * kPLdsRow];          // 3 x 17 KB
   __shared__ int32_t sseq[kPQ], slen[kPQ];
   __shared__ int32_t groups[kPQ + 1];
 
@@ -267,10 +283,13 @@ __global__ __launch_bounds__(kPThreads) void scores_prefill_kernel(float *__rest
     }
   }
   __syncthreads();
+  float *orow[2];   // this wavefront's score rows
 #pragma unroll
   for (int u = 0; u < 2; ++u) {
     qn[u] = slen[2 * wave + u];
     qs[u] = sseq[2 * wave + u];
+    const int qi = qbase + 2 * wave + u;
+    orow[u] = scores + (int64_t)(qi < n_q ? qi : 0) * ld;
   }
   const int ngroups = groups[kPQ];
 
@@ -283,77 +302,81 @@ __global__ __launch_bounds__(kPThreads) void scores_prefill_kernel(float *__rest
     if (k0 >= k1) continue;   // uniform over the workgroup
     const int nsteps = (k1 - k0 + kPStepKeys - 1) / kPStepKeys;
 
-    // key step loads: thread t takes 16-byte chunks t and t + 512 of the step's
-    // 64 rows (row = c / 16, chunk = c % 16); rows past k1 are clamped to
-    // k1 - 1.  A step starts on a multiple of 64 tokens, so with blocks of a
-    // multiple of 64 tokens (or a contiguous cache) it lies in one block: one
-    // lookup per step.
+    // key step loads: thread t takes 16-byte chunk ch = t % 16 of rows
+    // t / 16 and t / 16 + 32 of the step; rows past k1 are clamped to k1 - 1.
+    // A step starts on a multiple of 64 tokens, so with blocks of a multiple of
+    // 64 tokens (or a contiguous cache) it lies in one block: one lookup per
+    // step, and the per-thread part of the address is fixed.
     const bool one_block = keys.block_size % kPStepKeys == 0;
+    const int lrow = tid / CPR, lch = tid % CPR;
+    const int64_t toff[2] = {(int64_t)lrow * keys.row_stride + 16 * lch,
+                             (int64_t)(lrow + 32) * keys.row_stride + 16 * lch};
     auto load_step = [&](int st, u32x4 (&r)[2]) {
       const int sc = st < nsteps ? st : nsteps - 1;
       const int t0 = k0 + sc * kPStepKeys;
-      int64_t blk0 = 0;
-      int slot0 = 0;
-      if (one_block) blk0 = cache_block(keys, seq, t0, slot0);
+      if (one_block && t0 + kPStepKeys <= k1) {
+        int slot0;
+        const int64_t blk0 = cache_block(keys, seq, t0, slot0);
+        const uint8_t *base = cache_row(keys, blk0, slot0);
 #pragma unroll
-      for (int x = 0; x < 2; ++x) {
-        const int c = tid + kPThreads * x;
-        const int row = c / CPR, ch = c % CPR;
-        const int t = t0 + row < k1 ? t0 + row : k1 - 1;
-        const uint8_t *src;
-        if (one_block) {
-          src = cache_row(keys, blk0, slot0 + (t - t0));
-        } else {
+        for (int x = 0; x < 2; ++x) r[x] = load16_nt(base + toff[x]);
+      } else {
+#pragma unroll
+        for (int x = 0; x < 2; ++x) {
+          const int row = lrow + 32 * x;
+          const int t = t0 + row < k1 ? t0 + row : k1 - 1;
           int slot;
           const int64_t blk = cache_block(keys, seq, t, slot);
-          src = cache_row(keys, blk, slot);
+          r[x] = load16_nt(cache_row(keys, blk, slot) + 16 * lch);
         }
-        r[x] = load16_nt(src + 16 * ch);
       }
     };
     auto store_step = [&](int st, const u32x4 (&r)[2]) {
-      uint8_t *buf = ring[st % 3];
-#pragma unroll
-      for (int x = 0; x < 2; ++x) {
-        const int c = tid + kPThreads * x;
-        const int row = c / CPR, ch = c % CPR;
-        *reinterpret_cast<u32x4 *>(buf + row * kPRowB + 16 * (ch ^ (row & (CPR - 1)))) = r[x];
-      }
+      uint8_t *buf = ring[st % 3] + lrow * kPLdsRow + 16 * lch;
+      *reinterpret_cast<u32x4 *>(buf) = r[0];
+      *reinterpret_cast<u32x4 *>(buf + 32 * kPLdsRow) = r[1];
     };
+    // key operand of tile tl: lane (col, half) reads 128 contiguous bytes of row
+    // 32 tl + col from byte 128 half (the padded rows keep 16 lanes on distinct banks)
+    const int bofs = col * kPLdsRow + 128 * half;
+    // full[u]: every key of the step is visible to query u (wave-uniform)
+    bool full[2];
     auto epilogue = [&](const f32x16 &acc, int u, int key) {
       float s = 0.0f;
 #pragma unroll
-      for (int r = 0; r < 16; ++r) s = fmaf(wr[u][r], fmaxf(acc[r], 0.0f), s);
-      s += __shfl_xor(s, 32, 64);
-      const int qi = qbase + 2 * wave + u;
-      if (half == 0 && qs[u] == seq && key < qn[u] && key < k1) scores[(int64_t)qi * ld + key] = s;
+      for (int r = 0; r < 16; ++r) s = fmaf(wr[u][r], relu(acc[r]), s);
+      s = halves_sum(s);
+      if (full[u]) {
+        orow[u][key] = s;   // both lane halves hold the same sum: one unmasked store
+      } else if (half == 0 && qs[u] == seq && key < qn[u] && key < k1) {
+        orow[u][key] = s;
+      }
     };
     // Per step: 4 (tile, query) combinations; the MFMAs of one overlap the
     // epilogue (ReLU, head weights, head sum) of the previous one.
     auto compute_step = [&](int st) {
       const uint8_t *buf = ring[st % 3];
       const int kb = k0 + st * kPStepKeys;
+#pragma unroll
+      for (int u = 0; u < 2; ++u) full[u] = qs[u] == seq && kb + kPStepKeys <= qn[u] && kb + kPStepKeys <= k1;
       bf16x8 b[2][KS];
 #pragma unroll
       for (int tl = 0; tl < 2; ++tl) {
-        const int row = tl * 32 + col;
+        const uint8_t *rp = buf + tl * 32 * kPLdsRow + bofs;
 #pragma unroll
-        for (int j = 0; j < KS; ++j) {
-          const int ch = half * (CPR / 2) + j;
-          b[tl][j] = as_bf16x8(*reinterpret_cast<const u32x4 *>(buf + row * kPRowB + 16 * (ch ^ (row & (CPR - 1)))));
-        }
+        for (int j = 0; j < KS; ++j) b[tl][j] = as_bf16x8(*reinterpret_cast<const u32x4 *>(rp + 16 * j));
       }
-      f32x16 prev = {};
+      f32x16 acc[2];   // combination c accumulates in acc[c & 1]
 #pragma unroll
       for (int c = 0; c <= 4; ++c) {
-        f32x16 acc = {};
         if (c < 4) {
           const int tl = c >> 1, u = c & 1;
+          acc[c & 1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[u][0], b[tl][0], f32x16{}, 0, 0, 0);
 #pragma unroll
-          for (int ks = 0; ks < KS; ++ks) acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[u][ks], b[tl][ks], acc, 0, 0, 0);
+          for (int ks = 1; ks < KS; ++ks)
+            acc[c & 1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[u][ks], b[tl][ks], acc[c & 1], 0, 0, 0);
         }
-        if (c > 0) epilogue(prev, (c - 1) & 1, kb + ((c - 1) >> 1) * 32 + col);
-        prev = acc;
+        if (c > 0) epilogue(acc[(c - 1) & 1], (c - 1) & 1, kb + ((c - 1) >> 1) * 32 + col);
       }
     };
 
