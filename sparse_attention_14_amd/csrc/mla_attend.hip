@@ -33,6 +33,7 @@ constexpr int kW = 576, kL = 512, kTile = 64, kHG = 16;
 constexpr int kRowBytes = kW * 2 + 16;          // padded LDS row
 constexpr int kChunks = kW * 2 / 16;            // 16-byte chunks per row (72)
 constexpr int kMaxSplits = 32;
+constexpr int kAttTargetWGs = 256;   // workgroups aimed at by the split count
 
 struct AttArgs {
   float *out;
@@ -429,7 +430,7 @@ AttendPlan plan_attend(int n_q, int n_heads, int kv_lora, int width, int k, int 
     const int n_hg = n_heads / kHG;
     const int steps = (k + kStepRows - 1) / kStepRows;
     // ~256 workgroups; each split is a whole number of 128-row steps
-    int s = (256 + n_q * n_hg - 1) / (n_q * n_hg);
+    int s = (kAttTargetWGs + n_q * n_hg - 1) / (n_q * n_hg);
     if (s > steps) s = steps;
     if (s > kMaxSplits) s = kMaxSplits;
     if (s < 1) s = 1;
