@@ -77,7 +77,8 @@ typedef enum {
  *     e4m3fn(byte) * scale), at scale[p * scale_block_stride + t % block_size];
  *     scale is ignored for other dtypes.
  *   - rows, row_stride and block_stride must be multiples of 16 bytes, and
- *     row_stride >= width * element size.
+ *     row_stride >= width * element size.  A row_stride above 16 MiB returns
+ *     DSA_ERR_UNSUPPORTED.
  */
 typedef struct {
   const void *rows;

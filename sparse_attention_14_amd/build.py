@@ -17,6 +17,12 @@ OUT = os.path.join(HERE, "libdsa.so")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
 
+# Per-file code-generation options.  index_scores.hip: MFMA results in ordinary
+# VGPRs (not accumulation registers), so the score epilogue reads them without a
+# v_accvgpr_read copy per element.
+FILE_FLAGS = {"index_scores.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
+
+
 def sources():
     return sorted(glob.glob(os.path.join(HERE, "csrc", "*.hip")))
 
@@ -32,7 +38,7 @@ def build(verbose: bool = False, jobs: int = 4) -> str:
     for src in sources():
         obj = os.path.join(objdir, os.path.basename(src) + ".o")
         objs.append(obj)
-        cmd = [HIPCC, *flags, "-c", src, "-o", obj]
+        cmd = [HIPCC, *flags, *FILE_FLAGS.get(os.path.basename(src), []), "-c", src, "-o", obj]
         if verbose:
             print(" ".join(cmd), flush=True)
         procs.append((cmd, subprocess.Popen(cmd, stdout=subprocess.PIPE, stderr=subprocess.STDOUT)))

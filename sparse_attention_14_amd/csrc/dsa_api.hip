@@ -29,6 +29,7 @@ dsa_status check_cache(const dsa_cache *c) {
   if (c->dtype == DSA_FP8_E4M3FN && (!c->scale || c->scale_block_stride < c->block_size))
     return DSA_ERR_INVALID_ARGUMENT;
   if (!aligned16(c->rows) || (c->row_stride & 15) || (c->block_stride & 15)) return DSA_ERR_UNSUPPORTED;
+  if (c->row_stride > (int64_t(1) << 24)) return DSA_ERR_UNSUPPORTED;   // in-tile offsets are 32-bit
   if (c->block_table && (c->block_size & 31)) return DSA_ERR_UNSUPPORTED;
   return DSA_OK;
 }

@@ -22,13 +22,9 @@
 namespace dsa {
 namespace {
 
-// max(x, 0) / min(x, 0) on the bits: IEEE floats order like sign-magnitude
-// integers, so a signed-integer clamp is the float clamp (-0 becomes +0), in one
-// instruction.  lim = INT_MAX keeps the positive side, INT_MIN the negative one.
-__device__ __forceinline__ float relu_side(float x, int lim) {
-  const int b = __float_as_int(x);
-  return __int_as_float(lim >= 0 ? min(max(b, 0), lim) : max(min(b, 0), lim));
-}
+// max(x, 0) on the bits: IEEE floats order like sign-magnitude integers, so a
+// signed-integer max with 0 is the float ReLU (-0 becomes +0, a negative NaN 0),
+// in one instruction.
 __device__ __forceinline__ float relu(float x) { return __int_as_float(max(__float_as_int(x), 0)); }
 
 // Sum of a value over lanes l and l ^ 32, the same in both lanes and formed in
@@ -41,11 +37,14 @@ __device__ __forceinline__ float halves_sum(float x) {
 constexpr int kMaxTilesPerWave = 8;
 constexpr int kPrefillMinQueries = 64;   // the GEMM-shaped kernel takes over from here
 
+
 // One wavefront scores TPW consecutive 32-key tiles.  The tile loop is fully
 // unrolled and every tile load is issued unconditionally (tiles past the row's
 // end reload its last tile and their scores are dropped), so the code is
 // straight-line and the compiler waits for exactly the tile it needs while the
-// next P tiles stay in flight.
+// next P tiles stay in flight.  Tile positions, block-table lookups and tile
+// base addresses are wavefront-uniform (scalar); a lane adds one precomputed
+// 32-bit offset per load.
 template <bool FP8, int D, int MT, int TPW>
 __global__ __launch_bounds__(256) void scores_mfma_kernel(float *__restrict__ scores, int64_t ld,
                                                           const uint16_t *__restrict__ q, const float *__restrict__ w,
@@ -61,27 +60,102 @@ __global__ __launch_bounds__(256) void scores_mfma_kernel(float *__restrict__ sc
   constexpr int TILEB = 32 * ROWB;      // bytes of a 32-key tile
   constexpr int NLD = TILEB / 1024;     // 1 KB wavefront loads per tile
   constexpr int P = TPW < 2 ? TPW : 2;  // tiles in flight ahead of the one being scored
+  static_assert(64 % CPR == 0, "a 1 KB load must cover whole rows");
   __shared__ __align__(16) uint8_t stage_all[4][TILEB];
 
+  // Fetch every kernel argument at once: the compiler would otherwise load each
+  // one just before its first use, one dependent round trip after another.  The
+  // statement reads the arguments (so they are loaded before it) and yields a
+  // zero that the wavefront index depends on (so it runs first); it touches no
+  // memory.
+  int zero;
+  asm("s_mov_b32 %0, 0"
+      : "=s"(zero)
+      : "s"(scores), "s"(ld), "s"(q), "s"(w), "s"(keys.rows), "s"(keys.scale), "s"(keys.row_stride),
+        "s"(keys.block_stride), "s"(keys.scale_block_stride), "s"(keys.table), "s"(keys.block_size),
+        "s"(keys.max_blocks), "s"(q_seq), "s"(seq_ident), "s"(q_len), "s"(n_heads), "s"(bounds), "s"(topk));
   const int qi = blockIdx.y;
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int half = lane >> 5, col = lane & 31;
   const int n = q_len[qi];
   const int ntile = (n + 31) / 32;
-  const int wid = blockIdx.x * 4 + wave;
+  const int wid = blockIdx.x * 4 + wave + zero;
   const int tile_begin = wid * TPW;
-  uint32_t lane_max = 0;   // largest score key this lane wrote (bounds only)
+  float lane_best = -__builtin_inff();   // largest score of this lane's keys (bounds only)
 
   if (tile_begin < ntile) {
     const int seq = seq_of(q_seq, qi, seq_ident);
     uint8_t *stage = stage_all[wave];
-    // q as the A operand: lane (col, half) holds head 32*mt + col, dims half*HALF + 8*ks + [0, 8).
+    // First row, first scale and last visible row of every tile (a 32-key tile
+    // never straddles a block).  All of it is wavefront-uniform; the block
+    // lookups are issued together, before any vector load.
+    int bi[TPW], slot[TPW], tlast[TPW];
+#pragma unroll
+    for (int it = 0; it < TPW; ++it) {
+      int tile = tile_begin + it;
+      tile = tile < ntile ? tile : ntile - 1;
+      const int t0 = tile * 32;
+      bi[it] = t0 / keys.block_size;
+      slot[it] = t0 - bi[it] * keys.block_size;
+      tlast[it] = n - 1 - t0;
+    }
+    int blk[kMaxTilesPerWave] = {};
+    if (keys.table) {
+      const int32_t *trow = keys.table + (int64_t)seq * keys.max_blocks;
+#pragma unroll
+      for (int it = 0; it < TPW; ++it) blk[it] = trow[bi[it]];
+      // every lookup is in flight before the first is used
+      asm("" : "+s"(blk[0]), "+s"(blk[1]), "+s"(blk[2]), "+s"(blk[3]), "+s"(blk[4]), "+s"(blk[5]), "+s"(blk[6]),
+          "+s"(blk[7]));
+    } else {
+#pragma unroll
+      for (int it = 0; it < TPW; ++it) blk[it] = seq;
+    }
+    const uint8_t *tbase[TPW];
+    const float *sbase[TPW];
+#pragma unroll
+    for (int it = 0; it < TPW; ++it) {
+      tbase[it] = keys.rows + (int64_t)blk[it] * keys.block_stride + (int64_t)slot[it] * keys.row_stride;
+      sbase[it] = FP8 ? keys.scale + (int64_t)blk[it] * keys.scale_block_stride + slot[it] : nullptr;
+    }
+
+    // Loads are coalesced: 16-byte piece j*64 + lane of the tile's rows (1 KB per
+    // wavefront instruction), i.e. row (64 j + lane) / CPR, chunk lane % CPR.
+    // A row past the last visible one is replaced by the last visible row, by a
+    // min() on the byte offsets (the row stride is positive and below 2^24).
+    // They go through a wavefront-private LDS tile (chunk slots XOR-swizzled by
+    // the row against bank conflicts) into the MFMA operand layout.  Keys are
+    // read once per call: non-temporal loads.
+    const uint32_t rs = (uint32_t)keys.row_stride;
+    const uint32_t ch16 = 16u * (uint32_t)(lane % CPR);
+    uint32_t loff[NLD];
+#pragma unroll
+    for (int j = 0; j < NLD; ++j) loff[j] = (uint32_t)((64 * j + lane) / CPR) * rs + ch16;
+    struct Raw {
+      u32x4 v[NLD];
+      float sc;
+    };
+    auto issue = [&](int it, Raw &r) {
+      const uint32_t lim = (uint32_t)tlast[it] * rs + ch16;
+#pragma unroll
+      for (int j = 0; j < NLD; ++j) r.v[j] = load16_nt(tbase[it] + (loff[j] < lim ? loff[j] : lim));
+      if (FP8) r.sc = sbase[it][col < tlast[it] ? col : tlast[it]];
+    };
+    Raw buf[P];
+#pragma unroll
+    for (int p = 0; p < P; ++p) issue(p, buf[p]);
+
+    // q as the A operand: lane (col, half) holds head 32*mt + col, dims
+    // half*HALF + 8*ks + [0, 8); head weights per accumulator element.  Loaded
+    // after the first key tiles and unconditionally (clamped, then zeroed), so
+    // that no branch separates the key loads from their use.
     bf16x8 a[MT][KS];
     float wr[MT][16];
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt) {
       const int head = 32 * mt + col;
-      const uint16_t *qrow = q + ((int64_t)qi * n_heads + (head < n_heads ? head : 0)) * D + half * HALF;
+      const uint16_t *qrow = q + ((int64_t)qi * n_heads + (head < n_heads ? head : n_heads - 1)) * D + half * HALF;
 #pragma unroll
       for (int ks = 0; ks < KS; ++ks) {
         u32x4 v = load16(qrow + 8 * ks);
@@ -92,51 +166,10 @@ __global__ __launch_bounds__(256) void scores_mfma_kernel(float *__restrict__ sc
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         const int m = 32 * mt + 8 * (r >> 2) + 4 * half + (r & 3);
-        wr[mt][r] = m < n_heads ? w[(int64_t)qi * n_heads + m] : 0.0f;
+        const float x = w[(int64_t)qi * n_heads + (m < n_heads ? m : n_heads - 1)];
+        wr[mt][r] = m < n_heads ? x : 0.0f;
       }
     }
-    // Physical block of every tile of this wavefront, looked up once (a 32-key
-    // tile never straddles a block).
-    int64_t blk[TPW];
-    int bslot[TPW];
-#pragma unroll
-    for (int it = 0; it < TPW; ++it) {
-      int tile = tile_begin + it;
-      tile = tile < ntile ? tile : ntile - 1;
-      const int t0 = tile * 32;
-      const int bi = t0 / keys.block_size;
-      blk[it] = keys.table ? (int64_t)keys.table[(int64_t)seq * keys.max_blocks + bi] : (int64_t)seq;
-      bslot[it] = t0 - bi * keys.block_size;
-    }
-
-    // Loads are coalesced: 16-byte piece j*64 + lane of the tile's rows (1 KB per
-    // wavefront instruction), i.e. key kk = (1024 j + 16 lane) / ROWB, chunk ch.
-    // They go through a wavefront-private LDS tile (chunk slots XOR-swizzled by
-    // the key index against bank conflicts) into the MFMA operand layout.  Keys
-    // are read once per call: non-temporal loads.
-    struct Raw {
-      u32x4 v[NLD];
-      float sc;
-    };
-    auto issue = [&](int it, Raw &r) {
-      int tile = tile_begin + it;
-      tile = tile < ntile ? tile : ntile - 1;
-      const int last = n - 1 - tile * 32;    // clamp rows beyond the visible tokens
-#pragma unroll
-      for (int j = 0; j < NLD; ++j) {
-        const int byte = 1024 * j + 16 * lane;
-        const int kk = byte / ROWB, ch = (byte % ROWB) / 16;
-        const int kc = kk < last ? kk : last;
-        r.v[j] = load16_nt(cache_row(keys, blk[it], bslot[it] + kc) + 16 * ch);
-      }
-      if (FP8) {
-        const int kc = col < last ? col : last;
-        r.sc = keys.scale[blk[it] * keys.scale_block_stride + bslot[it] + kc];
-      }
-    };
-    Raw buf[P];
-#pragma unroll
-    for (int p = 0; p < P; ++p) issue(p, buf[p]);
 #pragma unroll
     for (int it = 0; it < TPW; ++it) {
       Raw &cur = buf[it % P];
@@ -146,8 +179,7 @@ __global__ __launch_bounds__(256) void scores_mfma_kernel(float *__restrict__ sc
       __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 #pragma unroll
       for (int j = 0; j < NLD; ++j) {
-        const int byte = 1024 * j + 16 * lane;
-        const int kk = byte / ROWB, ch = (byte % ROWB) / 16;
+        const int kk = (64 * j + lane) / CPR, ch = lane % CPR;
         *reinterpret_cast<u32x4 *>(stage + kk * ROWB + 16 * (ch ^ (kk & (CPR - 1)))) = cur.v[j];
       }
       const float sc = FP8 ? cur.sc : 1.0f;
@@ -167,10 +199,10 @@ __global__ __launch_bounds__(256) void scores_mfma_kernel(float *__restrict__ sc
           b[j] = as_bf16x8(x);
         }
       }
-      // Epilogue.  fp8: ReLU(acc * sc) * w summed over heads equals
-      // sc * sum w * (acc clamped to the side of 0 that the sign of sc keeps),
-      // with one multiply per key instead of one per head.
-      const int lim = sc >= 0.0f ? 0x7FFFFFFF : (int)0x80000000;
+      // Epilogue.  fp8: sum_h w_h ReLU(acc_h * sc) = |sc| * sum_h w_h ReLU(acc_h * sign(sc)),
+      // the sign applied by flipping the accumulator's sign bit: one multiply per
+      // key instead of one per head, and the same summation order for every key.
+      const uint32_t flip = FP8 ? (__float_as_uint(sc) & 0x80000000u) : 0u;
       float s = 0.0f;
 #pragma unroll
       for (int mt = 0; mt < MT; ++mt) {
@@ -178,14 +210,15 @@ __global__ __launch_bounds__(256) void scores_mfma_kernel(float *__restrict__ sc
 #pragma unroll
         for (int ks = 0; ks < KS; ++ks) acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[mt][ks], b[ks], acc, 0, 0, 0);
 #pragma unroll
-        for (int r = 0; r < 16; ++r) s = fmaf(wr[mt][r], FP8 ? relu_side(acc[r], lim) : relu(acc[r]), s);
+        for (int r = 0; r < 16; ++r) s = fmaf(wr[mt][r], relu(__uint_as_float(__float_as_uint(acc[r]) ^ flip)), s);
       }
-      if (FP8) s *= sc;
+      if (FP8) s *= fabsf(sc);
       s = halves_sum(s);
       const int t = (tile_begin + it) * 32 + col;
-      const bool ok = half == 0 && t < n;
-      if (ok) scores[(int64_t)qi * ld + t] = s;
-      lane_max = max(lane_max, ok ? order_key(s) : 0u);
+      if (half == 0 && t < n) scores[(int64_t)qi * ld + t] = s;
+      // only wavefronts whose keys are all visible report a bound, so every
+      // score reaches the maximum unmasked
+      lane_best = fmaxf(lane_best, s);
     }
   }
 
@@ -201,7 +234,7 @@ __global__ __launch_bounds__(256) void scores_mfma_kernel(float *__restrict__ sc
     if ((wid + 1) * per_wave <= n && rank >= 1) {
       // rank-th largest of the 32 lane maxima (lanes 32..63 hold 0): extract
       // the maximum rank times
-      uint32_t v = half == 0 ? lane_max : 0u;
+      uint32_t v = half == 0 ? order_key(lane_best) : 0u;
       for (int i = 0; i < rank; ++i) {
         T = wave_max_u32(v);
         const uint64_t hit = __ballot(v == T);
