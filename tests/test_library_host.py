@@ -73,6 +73,7 @@ def test_index_scores_validation(lib):
     assert _scores(lib, _cache(dtype=2, row_stride=128, block_stride=128 * 1024)) == 1   # fp8 without scales
     assert _scores(lib, _cache(row_stride=200, block_stride=200 * 1024)) == 1           # row_stride < width bytes
     assert _scores(lib, _cache(rows=8)) == 2                          # misaligned rows
+    assert _scores(lib, _cache(row_stride=(1 << 24) + 16, block_stride=((1 << 24) + 16) * 1024)) == 2  # > 16 MiB rows
     assert _scores(lib, _cache(table=16, max_blocks=4, block_size=48, block_stride=256 * 48)) == 2  # block % 32
     assert _scores(lib, _cache(), q_dtype=7) == 1
 
