@@ -294,52 +294,50 @@ __global__ __launch_bounds__(kAttThreads) void attend_bf16_kernel(AttArgs a) {
   }
 }
 
-// Combine split partials in split order.  One workgroup per (query, head): one
-// wavefront turns the splits' (max, sum) into weights, then every thread sums
-// its 4 columns over the splits with all loads in flight.
+// Combine split partials in split order.  One workgroup per (query, head), one
+// thread per 4 output columns.  Every thread issues all of its loads at once
+// (the splits' (max, sum) pairs and its 4 columns of every split; padding
+// splits reload the last one and get weight 0), then forms the weights and the
+// weighted sum in split order.
+template <int NS>   // splits, rounded up to a multiple of 8
 __global__ __launch_bounds__(128) void merge_kernel(float *__restrict__ out, float *__restrict__ lse,
                                                     const float *__restrict__ part_o,
-                                                    const float *__restrict__ part_ml, int splits, int H, int L) {
-  __shared__ float wgt[kMaxSplits];
-  __shared__ float tot[2];
+                                                    const float *__restrict__ part_ml, int splits, int H) {
   const int qh = blockIdx.x;
   const int qi = qh / H, h = qh - qi * H;
-  const int tid = threadIdx.x;
-  if (tid < 64) {
-    const bool ok = tid < splits;
-    const int64_t b = (((int64_t)qi * splits + (ok ? tid : 0)) * H + h) * 2;
-    const float m = ok ? part_ml[b] : -INFINITY;
-    const float l = ok ? part_ml[b + 1] : 0.0f;
-    float M = m;
-    for (int off = 32; off > 0; off >>= 1) M = fmaxf(M, __shfl_xor(M, off, 64));
-    const float w = (ok && M != -INFINITY) ? exp2f(m - M) : 0.0f;
-    float Ls = w * l;
-    for (int off = 32; off > 0; off >>= 1) Ls += __shfl_xor(Ls, off, 64);
-    if (ok) wgt[tid] = Ls > 0.0f ? w / Ls : 0.0f;
-    if (tid == 0) {
-      tot[0] = M;
-      tot[1] = Ls;
-    }
-  }
-  __syncthreads();
-  for (int c = tid * 4; c < L; c += 128 * 4) {
-    f32x4 v[kMaxSplits];
+  const int c = threadIdx.x * 4;
+  f32x4 v[NS];
+  float m[NS], l[NS];
 #pragma unroll
-    for (int sp = 0; sp < kMaxSplits; ++sp)
-      if (sp < splits) v[sp] = *reinterpret_cast<const f32x4 *>(part_o + (((int64_t)qi * splits + sp) * H + h) * L + c);
-    f32x4 acc = {0, 0, 0, 0};
-#pragma unroll
-    for (int sp = 0; sp < kMaxSplits; ++sp)
-      if (sp < splits) {
-        const float w = wgt[sp];
-        acc[0] = fmaf(w, v[sp][0], acc[0]);
-        acc[1] = fmaf(w, v[sp][1], acc[1]);
-        acc[2] = fmaf(w, v[sp][2], acc[2]);
-        acc[3] = fmaf(w, v[sp][3], acc[3]);
-      }
-    *reinterpret_cast<f32x4 *>(out + (int64_t)qh * L + c) = acc;
+  for (int sp = 0; sp < NS; ++sp) {
+    const int s = sp < splits ? sp : splits - 1;
+    const int64_t b = ((int64_t)qi * splits + s) * H + h;
+    v[sp] = *reinterpret_cast<const f32x4 *>(part_o + b * kL + c);
+    const auto x = *reinterpret_cast<const float2 *>(part_ml + b * 2);
+    m[sp] = x.x;
+    l[sp] = x.y;
   }
-  if (tid == 0 && lse) lse[qh] = tot[1] > 0.0f ? (tot[0] + log2f(tot[1])) * kLn2 : -INFINITY;
+  float M = -INFINITY;
+#pragma unroll
+  for (int sp = 0; sp < NS; ++sp) M = sp < splits ? fmaxf(M, m[sp]) : M;
+  float w[NS], Ls = 0.0f;
+#pragma unroll
+  for (int sp = 0; sp < NS; ++sp) {
+    w[sp] = (sp < splits && M != -INFINITY) ? exp2f(m[sp] - M) : 0.0f;
+    Ls = fmaf(w[sp], l[sp], Ls);
+  }
+  const float inv = Ls > 0.0f ? 1.0f / Ls : 0.0f;
+  f32x4 acc = {0, 0, 0, 0};
+#pragma unroll
+  for (int sp = 0; sp < NS; ++sp) {
+    const float ws = w[sp] * inv;
+    acc[0] = fmaf(ws, v[sp][0], acc[0]);
+    acc[1] = fmaf(ws, v[sp][1], acc[1]);
+    acc[2] = fmaf(ws, v[sp][2], acc[2]);
+    acc[3] = fmaf(ws, v[sp][3], acc[3]);
+  }
+  *reinterpret_cast<f32x4 *>(out + (int64_t)qh * kL + c) = acc;
+  if (threadIdx.x == 0 && lse) lse[qh] = Ls > 0.0f ? (M + log2f(Ls)) * kLn2 : -INFINITY;
 }
 
 // ------------------------------------------------------------------- f32 path
@@ -486,8 +484,14 @@ hipError_t launch_attend(float *out, float *lse, const void *q, int dt, const Ca
     hipLaunchKernelGGL(attend_bf16_kernel<true>, grid, dim3(kAttThreads), 0, stream, a);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(merge_kernel, dim3(n_q * n_heads), dim3(128), 0, stream, out, lse, a.part_o, a.part_ml,
-                       plan.splits, n_heads, kv_lora);
+#define DSA_MERGE(NS)                                                                                         \
+  hipLaunchKernelGGL(merge_kernel<NS>, dim3(n_q * n_heads), dim3(kL / 4), 0, stream, out, lse, a.part_o, a.part_ml, \
+                     plan.splits, n_heads)
+    if (plan.splits <= 8) DSA_MERGE(8);
+    else if (plan.splits <= 16) DSA_MERGE(16);
+    else if (plan.splits <= 24) DSA_MERGE(24);
+    else DSA_MERGE(32);
+#undef DSA_MERGE
   } else {
     hipLaunchKernelGGL(attend_bf16_kernel<false>, grid, dim3(kAttThreads), 0, stream, a);
   }
