@@ -248,13 +248,14 @@ def main():
         dpp = device.upload(pp)
         print(f"[bench] generated and uploaded {wp.name} in {time.time() - t0:.1f}s", file=sys.stderr, flush=True)
         ps = torch.empty(pp.n_q, pp.max_len, device="cuda")
-        for _ in range(2):
+        # ~30 ms of warm-up: the shader clock settles under sustained MFMA load
+        for _ in range(30):
             dsa.dsa_index_scores(ps, dpp.q_idx, pp.q_idx_dtype, dpp.w_idx, dpp.keys, dpp.q_len, pp.idx_heads,
                                  pp.max_len)
         torch.cuda.synchronize()
         e0 = torch.cuda.Event(enable_timing=True)
         e1 = torch.cuda.Event(enable_timing=True)
-        reps = 5
+        reps = 20
         e0.record()
         for _ in range(reps):
             dsa.dsa_index_scores(ps, dpp.q_idx, pp.q_idx_dtype, dpp.w_idx, dpp.keys, dpp.q_len, pp.idx_heads,

@@ -247,14 +247,17 @@ __global__ __launch_bounds__(256) void scores_mfma_kernel(float *__restrict__ sc
 
 // Many queries (chunked prefill), bf16 q and keys, 128-wide keys, up to 32
 // heads: a GEMM over (query, head) rows and key columns with K = 128.  A
-// workgroup owns kPQ consecutive queries and one range of keys; 64-key steps
+// workgroup owns kPQ consecutive queries and one range of keys; 128-key steps
 // are staged in LDS once and shared by its 8 wavefronts, each scoring 2
-// queries x 2 key tiles per step (8 MFMAs 32x32x16 per query and tile), so a
-// wavefront reads a key tile from LDS once for both of its queries.  Key steps
-// are loaded two steps ahead through a 3-slot LDS ring.  Queries of a block
-// that belong to different sequences are processed one sequence at a time.
+// queries x 4 key tiles per step (8 MFMAs 32x32x16 per query and tile), so a
+// wavefront reads a key tile from LDS once for both of its queries, one tile
+// ahead of its MFMAs.  The next step's keys are loaded into registers while
+// a step is scored and written to the other slot of a 2-slot LDS ring: one
+// barrier per step.  Queries of a block that belong to different sequences are
+// processed one sequence at a time.
 constexpr int kPQ = 16;            // queries per workgroup
-constexpr int kPStepKeys = 64;     // keys per step (two 32-key tiles)
+constexpr int kPStepKeys = 128;    // keys per step (four 32-key tiles)
+constexpr int kPTiles = kPStepKeys / 32;
 constexpr int kPThreads = 512;
 constexpr int kPRowB = 256;        // bf16 key row bytes (128 dims)
 constexpr int kPLdsRow = kPRowB + 16;   // padded LDS row: conflict-free 16-byte operand reads
@@ -266,7 +269,7 @@ __global__ __launch_bounds__(kPThreads) void scores_prefill_kernel(float *__rest
                                                                    const int32_t *__restrict__ q_len, int n_q,
                                                                    int n_heads, int keys_per_split) {
   constexpr int D = 128, KS = D / 16, HALF = D / 2, CPR = kPRowB / 16;   // 16 chunks per row
-  __shared__ __align__(16) uint8_t ring[3][kPStepKeys * kPLdsRow];          // 3 x 17 KB
+  __shared__ __align__(16) uint8_t ring[2][kPStepKeys * kPLdsRow];          // 2 x 34 KB
   __shared__ int32_t sseq[kPQ], slen[kPQ];
   __shared__ int32_t groups[kPQ + 1];
 
@@ -335,99 +338,100 @@ __global__ __launch_bounds__(kPThreads) void scores_prefill_kernel(float *__rest
     if (k0 >= k1) continue;   // uniform over the workgroup
     const int nsteps = (k1 - k0 + kPStepKeys - 1) / kPStepKeys;
 
-    // key step loads: thread t takes 16-byte chunk ch = t % 16 of rows
-    // t / 16 and t / 16 + 32 of the step; rows past k1 are clamped to k1 - 1.
-    // A step starts on a multiple of 64 tokens, so with blocks of a multiple of
-    // 64 tokens (or a contiguous cache) it lies in one block: one lookup per
-    // step, and the per-thread part of the address is fixed.
-    const bool one_block = keys.block_size % kPStepKeys == 0;
+    // key step loads: thread t takes 16-byte chunk lch = t % 16 of rows
+    // lrow + 32 x (x < 4) of the step, lrow = t / 16; rows past k1 are clamped
+    // to k1 - 1.  Steps start on multiples of 32 tokens and blocks hold a
+    // multiple of 32, so each 32-row group lies in one block: one uniform
+    // lookup per group, no branch.
     const int lrow = tid / CPR, lch = tid % CPR;
-    const int64_t toff[2] = {(int64_t)lrow * keys.row_stride + 16 * lch,
-                             (int64_t)(lrow + 32) * keys.row_stride + 16 * lch};
-    auto load_step = [&](int st, u32x4 (&r)[2]) {
+    auto load_step = [&](int st, u32x4 (&r)[kPTiles]) {
       const int sc = st < nsteps ? st : nsteps - 1;
       const int t0 = k0 + sc * kPStepKeys;
-      if (one_block && t0 + kPStepKeys <= k1) {
+#pragma unroll
+      for (int x = 0; x < kPTiles; ++x) {
+        const int g0 = t0 + 32 * x;
+        const int gl = g0 < k1 ? g0 : ((k1 - 1) & ~31);   // the group's first row (in range)
         int slot0;
-        const int64_t blk0 = cache_block(keys, seq, t0, slot0);
-        const uint8_t *base = cache_row(keys, blk0, slot0);
-#pragma unroll
-        for (int x = 0; x < 2; ++x) r[x] = load16_nt(base + toff[x]);
-      } else {
-#pragma unroll
-        for (int x = 0; x < 2; ++x) {
-          const int row = lrow + 32 * x;
-          const int t = t0 + row < k1 ? t0 + row : k1 - 1;
-          int slot;
-          const int64_t blk = cache_block(keys, seq, t, slot);
-          r[x] = load16_nt(cache_row(keys, blk, slot) + 16 * lch);
-        }
+        const int64_t blk = cache_block(keys, seq, gl, slot0);
+        const int t = g0 + lrow < k1 ? g0 + lrow : k1 - 1;
+        r[x] = load16_nt(cache_row(keys, blk, slot0 + (t - gl)) + 16 * lch);
       }
     };
-    auto store_step = [&](int st, const u32x4 (&r)[2]) {
-      uint8_t *buf = ring[st % 3] + lrow * kPLdsRow + 16 * lch;
-      *reinterpret_cast<u32x4 *>(buf) = r[0];
-      *reinterpret_cast<u32x4 *>(buf + 32 * kPLdsRow) = r[1];
+    auto store_step = [&](int st, const u32x4 (&r)[kPTiles]) {
+      uint8_t *buf = ring[st & 1] + lrow * kPLdsRow + 16 * lch;
+#pragma unroll
+      for (int x = 0; x < kPTiles; ++x) *reinterpret_cast<u32x4 *>(buf + 32 * x * kPLdsRow) = r[x];
     };
     // key operand of tile tl: lane (col, half) reads 128 contiguous bytes of row
     // 32 tl + col from byte 128 half (the padded rows keep 16 lanes on distinct banks)
     const int bofs = col * kPLdsRow + 128 * half;
-    // full[u]: every key of the step is visible to query u (wave-uniform)
-    bool full[2];
-    auto epilogue = [&](const f32x16 &acc, int u, int key) {
+    auto read_b = [&](int st, int tl, bf16x8 (&b)[KS]) {
+      const uint8_t *rp = ring[st & 1] + tl * 32 * kPLdsRow + bofs;
+#pragma unroll
+      for (int j = 0; j < KS; ++j) b[j] = as_bf16x8(*reinterpret_cast<const u32x4 *>(rp + 16 * j));
+    };
+    // Epilogue of one (query u, key tile) combination: ReLU, head weights, head
+    // sum.  fu: every key of the tile is visible to query u (wave-uniform), so
+    // both lane halves (which hold the same sum) store unmasked.
+    auto epilogue = [&](const f32x16 &acc, int u, int key, bool fu) {
       float s = 0.0f;
 #pragma unroll
       for (int r = 0; r < 16; ++r) s = fmaf(wr[u][r], relu(acc[r]), s);
       s = halves_sum(s);
-      if (full[u]) {
-        orow[u][key] = s;   // both lane halves hold the same sum: one unmasked store
+      if (fu) {
+        orow[u][key] = s;
       } else if (half == 0 && qs[u] == seq && key < qn[u] && key < k1) {
         orow[u][key] = s;
       }
     };
-    // Per step: 4 (tile, query) combinations; the MFMAs of one overlap the
-    // epilogue (ReLU, head weights, head sum) of the previous one.
+    // Per step: 8 (tile, query) combinations; the MFMAs of one overlap the
+    // epilogue of the one before it, across steps too: the last combination's
+    // epilogue is deferred past the barrier into the next step's first MFMAs.
+    f32x16 acc[2];   // query u accumulates in acc[u]
+    bool pend = false, pend_full = false;
+    int pend_key = 0;
     auto compute_step = [&](int st) {
-      const uint8_t *buf = ring[st % 3];
       const int kb = k0 + st * kPStepKeys;
-#pragma unroll
-      for (int u = 0; u < 2; ++u) full[u] = qs[u] == seq && kb + kPStepKeys <= qn[u] && kb + kPStepKeys <= k1;
       bf16x8 b[2][KS];
+      read_b(st, 0, b[0]);
 #pragma unroll
-      for (int tl = 0; tl < 2; ++tl) {
-        const uint8_t *rp = buf + tl * 32 * kPLdsRow + bofs;
+      for (int tl = 0; tl < kPTiles; ++tl) {
+        if (tl + 1 < kPTiles) read_b(st, tl + 1, b[(tl + 1) & 1]);
+        const int key0 = kb + 32 * tl;
+        bool full[2];
 #pragma unroll
-        for (int j = 0; j < KS; ++j) b[tl][j] = as_bf16x8(*reinterpret_cast<const u32x4 *>(rp + 16 * j));
-      }
-      f32x16 acc[2];   // combination c accumulates in acc[c & 1]
+        for (int u = 0; u < 2; ++u) full[u] = qs[u] == seq && key0 + 32 <= qn[u] && key0 + 32 <= k1;
 #pragma unroll
-      for (int c = 0; c <= 4; ++c) {
-        if (c < 4) {
-          const int tl = c >> 1, u = c & 1;
-          acc[c & 1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[u][0], b[tl][0], f32x16{}, 0, 0, 0);
+        for (int u = 0; u < 2; ++u) {
+          acc[u] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[u][0], b[tl & 1][0], f32x16{}, 0, 0, 0);
 #pragma unroll
           for (int ks = 1; ks < KS; ++ks)
-            acc[c & 1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[u][ks], b[tl][ks], acc[c & 1], 0, 0, 0);
+            acc[u] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[u][ks], b[tl & 1][ks], acc[u], 0, 0, 0);
+          // the previous combination: (tile tl - 1, query 1) or (tile tl, query 0)
+          if (u == 0) {
+            if (pend) epilogue(acc[1], 1, pend_key, pend_full);
+          } else {
+            epilogue(acc[0], 0, key0 + col, full[0]);
+          }
         }
-        if (c > 0) epilogue(acc[(c - 1) & 1], (c - 1) & 1, kb + ((c - 1) >> 1) * 32 + col);
+        pend = true;
+        pend_key = key0 + col;
+        pend_full = full[1];
       }
     };
 
-    u32x4 ra[2], rb[2];
-    load_step(0, ra);
-    load_step(1, rb);
-    store_step(0, ra);
+    u32x4 rn[kPTiles];
+    load_step(0, rn);
+    store_step(0, rn);
     __syncthreads();
-    for (int st = 0; st < nsteps; st += 2) {
-      load_step(st + 2, ra);
+    for (int st = 0; st < nsteps; ++st) {
+      load_step(st + 1, rn);
       compute_step(st);
-      store_step(st + 1, rb);
-      __syncthreads();
-      load_step(st + 3, rb);
-      if (st + 1 < nsteps) compute_step(st + 1);
-      store_step(st + 2, ra);
+      store_step(st + 1, rn);
       __syncthreads();
     }
+    if (pend) epilogue(acc[1], 1, pend_key, pend_full);
+    pend = false;
   }
 }
 
