@@ -257,7 +257,7 @@ __global__ __launch_bounds__(256) void scores_mfma_kernel(float *__restrict__ sc
 // processed one sequence at a time.
 constexpr int kPQ = 16;            // queries per workgroup
 constexpr int kPStepKeys = 128;    // keys per step (four 32-key tiles)
-constexpr int kPTiles = kPStepKeys / 32;
+constexpr int kPTiles = kPStepKeys / 32;   // 4 (the block lookups below name four)
 constexpr int kPThreads = 512;
 constexpr int kPRowB = 256;        // bf16 key row bytes (128 dims)
 constexpr int kPLdsRow = kPRowB + 16;   // padded LDS row: conflict-free 16-byte operand reads
@@ -347,14 +347,33 @@ __global__ __launch_bounds__(kPThreads) void scores_prefill_kernel(float *__rest
     auto load_step = [&](int st, u32x4 (&r)[kPTiles]) {
       const int sc = st < nsteps ? st : nsteps - 1;
       const int t0 = k0 + sc * kPStepKeys;
+      int gl[kPTiles], bi[kPTiles], blk[kPTiles];
 #pragma unroll
       for (int x = 0; x < kPTiles; ++x) {
         const int g0 = t0 + 32 * x;
-        const int gl = g0 < k1 ? g0 : ((k1 - 1) & ~31);   // the group's first row (in range)
-        int slot0;
-        const int64_t blk = cache_block(keys, seq, gl, slot0);
+        gl[x] = g0 < k1 ? g0 : ((k1 - 1) & ~31);   // the group's first row (in range)
+        bi[x] = gl[x] / keys.block_size;
+      }
+      // all lookups in flight together, then all key loads (no branch between
+      // a load and the next)
+      if (keys.table) {
+        // the block table is read-only here: read it through the constant
+        // address space, so the uniform lookups are scalar loads
+        const auto trow = reinterpret_cast<const __attribute__((address_space(4))) int32_t *>(
+            reinterpret_cast<uintptr_t>(keys.table + (int64_t)seq * keys.max_blocks));
+#pragma unroll
+        for (int x = 0; x < kPTiles; ++x) blk[x] = trow[bi[x]];
+        asm("" : "+s"(blk[0]), "+s"(blk[1]), "+s"(blk[2]), "+s"(blk[3]));   // all four before any use
+      } else {
+#pragma unroll
+        for (int x = 0; x < kPTiles; ++x) blk[x] = seq;
+      }
+#pragma unroll
+      for (int x = 0; x < kPTiles; ++x) {
+        const int g0 = t0 + 32 * x;
         const int t = g0 + lrow < k1 ? g0 + lrow : k1 - 1;
-        r[x] = load16_nt(cache_row(keys, blk, slot0 + (t - gl)) + 16 * lch);
+        const int slot = t - bi[x] * keys.block_size;
+        r[x] = load16_nt(cache_row(keys, (int64_t)blk[x], slot) + 16 * lch);
       }
     };
     auto store_step = [&](int st, const u32x4 (&r)[kPTiles]) {
@@ -371,23 +390,24 @@ __global__ __launch_bounds__(kPThreads) void scores_prefill_kernel(float *__rest
       for (int j = 0; j < KS; ++j) b[j] = as_bf16x8(*reinterpret_cast<const u32x4 *>(rp + 16 * j));
     };
     // Epilogue of one (query u, key tile) combination: ReLU, head weights, head
-    // sum.  fu: every key of the tile is visible to query u (wave-uniform), so
-    // both lane halves (which hold the same sum) store unmasked.
-    auto epilogue = [&](const f32x16 &acc, int u, int key, bool fu) {
+    // sum.  The store is predicated once: every key of the tile visible to
+    // query u (both lane halves hold the same sum and store it), or this
+    // lane's key visible (lower half).
+    auto head_sum = [&](const f32x16 &acc, int u) {
       float s = 0.0f;
 #pragma unroll
       for (int r = 0; r < 16; ++r) s = fmaf(wr[u][r], relu(acc[r]), s);
-      s = halves_sum(s);
-      if (fu) {
-        orow[u][key] = s;
-      } else if (half == 0 && qs[u] == seq && key < qn[u] && key < k1) {
-        orow[u][key] = s;
-      }
+      return halves_sum(s);
     };
-    // Per step: 8 (tile, query) combinations; the MFMAs of one overlap the
-    // epilogue of the one before it, across steps too: the last combination's
-    // epilogue is deferred past the barrier into the next step's first MFMAs.
-    f32x16 acc[2];   // query u accumulates in acc[u]
+    auto store_score = [&](float s, int u, int key, bool fu, bool live) {
+      const bool ok = live && (fu || (half == 0 && qs[u] == seq && key < qn[u] && key < k1));
+      if (ok) orow[u][key] = s;
+    };
+    // Per step: 8 (tile, query) combinations.  The 8 MFMAs of one combination
+    // are interleaved (scheduling groups of 1 MFMA + 5 VALU) with the epilogue
+    // of the one before it, across steps too: the last combination's epilogue
+    // runs past the barrier, under the next step's first MFMAs.
+    f32x16 acc[2] = {f32x16{}, f32x16{}};   // query u accumulates in acc[u]
     bool pend = false, pend_full = false;
     int pend_key = 0;
     auto compute_step = [&](int st) {
@@ -407,12 +427,15 @@ __global__ __launch_bounds__(kPThreads) void scores_prefill_kernel(float *__rest
 #pragma unroll
           for (int ks = 1; ks < KS; ++ks)
             acc[u] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[u][ks], b[tl & 1][ks], acc[u], 0, 0, 0);
-          // the previous combination: (tile tl - 1, query 1) or (tile tl, query 0)
-          if (u == 0) {
-            if (pend) epilogue(acc[1], 1, pend_key, pend_full);
-          } else {
-            epilogue(acc[0], 0, key0 + col, full[0]);
+          // the previous combination (query u ^ 1): (tile tl - 1, query 1) or (tile tl, query 0)
+          const float sp = head_sum(acc[u ^ 1], u ^ 1);
+#pragma unroll
+          for (int i = 0; i < KS; ++i) {
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // 1 MFMA
+            __builtin_amdgcn_sched_group_barrier(0x002, 5, 0);   // 5 VALU
           }
+          if (u == 0) store_score(sp, 1, pend_key, pend_full, pend);
+          else store_score(sp, 0, key0 + col, full[0], true);
         }
         pend = true;
         pend_key = key0 + col;
@@ -430,7 +453,7 @@ __global__ __launch_bounds__(kPThreads) void scores_prefill_kernel(float *__rest
       store_step(st + 1, rn);
       __syncthreads();
     }
-    if (pend) epilogue(acc[1], 1, pend_key, pend_full);
+    store_score(head_sum(acc[1], 1), 1, pend_key, pend_full, pend);
     pend = false;
   }
 }
