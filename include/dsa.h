@@ -170,6 +170,37 @@ dsa_status dsa_decode_step(float *out, float *lse, const void *q_idx, dsa_dtype 
 size_t dsa_decode_step_workspace_size(int32_t batch, int32_t max_len, int32_t k, int32_t mla_heads,
                                       int32_t kv_lora);
 
+/*
+ * One fused DSA decode step over a multi-token window ("GLM 5.3 Flash
+ * (strata-poly)", section "How it uses the card", "Guessing ahead", and the
+ * --window option: the known token and up to three guesses go through the
+ * model together).  Sequence b holds seq_len[b] tokens, the last `window` of
+ * them the window's tokens: query j (0 <= j < window) of sequence b is the
+ * token at 0-based position seq_len[b] - window + j and sees the
+ * seq_len[b] - window + j + 1 tokens up to and including itself (0 when that is
+ * not positive: the query sees nothing, keeps no index, out = 0, lse = -inf).
+ * Each query's result is that of a single-token step whose sequence ends at its
+ * position: the same scores and indices; attention within the tolerance of
+ * the split order.
+ *   queries are row i = b * window + j of
+ *   q_idx [batch * window][idx_heads][keys->width], w_idx [batch * window][idx_heads],
+ *   q_mla [batch * window][mla_heads][latent->width],
+ *   out [batch * window][mla_heads][kv_lora], lse [batch * window][mla_heads] (nullable),
+ *   scores_out [batch * window][max_len], indices_out [batch * window][k] (optional).
+ * max_len >= max_b seq_len[b].  1 <= window <= 64 (DSA_ERR_UNSUPPORTED above),
+ * batch * window <= 2^24.  window = 1 is dsa_decode_step.  Other arguments,
+ * errors and the workspace contract as for dsa_decode_step, with the size from
+ * dsa_decode_window_workspace_size (0 for invalid arguments).
+ */
+dsa_status dsa_decode_window(float *out, float *lse, const void *q_idx, dsa_dtype q_idx_dtype, const float *w_idx,
+                             const dsa_cache *keys, int32_t idx_heads, const void *q_mla, dsa_dtype q_mla_dtype,
+                             const dsa_cache *latent, int32_t kv_lora, int32_t mla_heads, const int32_t *seq_len,
+                             int32_t batch, int32_t window, int32_t max_len, int32_t k, float softmax_scale,
+                             float *scores_out, int32_t *indices_out, void *workspace, size_t workspace_bytes,
+                             void *stream);
+size_t dsa_decode_window_workspace_size(int32_t batch, int32_t window, int32_t max_len, int32_t k,
+                                        int32_t mla_heads, int32_t kv_lora);
+
 /* Zero-fill a workspace on `stream` with a fill kernel (no hipMemset node, so it
  * may be captured in a graph).  bytes must be a multiple of 4. */
 dsa_status dsa_workspace_clear(void *workspace, size_t bytes, void *stream);

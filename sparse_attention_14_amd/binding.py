@@ -46,6 +46,7 @@ class DsaCache(ctypes.Structure):
 _lib = None
 EXPORTS = ("dsa_index_scores", "dsa_topk", "dsa_topk_workspace_size", "mla_sparse_attend",
            "mla_sparse_attend_workspace_size", "dsa_decode_step", "dsa_decode_step_workspace_size",
+           "dsa_decode_window", "dsa_decode_window_workspace_size",
            "dsa_workspace_clear", "dsa_status_string")
 
 
@@ -69,6 +70,9 @@ def load(path: str = LIB_PATH):
         "dsa_decode_step": (ctypes.c_int, [P, P, P, ctypes.c_int, P, CP, i32, P, ctypes.c_int, CP, i32, i32, P, i32,
                                            i32, i32, f32, P, P, P, sz, P]),
         "dsa_decode_step_workspace_size": (sz, [i32, i32, i32, i32, i32]),
+        "dsa_decode_window": (ctypes.c_int, [P, P, P, ctypes.c_int, P, CP, i32, P, ctypes.c_int, CP, i32, i32, P,
+                                             i32, i32, i32, i32, f32, P, P, P, sz, P]),
+        "dsa_decode_window_workspace_size": (sz, [i32, i32, i32, i32, i32, i32]),
         "dsa_workspace_clear": (ctypes.c_int, [P, sz, P]),
         "dsa_status_string": (ctypes.c_char_p, [ctypes.c_int]),
     }
@@ -161,6 +165,23 @@ def dsa_decode_step(out, lse, q_idx, q_idx_dtype, w_idx, keys: DeviceCache, q_ml
         _p(q_mla), DTYPES[q_mla_dtype], ctypes.byref(latent.desc), kv_lora, q_mla.shape[1], _p(seq_len),
         seq_len.shape[0], max_len, k, float(softmax_scale), _p(scores_out), _p(indices_out), _p(workspace),
         ws_bytes, _stream(stream)))
+
+
+def dsa_decode_window_workspace_size(batch, window, max_len, k, mla_heads, kv_lora) -> int:
+    return int(load().dsa_decode_window_workspace_size(batch, window, max_len, k, mla_heads, kv_lora))
+
+
+def dsa_decode_window(out, lse, q_idx, q_idx_dtype, w_idx, keys: DeviceCache, q_mla, q_mla_dtype,
+                      latent: DeviceCache, kv_lora, seq_len, window, max_len, k, softmax_scale, workspace,
+                      scores_out=None, indices_out=None, stream=None):
+    """Queries are rows b * window + j of q_idx / w_idx / q_mla (see include/dsa.h)."""
+    lib = load()
+    ws_bytes = workspace.numel() * workspace.element_size()
+    _check("dsa_decode_window", lib.dsa_decode_window(
+        _p(out), _p(lse), _p(q_idx), DTYPES[q_idx_dtype], _p(w_idx), ctypes.byref(keys.desc), q_idx.shape[1],
+        _p(q_mla), DTYPES[q_mla_dtype], ctypes.byref(latent.desc), kv_lora, q_mla.shape[1], _p(seq_len),
+        seq_len.shape[0], window, max_len, k, float(softmax_scale), _p(scores_out), _p(indices_out),
+        _p(workspace), ws_bytes, _stream(stream)))
 
 
 def dsa_workspace_clear(workspace, stream=None):

@@ -10,6 +10,7 @@ namespace {
 
 constexpr int kMaxTopk = 2048;
 constexpr int kMaxLenTopk = 262144;
+constexpr int kMaxWindow = 64;    // queries per sequence in one decode window
 
 int elem_bytes(dsa_dtype d) { return d == DSA_F32 ? 4 : (d == DSA_BF16 ? 2 : 1); }
 
@@ -95,13 +96,15 @@ size_t round256(size_t b) { return (b + 255) / 256 * 256; }
 struct StepLayout {
   int64_t ld;
   int n_bounds;
-  size_t off_scores, off_idx, off_bounds, off_topk, off_att, total;
+  size_t off_scores, off_idx, off_bounds, off_topk, off_att, off_rows, total;
   TopkPlan tp;
   AttendPlan ap;
 };
 
+// batch = queries of the step (sequences x window); window > 1 adds the rows'
+// (sequence, visible count) arrays.
 StepLayout step_layout(int32_t batch, int32_t max_len, int32_t k, int32_t mla_heads, int32_t kv_lora,
-                       int latent_dt, int width) {
+                       int latent_dt, int width, int32_t window = 1) {
   StepLayout L{};
   L.ld = ((int64_t)max_len + 63) / 64 * 64;
   L.tp = plan_topk(batch, k, max_len);
@@ -118,6 +121,8 @@ StepLayout step_layout(int32_t batch, int32_t max_len, int32_t k, int32_t mla_he
   off += round256(L.tp.total);
   L.off_att = off;
   off += round256(L.ap.total);
+  L.off_rows = off;
+  if (window > 1) off += 2 * round256((size_t)batch * 4);
   L.total = off;
   return L;
 }
@@ -203,22 +208,40 @@ size_t dsa_decode_step_workspace_size(int32_t batch, int32_t max_len, int32_t k,
   return step_layout(batch, max_len, k, mla_heads, kv_lora, kBF16, 576).total;
 }
 
-dsa_status dsa_decode_step(float *out, float *lse, const void *q_idx, dsa_dtype q_idx_dtype, const float *w_idx,
-                           const dsa_cache *keys, int32_t idx_heads, const void *q_mla, dsa_dtype q_mla_dtype,
-                           const dsa_cache *latent, int32_t kv_lora, int32_t mla_heads, const int32_t *seq_len,
-                           int32_t batch, int32_t max_len, int32_t k, float softmax_scale, float *scores_out,
-                           int32_t *indices_out, void *workspace, size_t workspace_bytes, void *stream) {
+size_t dsa_decode_window_workspace_size(int32_t batch, int32_t window, int32_t max_len, int32_t k,
+                                        int32_t mla_heads, int32_t kv_lora) {
+  if (batch <= 0 || window < 1 || window > kMaxWindow || max_len < 1 || k < 1 || mla_heads <= 0 || kv_lora <= 0)
+    return 0;
+  return step_layout(batch * window, max_len, k, mla_heads, kv_lora, kBF16, 576, window).total;
+}
+
+}  // extern "C"
+
+namespace {
+
+// The fused step over n_q = batch * window queries (window 1: one query per
+// sequence, its newest token).
+dsa_status decode_impl(float *out, float *lse, const void *q_idx, dsa_dtype q_idx_dtype, const float *w_idx,
+                       const dsa_cache *keys, int32_t idx_heads, const void *q_mla, dsa_dtype q_mla_dtype,
+                       const dsa_cache *latent, int32_t kv_lora, int32_t mla_heads, const int32_t *seq_len,
+                       int32_t batch, int32_t window, int32_t max_len, int32_t k, float softmax_scale,
+                       float *scores_out, int32_t *indices_out, void *workspace, size_t workspace_bytes,
+                       void *stream) {
   if (batch < 0 || max_len < 0) return DSA_ERR_INVALID_ARGUMENT;
+  if (window < 1) return DSA_ERR_INVALID_ARGUMENT;
+  if (window > kMaxWindow) return DSA_ERR_UNSUPPORTED;
   if (batch == 0) return DSA_OK;
   if (!out || !seq_len || k < 1 || max_len < 1) return DSA_ERR_INVALID_ARGUMENT;
+  if ((int64_t)batch * window > (int64_t)1 << 24) return DSA_ERR_UNSUPPORTED;
   dsa_status s = check_scores(q_idx, q_idx_dtype, w_idx, keys, idx_heads);
   if (s != DSA_OK) return s;
   s = check_attend(q_mla, q_mla_dtype, latent, kv_lora, mla_heads);
   if (s != DSA_OK) return s;
   if (k > kMaxTopk || max_len > kMaxLenTopk) return DSA_ERR_UNSUPPORTED;
+  const int32_t n_q = batch * window;
   // The workspace size query assumes the bf16 latent plan, which is the larger one.
-  const StepLayout L = step_layout(batch, max_len, k, mla_heads, kv_lora, kBF16, 576);
-  const StepLayout A = step_layout(batch, max_len, k, mla_heads, kv_lora, q_mla_dtype, latent->width);
+  const StepLayout L = step_layout(n_q, max_len, k, mla_heads, kv_lora, kBF16, 576, window);
+  const StepLayout A = step_layout(n_q, max_len, k, mla_heads, kv_lora, q_mla_dtype, latent->width, window);
   if (!workspace || workspace_bytes < L.total) return DSA_ERR_WORKSPACE_TOO_SMALL;
   hipStream_t st = static_cast<hipStream_t>(stream);
   uint8_t *ws = static_cast<uint8_t *>(workspace);
@@ -227,18 +250,55 @@ dsa_status dsa_decode_step(float *out, float *lse, const void *q_idx, dsa_dtype 
   int32_t *idx = indices_out ? indices_out : reinterpret_cast<int32_t *>(ws + L.off_idx);
   void *ws_topk = ws + L.off_topk;
   void *ws_att = ws + L.off_att;
+  // the queries' sequences and visible counts
+  const int32_t *q_seq = nullptr;
+  const int32_t *q_len = seq_len;
+  int seq_ident = 1;
+  if (window > 1) {
+    int32_t *rs = reinterpret_cast<int32_t *>(ws + L.off_rows);
+    int32_t *rl = reinterpret_cast<int32_t *>(ws + L.off_rows + round256((size_t)n_q * 4));
+    if (launch_window_rows(seq_len, batch, window, rs, rl, st) != hipSuccess) return DSA_ERR_DEVICE;
+    q_seq = rs;
+    q_len = rl;
+    seq_ident = 0;
+  }
   // bf16/fp8 keys: the score kernel also reports the top-k's candidate bounds
   uint32_t *bounds = (L.tp.chunks > 1 && q_idx_dtype != DSA_F32)
                          ? reinterpret_cast<uint32_t *>(ws + L.off_bounds) : nullptr;
-  hipError_t e = launch_index_scores(scores, ld, q_idx, q_idx_dtype, w_idx, to_dev(keys), keys->dtype, nullptr, 1,
-                                     seq_len, batch, idx_heads, max_len, ScoreBounds{bounds, k}, st);
+  hipError_t e = launch_index_scores(scores, ld, q_idx, q_idx_dtype, w_idx, to_dev(keys), keys->dtype, q_seq,
+                                     seq_ident, q_len, n_q, idx_heads, max_len, ScoreBounds{bounds, k}, st);
   if (e != hipSuccess) return DSA_ERR_DEVICE;
-  e = launch_topk(idx, nullptr, scores, ld, seq_len, L.tp, ws_topk, bounds, L.n_bounds,
-                  score_group_tokens(batch, max_len), st);
+  e = launch_topk(idx, nullptr, scores, ld, q_len, L.tp, ws_topk, bounds, L.n_bounds,
+                  score_group_tokens(n_q, max_len), st);
   if (e != hipSuccess) return DSA_ERR_DEVICE;
-  e = launch_attend(out, lse, q_mla, q_mla_dtype, to_dev(latent), kv_lora, idx, k, nullptr, 1, batch, mla_heads,
-                    softmax_scale, A.ap, ws_att, st);
+  e = launch_attend(out, lse, q_mla, q_mla_dtype, to_dev(latent), kv_lora, idx, k, q_seq, seq_ident, n_q,
+                    mla_heads, softmax_scale, A.ap, ws_att, st);
   return from_hip(e);
+}
+
+}  // namespace
+
+extern "C" {
+
+dsa_status dsa_decode_step(float *out, float *lse, const void *q_idx, dsa_dtype q_idx_dtype, const float *w_idx,
+                           const dsa_cache *keys, int32_t idx_heads, const void *q_mla, dsa_dtype q_mla_dtype,
+                           const dsa_cache *latent, int32_t kv_lora, int32_t mla_heads, const int32_t *seq_len,
+                           int32_t batch, int32_t max_len, int32_t k, float softmax_scale, float *scores_out,
+                           int32_t *indices_out, void *workspace, size_t workspace_bytes, void *stream) {
+  return decode_impl(out, lse, q_idx, q_idx_dtype, w_idx, keys, idx_heads, q_mla, q_mla_dtype, latent, kv_lora,
+                     mla_heads, seq_len, batch, 1, max_len, k, softmax_scale, scores_out, indices_out, workspace,
+                     workspace_bytes, stream);
+}
+
+dsa_status dsa_decode_window(float *out, float *lse, const void *q_idx, dsa_dtype q_idx_dtype, const float *w_idx,
+                             const dsa_cache *keys, int32_t idx_heads, const void *q_mla, dsa_dtype q_mla_dtype,
+                             const dsa_cache *latent, int32_t kv_lora, int32_t mla_heads, const int32_t *seq_len,
+                             int32_t batch, int32_t window, int32_t max_len, int32_t k, float softmax_scale,
+                             float *scores_out, int32_t *indices_out, void *workspace, size_t workspace_bytes,
+                             void *stream) {
+  return decode_impl(out, lse, q_idx, q_idx_dtype, w_idx, keys, idx_heads, q_mla, q_mla_dtype, latent, kv_lora,
+                     mla_heads, seq_len, batch, window, max_len, k, softmax_scale, scores_out, indices_out,
+                     workspace, workspace_bytes, stream);
 }
 
 }  // extern "C"

@@ -59,5 +59,9 @@ hipError_t launch_attend(float *out, float *lse, const void *q, int dt, const Ca
                          float scale, const AttendPlan &plan, void *workspace, hipStream_t stream);
 
 hipError_t launch_fill_zero(uint32_t *p, size_t words, hipStream_t stream);
+// Rows of a multi-token decode window: query i = b * window + j of sequence b
+// sits at position seq_len[b] - window + j and sees max(0, that + 1) tokens.
+hipError_t launch_window_rows(const int32_t *seq_len, int batch, int window, int32_t *q_seq, int32_t *q_len,
+                              hipStream_t stream);
 
 }  // namespace dsa

@@ -503,6 +503,24 @@ __global__ void fill_zero_kernel(uint32_t *p, size_t words) {
     p[i] = 0u;
 }
 
+__global__ void window_rows_kernel(const int32_t *__restrict__ seq_len, int batch, int window,
+                                   int32_t *__restrict__ q_seq, int32_t *__restrict__ q_len) {
+  const int i = blockIdx.x * blockDim.x + threadIdx.x;
+  if (i >= batch * window) return;
+  const int b = i / window, j = i - b * window;
+  const int n = seq_len[b] - window + j + 1;
+  q_seq[i] = b;
+  q_len[i] = n > 0 ? n : 0;
+}
+
+hipError_t launch_window_rows(const int32_t *seq_len, int batch, int window, int32_t *q_seq, int32_t *q_len,
+                              hipStream_t stream) {
+  const int n = batch * window;
+  hipLaunchKernelGGL(window_rows_kernel, dim3((n + 255) / 256), dim3(256), 0, stream, seq_len, batch, window, q_seq,
+                     q_len);
+  return hipGetLastError();
+}
+
 hipError_t launch_fill_zero(uint32_t *p, size_t words, hipStream_t stream) {
   if (words == 0) return hipSuccess;
   size_t blocks = (words + 255) / 256;

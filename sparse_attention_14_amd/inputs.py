@@ -181,6 +181,7 @@ class Workload:
     prefill_queries: int = 0       # > 0: one sequence, queries at the last positions (chunked prefill)
     spare_blocks: int = 2          # poisoned blocks beyond the used ones (paged)
     capacity_pad: int = 0          # poisoned rows beyond the longest sequence (contiguous)
+    window: int = 1                # decode: queries per sequence, at its last `window` positions
 
 
 def _fill_cache_rows(storage_rows: np.ndarray, dtype: str, rng: np.random.Generator, sigma: float,
@@ -316,9 +317,11 @@ def make_problem(wl: Workload) -> Problem:
             lens_seq = np.full(wl.batch, lo, dtype=np.int64)
         else:
             lens_seq = rng_for(wl.wid, "lens").integers(lo, hi + 1, size=wl.batch).astype(np.int64)
-        q_len = lens_seq.astype(np.int32)
-        q_seq = np.arange(wl.batch, dtype=np.int32)
-        nq = wl.batch
+        # query j of sequence b sits at position len_b - window + j and sees up to it
+        W = wl.window
+        q_seq = np.repeat(np.arange(wl.batch, dtype=np.int32), W)
+        q_len = np.maximum(np.repeat(lens_seq, W) - W + 1 + np.tile(np.arange(W), wl.batch), 0).astype(np.int32)
+        nq = wl.batch * W
     layout = _layout(wl, lens_seq, rng_for(wl.wid, "block_perm"))
     keys = _make_cache(wl, lens_seq, wl.key_dtype, wl.idx_dim, wl.key_sigma, "keys", layout, wl.key_scale_range)
     latent = _make_cache(wl, lens_seq, wl.latent_dtype, wl.kv_lora + wl.rope, wl.latent_sigma, "latent", layout)
@@ -363,7 +366,12 @@ DECODE_128K_FP8 = dataclasses.replace(DECODE_8K, name="decode_128k_fp8", wid=3, 
 PREFILL_64K = dataclasses.replace(DECODE_8K, name="prefill_chunk_2048_at_64k", wid=4, batch=1,
                                   seq_len=(65536, 65536), prefill_queries=2048)
 
+# Multi-token decode window: the known token and three guesses per sequence.
+DECODE_128K_FP8_W4 = dataclasses.replace(DECODE_128K_FP8, name="decode_128k_fp8_window4", wid=5, window=4)
+PAGED_DECODE_W4 = dataclasses.replace(PAGED_DECODE, name="paged_decode_16x16k_32k_window4", wid=6, window=4)
+
 FULL_WORKLOADS = {w.name: w for w in (TINY_FP32, DECODE_8K, PAGED_DECODE, DECODE_128K_FP8, PREFILL_64K)}
+WINDOW_WORKLOADS = {w.name: w for w in (DECODE_128K_FP8_W4, PAGED_DECODE_W4)}
 
 
 def small(wl: Workload, **kw) -> Workload:

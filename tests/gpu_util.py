@@ -144,3 +144,25 @@ def gpu_decode_step(dp, ws=None):
                         dp.q_len, p.max_len, p.topk, p.softmax_scale, ws, scores_out=scores, indices_out=idx)
     torch.cuda.synchronize()
     return out, lse, scores, idx, ws
+
+
+def gpu_decode_window(dp, ws=None):
+    """dsa_decode_window over the problem's sequences (rows b * window + j)."""
+    p = dp.host
+    W = p.meta["workload"].window
+    seq_len = torch.tensor(np.asarray(p.meta["seq_lens"], dtype=np.int32), device="cuda")
+    B = int(seq_len.shape[0])
+    n_q, H, L = p.n_q, p.mla_heads, p.kv_lora
+    assert n_q == B * W
+    max_len = int(max(p.meta["seq_lens"]))
+    out = torch.full((n_q, H, L), float("nan"), device="cuda")
+    lse = torch.full((n_q, H), float("nan"), device="cuda")
+    scores = torch.full((n_q, max_len), float("nan"), device="cuda")
+    idx = torch.full((n_q, p.topk), -7, dtype=torch.int32, device="cuda")
+    if ws is None:
+        ws = torch.zeros(dsa.dsa_decode_window_workspace_size(B, W, max_len, p.topk, H, L), dtype=torch.uint8,
+                         device="cuda")
+    dsa.dsa_decode_window(out, lse, dp.q_idx, p.q_idx_dtype, dp.w_idx, dp.keys, dp.q_mla, p.q_mla_dtype, dp.latent,
+                          L, seq_len, W, max_len, p.topk, p.softmax_scale, ws, scores_out=scores, indices_out=idx)
+    torch.cuda.synchronize()
+    return out, lse, scores, idx, ws

@@ -128,6 +128,33 @@ def test_decode_step_validation(lib):
     assert call(ws=16, wsb=64) == 3
 
 
+def test_decode_window_validation(lib):
+    keys = _cache()
+    lat = _cache(width=576, row_stride=1152, block_stride=1152 * 1024)
+    f = lib.dsa_decode_window
+
+    def call(batch=1, window=4, ws=None, wsb=0, k=2048, max_len=100, out=16, seq_len=16):
+        return f(out, None, 16, 1, 16, ctypes.byref(keys), 32, 16, 1, ctypes.byref(lat), 512, 64, seq_len, batch,
+                 window, max_len, k, 0.04, None, None, ws, wsb, None)
+
+    assert call(batch=0) == 0
+    assert call(window=0) == 1
+    assert call(window=-2) == 1
+    assert call(window=65) == 2
+    assert call(out=None) == 1
+    assert call(seq_len=None) == 1
+    assert call() == 3                                                # no workspace
+    assert call(ws=16, wsb=64) == 3
+    # sizes: a window of w over b sequences needs at least what b * w single-token rows need
+    ws1 = lib.dsa_decode_step_workspace_size(16, 131072, 2048, 64, 512)
+    ws4 = lib.dsa_decode_window_workspace_size(4, 4, 131072, 2048, 64, 512)
+    assert ws4 >= ws1 > 0
+    assert lib.dsa_decode_window_workspace_size(4, 1, 131072, 2048, 64, 512) == \
+        lib.dsa_decode_step_workspace_size(4, 131072, 2048, 64, 512)
+    assert lib.dsa_decode_window_workspace_size(4, 0, 131072, 2048, 64, 512) == 0
+    assert lib.dsa_decode_window_workspace_size(4, 65, 131072, 2048, 64, 512) == 0
+
+
 def test_workspace_clear_validation(lib):
     assert lib.dsa_workspace_clear(None, 0, None) == 0
     assert lib.dsa_workspace_clear(None, 16, None) == 1
