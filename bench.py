@@ -45,6 +45,7 @@ def parse():
     ap.add_argument("--copies", type=int, default=6, help="device copies of the caches rotated over")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--no-prefill", action="store_true")
+    ap.add_argument("--no-window", action="store_true", help="skip the multi-token decode window leg")
     ap.add_argument("--copy-probe", action="store_true",
                     help="only run a plain 1 GiB device copy three times (calibrates HBM byte counters) and exit")
     return ap.parse_args()
@@ -61,6 +62,48 @@ def decode_algorithmic_bytes(p) -> int:
     q = p.q_idx.size * eb[p.q_idx_dtype] + p.w_idx.size * 4 + p.q_mla.size * eb[p.q_mla_dtype]
     out = p.n_q * p.mla_heads * (p.kv_lora + 1) * 4
     return keys + latent + q + out
+
+
+def window_algorithmic_bytes(p) -> int:
+    """As decode_algorithmic_bytes for a multi-token window: the window's queries
+    share their sequence's keys, which are counted once per sequence."""
+    eb = {"f32": 4, "bf16": 2, "e4m3fn": 1}
+    n_tok = int(sum(int(n) for n in p.meta["seq_lens"]))
+    kept = int(sum(min(int(n), p.topk) for n in p.q_len))
+    keys = n_tok * p.idx_dim * eb[p.keys.dtype] + (n_tok * 4 if p.keys.dtype == "e4m3fn" else 0)
+    latent = kept * (p.kv_lora + p.rope) * eb[p.latent.dtype]
+    q = p.q_idx.size * eb[p.q_idx_dtype] + p.w_idx.size * 4 + p.q_mla.size * eb[p.q_mla_dtype]
+    out = p.n_q * p.mla_heads * (p.kv_lora + 1) * 4
+    return keys + latent + q + out
+
+
+def time_graph_steps(torch, step, n_copies, steps, warmup):
+    """Seconds per step: steps over every input copy in turn captured as one HIP
+    graph, replayed (plus single-step graphs for a remainder)."""
+    side = torch.cuda.Stream()
+
+    def capture(fn):
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g, stream=side):
+            fn()
+        return g
+
+    seq_graph = capture(lambda: [step(ci) for ci in range(n_copies)])
+    single = [capture(lambda ci=ci: step(ci)) for ci in range(n_copies)]
+    torch.cuda.synchronize()
+
+    def run(n):
+        for _ in range(n // n_copies):
+            seq_graph.replay()
+        for ci in range(n % n_copies):
+            single[ci].replay()
+
+    run(warmup)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    run(steps)
+    torch.cuda.synchronize()
+    return (time.perf_counter() - t0) / steps
 
 
 def score_kernel_bytes(p) -> int:
@@ -297,6 +340,45 @@ def main():
                    "topk_ms": round(t_pt * 1e3, 3), "sparse_mla_ms": round(t_pa * 1e3, 3),
                    "sparse_mla_tflops": round(mla_flops / t_pa / 1e12, 1)}
 
+    # ------------------------------------------- multi-token decode window ---
+    window = None
+    if not args.no_window:
+        if not args.no_prefill:
+            del pp, dpp, ps, pidx, tws, pout, plse, aws
+        else:
+            del copies, workspaces, seq_graph, single
+        torch.cuda.empty_cache()
+        ww = inputs.DECODE_128K_FP8_W4
+        t0 = time.time()
+        pw = inputs.make_problem(ww)
+        dpw = device.upload(pw)
+        print(f"[bench] generated and uploaded {ww.name} in {time.time() - t0:.1f}s", file=sys.stderr, flush=True)
+        W = ww.window
+        seq_len = torch.tensor(np.asarray(pw.meta["seq_lens"], dtype=np.int32), device="cuda")
+        nb, n_wc = int(seq_len.shape[0]), 3
+        wcopies = [(dpw.keys, dpw.latent)] + [(clone_cache(dpw.keys), clone_cache(dpw.latent)) for _ in range(n_wc - 1)]
+        wout = torch.empty(pw.n_q, H, L, device="cuda")
+        wlse = torch.empty(pw.n_q, H, device="cuda")
+        wmax = int(max(pw.meta["seq_lens"]))
+        wwsz = dsa.dsa_decode_window_workspace_size(nb, W, wmax, k, H, L)
+        wws = [torch.zeros(wwsz, dtype=torch.uint8, device="cuda") for _ in wcopies]
+
+        def wstep(ci):
+            keys, lat = wcopies[ci]
+            dsa.dsa_decode_window(wout, wlse, dpw.q_idx, pw.q_idx_dtype, dpw.w_idx, keys, dpw.q_mla, pw.q_mla_dtype,
+                                  lat, L, seq_len, W, wmax, k, pw.softmax_scale, wws[ci])
+
+        for i in range(3):
+            wstep(i % n_wc)
+        torch.cuda.synchronize()
+        assert torch.isfinite(wout).all().item(), "non-finite window output"
+        t_w = time_graph_steps(torch, wstep, n_wc, max(args.steps // 2, 30), max(args.warmup, 6))
+        wbytes = window_algorithmic_bytes(pw)
+        window = {"workload": ww.name, "sequences": nb, "window": W, "queries": pw.n_q, "context": wmax,
+                  "us_per_step": round(t_w * 1e6, 2), "us_per_query": round(t_w * 1e6 / pw.n_q, 2),
+                  "bytes_per_step": wbytes, "GB_per_s": round(wbytes / t_w / 1e9, 1),
+                  "hbm_frac": round(wbytes / t_w / 1e9 / HBM_PEAK_GBS, 4), "cache_copies": n_wc}
+
     # ------------------------------------------------------ CPU baseline ---
     cpu = None
     if not args.no_cpu:
@@ -318,7 +400,7 @@ def main():
         "decode_us_per_step": round(t_step * 1e6, 2), "decode_us_per_step_eager": round(t_eager * 1e6, 2),
         "decode_us_per_step_one_per_launch": round(t_single * 1e6, 2),
         "decode_bytes_per_step": step_bytes, "decode_hbm_frac": round(gbs / HBM_PEAK_GBS, 4),
-        "roofline": roofline, "prefill": prefill, "cpu_baseline": cpu, "device": dev_name,
+        "roofline": roofline, "prefill": prefill, "window": window, "cpu_baseline": cpu, "device": dev_name,
     }
     print(json.dumps(line))
 

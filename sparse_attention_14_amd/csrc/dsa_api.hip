@@ -4,6 +4,8 @@
 #include "../../include/dsa.h"
 #include "kernels.hpp"
 
+#include <algorithm>
+
 using namespace dsa;
 
 namespace {
@@ -102,9 +104,11 @@ struct StepLayout {
 };
 
 // batch = queries of the step (sequences x window); window > 1 adds the rows'
-// (sequence, visible count) arrays.
+// (sequence, visible count) arrays.  score_rows: workgroup rows of the score
+// grid (batch, or batch / 2 when pairs of queries share key loads); the bound
+// area is sized for either, so the total does not depend on it.
 StepLayout step_layout(int32_t batch, int32_t max_len, int32_t k, int32_t mla_heads, int32_t kv_lora,
-                       int latent_dt, int width, int32_t window = 1) {
+                       int latent_dt, int width, int32_t window = 1, int32_t score_rows = 0) {
   StepLayout L{};
   L.ld = ((int64_t)max_len + 63) / 64 * 64;
   L.tp = plan_topk(batch, k, max_len);
@@ -114,9 +118,11 @@ StepLayout step_layout(int32_t batch, int32_t max_len, int32_t k, int32_t mla_he
   off += round256((size_t)batch * L.ld * 4);
   L.off_idx = off;
   off += round256((size_t)batch * k * 4);
-  L.n_bounds = score_groups_per_row(batch, max_len);
+  L.n_bounds = score_groups_per_row(score_rows > 0 ? score_rows : batch, max_len);
+  int most = score_groups_per_row(batch, max_len);
+  if (window % 2 == 0) most = std::max(most, score_groups_per_row(batch / 2, max_len));
   L.off_bounds = off;
-  off += round256((size_t)batch * L.n_bounds * 4);
+  off += round256((size_t)batch * most * 4);
   L.off_topk = off;
   off += round256(L.tp.total);
   L.off_att = off;
@@ -239,9 +245,13 @@ dsa_status decode_impl(float *out, float *lse, const void *q_idx, dsa_dtype q_id
   if (s != DSA_OK) return s;
   if (k > kMaxTopk || max_len > kMaxLenTopk) return DSA_ERR_UNSUPPORTED;
   const int32_t n_q = batch * window;
+  // neighbouring queries of a window share each key load (bf16/fp8 keys, up to 32 heads)
+  const bool pairs = window % 2 == 0 && idx_heads <= 32 && q_idx_dtype != DSA_F32 && keys->width == 128;
+  const int32_t score_rows = pairs ? n_q / 2 : n_q;
   // The workspace size query assumes the bf16 latent plan, which is the larger one.
-  const StepLayout L = step_layout(n_q, max_len, k, mla_heads, kv_lora, kBF16, 576, window);
-  const StepLayout A = step_layout(n_q, max_len, k, mla_heads, kv_lora, q_mla_dtype, latent->width, window);
+  const StepLayout L = step_layout(n_q, max_len, k, mla_heads, kv_lora, kBF16, 576, window, score_rows);
+  const StepLayout A = step_layout(n_q, max_len, k, mla_heads, kv_lora, q_mla_dtype, latent->width, window,
+                                   score_rows);
   if (!workspace || workspace_bytes < L.total) return DSA_ERR_WORKSPACE_TOO_SMALL;
   hipStream_t st = static_cast<hipStream_t>(stream);
   uint8_t *ws = static_cast<uint8_t *>(workspace);
@@ -266,10 +276,10 @@ dsa_status decode_impl(float *out, float *lse, const void *q_idx, dsa_dtype q_id
   uint32_t *bounds = (L.tp.chunks > 1 && q_idx_dtype != DSA_F32)
                          ? reinterpret_cast<uint32_t *>(ws + L.off_bounds) : nullptr;
   hipError_t e = launch_index_scores(scores, ld, q_idx, q_idx_dtype, w_idx, to_dev(keys), keys->dtype, q_seq,
-                                     seq_ident, q_len, n_q, idx_heads, max_len, ScoreBounds{bounds, k}, st);
+                                     seq_ident, q_len, n_q, idx_heads, max_len, ScoreBounds{bounds, k}, st, pairs);
   if (e != hipSuccess) return DSA_ERR_DEVICE;
   e = launch_topk(idx, nullptr, scores, ld, q_len, L.tp, ws_topk, bounds, L.n_bounds,
-                  score_group_tokens(n_q, max_len), st);
+                  score_group_tokens(score_rows, max_len), st);
   if (e != hipSuccess) return DSA_ERR_DEVICE;
   e = launch_attend(out, lse, q_mla, q_mla_dtype, to_dev(latent), kv_lora, idx, k, q_seq, seq_ident, n_q,
                     mla_heads, softmax_scale, A.ap, ws_att, st);

@@ -45,7 +45,13 @@ constexpr int kPrefillMinQueries = 64;   // the GEMM-shaped kernel takes over fr
 // next P tiles stay in flight.  Tile positions, block-table lookups and tile
 // base addresses are wavefront-uniform (scalar); a lane adds one precomputed
 // 32-bit offset per load.
-template <bool FP8, int D, int MT, int TPW>
+//
+// PAIR: the two M tiles are two queries of one sequence (rows 2 y and 2 y + 1,
+// up to 32 heads each), e.g. neighbouring queries of a multi-token decode
+// window: every key tile is loaded once for both, each query keeps its own
+// visible count, score row and candidate bounds.  Otherwise the M tiles are
+// heads 0-31 and 32-63 of one query (row y).
+template <bool FP8, int D, int MT, int TPW, bool PAIR>
 __global__ __launch_bounds__(256) void scores_mfma_kernel(float *__restrict__ scores, int64_t ld,
                                                           const uint16_t *__restrict__ q, const float *__restrict__ w,
                                                           CacheDev keys, const int32_t *__restrict__ q_seq,
@@ -61,6 +67,8 @@ __global__ __launch_bounds__(256) void scores_mfma_kernel(float *__restrict__ sc
   constexpr int NLD = TILEB / 1024;     // 1 KB wavefront loads per tile
   constexpr int P = TPW < 2 ? TPW : 2;  // tiles in flight ahead of the one being scored
   static_assert(64 % CPR == 0, "a 1 KB load must cover whole rows");
+  static_assert(!PAIR || MT == 2, "a query pair uses both M tiles");
+  constexpr int NQ = PAIR ? 2 : 1;      // queries (score rows) of the wavefront
   __shared__ __align__(16) uint8_t stage_all[4][TILEB];
 
   // Fetch every kernel argument at once: the compiler would otherwise load each
@@ -74,15 +82,20 @@ __global__ __launch_bounds__(256) void scores_mfma_kernel(float *__restrict__ sc
       : "s"(scores), "s"(ld), "s"(q), "s"(w), "s"(keys.rows), "s"(keys.scale), "s"(keys.row_stride),
         "s"(keys.block_stride), "s"(keys.scale_block_stride), "s"(keys.table), "s"(keys.block_size),
         "s"(keys.max_blocks), "s"(q_seq), "s"(seq_ident), "s"(q_len), "s"(n_heads), "s"(bounds), "s"(topk));
-  const int qi = blockIdx.y;
+  const int qi = PAIR ? 2 * blockIdx.y : blockIdx.y;   // first score row
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int half = lane >> 5, col = lane & 31;
-  const int n = q_len[qi];
+  int nq[NQ];   // visible tokens of each row
+#pragma unroll
+  for (int u = 0; u < NQ; ++u) nq[u] = q_len[qi + u];
+  const int n = PAIR ? (nq[0] > nq[NQ - 1] ? nq[0] : nq[NQ - 1]) : nq[0];
   const int ntile = (n + 31) / 32;
   const int wid = blockIdx.x * 4 + wave + zero;
   const int tile_begin = wid * TPW;
-  float lane_best = -__builtin_inff();   // largest score of this lane's keys (bounds only)
+  float lane_best[NQ];   // largest score of this lane's keys, per row (bounds only)
+#pragma unroll
+  for (int u = 0; u < NQ; ++u) lane_best[u] = -__builtin_inff();
 
   if (tile_begin < ntile) {
     const int seq = seq_of(q_seq, qi, seq_ident);
@@ -154,19 +167,20 @@ __global__ __launch_bounds__(256) void scores_mfma_kernel(float *__restrict__ sc
     float wr[MT][16];
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt) {
-      const int head = 32 * mt + col;
-      const uint16_t *qrow = q + ((int64_t)qi * n_heads + (head < n_heads ? head : n_heads - 1)) * D + half * HALF;
+      const int qm = PAIR ? qi + mt : qi;          // the tile's query
+      const int head = PAIR ? col : 32 * mt + col;
+      const uint16_t *qrow = q + ((int64_t)qm * n_heads + (head < n_heads ? head : n_heads - 1)) * D + half * HALF;
 #pragma unroll
       for (int ks = 0; ks < KS; ++ks) {
         u32x4 v = load16(qrow + 8 * ks);
         if (head >= n_heads) v = u32x4{0, 0, 0, 0};
         a[mt][ks] = as_bf16x8(v);
       }
-      // Accumulator element r of this lane is head 32*mt + 8*(r/4) + 4*half + r%4.
+      // Accumulator element r of this lane is head (PAIR ? 0 : 32*mt) + 8*(r/4) + 4*half + r%4.
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
-        const int m = 32 * mt + 8 * (r >> 2) + 4 * half + (r & 3);
-        const float x = w[(int64_t)qi * n_heads + (m < n_heads ? m : n_heads - 1)];
+        const int m = (PAIR ? 0 : 32 * mt) + 8 * (r >> 2) + 4 * half + (r & 3);
+        const float x = w[(int64_t)qm * n_heads + (m < n_heads ? m : n_heads - 1)];
         wr[mt][r] = m < n_heads ? x : 0.0f;
       }
     }
@@ -203,22 +217,28 @@ __global__ __launch_bounds__(256) void scores_mfma_kernel(float *__restrict__ sc
       // the sign applied by flipping the accumulator's sign bit: one multiply per
       // key instead of one per head, and the same summation order for every key.
       const uint32_t flip = FP8 ? (__float_as_uint(sc) & 0x80000000u) : 0u;
-      float s = 0.0f;
+      float s[NQ];
+#pragma unroll
+      for (int u = 0; u < NQ; ++u) s[u] = 0.0f;
 #pragma unroll
       for (int mt = 0; mt < MT; ++mt) {
         f32x16 acc = {};
 #pragma unroll
         for (int ks = 0; ks < KS; ++ks) acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[mt][ks], b[ks], acc, 0, 0, 0);
+        float &su = s[PAIR ? mt : 0];
 #pragma unroll
-        for (int r = 0; r < 16; ++r) s = fmaf(wr[mt][r], relu(__uint_as_float(__float_as_uint(acc[r]) ^ flip)), s);
+        for (int r = 0; r < 16; ++r) su = fmaf(wr[mt][r], relu(__uint_as_float(__float_as_uint(acc[r]) ^ flip)), su);
       }
-      if (FP8) s *= fabsf(sc);
-      s = halves_sum(s);
       const int t = (tile_begin + it) * 32 + col;
-      if (half == 0 && t < n) scores[(int64_t)qi * ld + t] = s;
-      // only wavefronts whose keys are all visible report a bound, so every
-      // score reaches the maximum unmasked
-      lane_best = fmaxf(lane_best, s);
+#pragma unroll
+      for (int u = 0; u < NQ; ++u) {
+        float x = FP8 ? s[u] * fabsf(sc) : s[u];
+        x = halves_sum(x);
+        if (half == 0 && t < nq[u]) scores[(int64_t)(qi + u) * ld + t] = x;
+        // only wavefronts whose keys are all visible to the row report a
+        // bound, so every score reaches the maximum unmasked
+        lane_best[u] = fmaxf(lane_best[u], x);
+      }
     }
   }
 
@@ -228,20 +248,23 @@ __global__ __launch_bounds__(256) void scores_mfma_kernel(float *__restrict__ sc
   // maximum is the score of a distinct token.  Other wavefronts report 0.
   if (bounds) {
     constexpr int per_wave = TPW * 32;
-    const int gfull = n / per_wave;
-    const int rank = bound_rank(topk, gfull, 32);
-    uint32_t T = 0;
-    if ((wid + 1) * per_wave <= n && rank >= 1) {
-      // rank-th largest of the 32 lane maxima (lanes 32..63 hold 0): extract
-      // the maximum rank times
-      uint32_t v = half == 0 ? order_key(lane_best) : 0u;
-      for (int i = 0; i < rank; ++i) {
-        T = wave_max_u32(v);
-        const uint64_t hit = __ballot(v == T);
-        if (lane == __ffsll((unsigned long long)hit) - 1) v = 0;
+#pragma unroll
+    for (int u = 0; u < NQ; ++u) {
+      const int gfull = nq[u] / per_wave;
+      const int rank = bound_rank(topk, gfull, 32);
+      uint32_t T = 0;
+      if ((wid + 1) * per_wave <= nq[u] && rank >= 1) {
+        // rank-th largest of the 32 lane maxima (lanes 32..63 hold 0): extract
+        // the maximum rank times
+        uint32_t v = half == 0 ? order_key(lane_best[u]) : 0u;
+        for (int i = 0; i < rank; ++i) {
+          T = wave_max_u32(v);
+          const uint64_t hit = __ballot(v == T);
+          if (lane == __ffsll((unsigned long long)hit) - 1) v = 0;
+        }
       }
+      if (lane == 0) bounds[(int64_t)(qi + u) * gridDim.x * 4 + wid] = T;
     }
-    if (lane == 0) bounds[(int64_t)qi * gridDim.x * 4 + wid] = T;
   }
 }
 
@@ -499,17 +522,18 @@ __global__ __launch_bounds__(256) void scores_f32_kernel(float *__restrict__ sco
   }
 }
 
-template <bool FP8, int D, int MT>
+template <bool FP8, int D, int MT, bool PAIR>
 hipError_t run_mfma(float *scores, int64_t ld, const void *q, const float *w, const CacheDev &keys,
                     const int32_t *q_seq, int seq_ident, const int32_t *q_len, int n_q, int n_heads, int max_len,
                     const ScoreBounds &sb, hipStream_t stream) {
+  const int rows = PAIR ? n_q / 2 : n_q;   // workgroup rows of the grid
   const int tiles = (max_len + 31) / 32;
-  const int tpw = score_tiles_per_wave(n_q, max_len);
+  const int tpw = score_tiles_per_wave(rows, max_len);
   const int gx = (tiles + 4 * tpw - 1) / (4 * tpw);
-  dim3 grid(gx, n_q);
+  dim3 grid(gx, rows);
   const uint16_t *qb = static_cast<const uint16_t *>(q);
-#define DSA_SK(T)                                                                                            \
-  hipLaunchKernelGGL((scores_mfma_kernel<FP8, D, MT, T>), grid, dim3(256), 0, stream, scores, ld, qb, w, keys, \
+#define DSA_SK(T)                                                                                                  \
+  hipLaunchKernelGGL((scores_mfma_kernel<FP8, D, MT, T, PAIR>), grid, dim3(256), 0, stream, scores, ld, qb, w, keys, \
                      q_seq, seq_ident, q_len, n_heads, sb.bounds, sb.topk)
   switch (tpw) {
     case 1: DSA_SK(1); break;
@@ -533,7 +557,7 @@ hipError_t run_f32(float *scores, int64_t ld, const void *q, const float *w, con
 
 hipError_t dispatch(float *scores, int64_t ld, const void *q, int q_dt, const float *w, const CacheDev &keys,
                     int key_dt, const int32_t *q_seq, int seq_ident, const int32_t *q_len, int n_q, int n_heads,
-                    int max_len, const ScoreBounds &sb, hipStream_t s) {
+                    int max_len, const ScoreBounds &sb, bool pairs, hipStream_t s) {
   const int D = keys.width;
   if (q_dt == kF32) {
     switch (D) {
@@ -557,17 +581,21 @@ hipError_t dispatch(float *scores, int64_t ld, const void *q, int q_dt, const fl
                        static_cast<const uint16_t *>(q), w, keys, q_seq, q_len, n_q, n_heads, per);
     return hipGetLastError();
   }
-#define DSA_SC(F, DD, M)                                                                                    \
-  return run_mfma<F, DD, M>(scores, ld, q, w, keys, q_seq, seq_ident, q_len, n_q, n_heads, max_len, sb, s)
+#define DSA_SC(F, DD, M, PR)                                                                                \
+  return run_mfma<F, DD, M, PR>(scores, ld, q, w, keys, q_seq, seq_ident, q_len, n_q, n_heads, max_len, sb, s)
+  if (pairs && !two && D == 128) {
+    if (fp8) DSA_SC(true, 128, 2, true);
+    DSA_SC(false, 128, 2, true);
+  }
   if (D == 128) {
-    if (fp8) { if (two) DSA_SC(true, 128, 2); DSA_SC(true, 128, 1); }
-    if (two) DSA_SC(false, 128, 2);
-    DSA_SC(false, 128, 1);
+    if (fp8) { if (two) DSA_SC(true, 128, 2, false); DSA_SC(true, 128, 1, false); }
+    if (two) DSA_SC(false, 128, 2, false);
+    DSA_SC(false, 128, 1, false);
   }
   if (D == 64) {
-    if (fp8) { if (two) DSA_SC(true, 64, 2); DSA_SC(true, 64, 1); }
-    if (two) DSA_SC(false, 64, 2);
-    DSA_SC(false, 64, 1);
+    if (fp8) { if (two) DSA_SC(true, 64, 2, false); DSA_SC(true, 64, 1, false); }
+    if (two) DSA_SC(false, 64, 2, false);
+    DSA_SC(false, 64, 1, false);
   }
 #undef DSA_SC
   return hipErrorInvalidValue;
@@ -578,8 +606,10 @@ hipError_t dispatch(float *scores, int64_t ld, const void *q, int q_dt, const fl
 hipError_t launch_index_scores(float *scores, int64_t ld, const void *q, int q_dt, const float *w,
                                const CacheDev &keys, int key_dt, const int32_t *q_seq, int seq_ident,
                                const int32_t *q_len, int n_q, int n_heads, int max_len, const ScoreBounds &sb,
-                               hipStream_t stream) {
-  return dispatch(scores, ld, q, q_dt, w, keys, key_dt, q_seq, seq_ident, q_len, n_q, n_heads, max_len, sb, stream);
+                               hipStream_t stream, bool pairs) {
+  if (pairs && ((n_q & 1) || keys.width != 128 || n_heads > 32 || q_dt == kF32)) return hipErrorInvalidValue;
+  return dispatch(scores, ld, q, q_dt, w, keys, key_dt, q_seq, seq_ident, q_len, n_q, n_heads, max_len, sb, pairs,
+                  stream);
 }
 
 int score_tiles_per_wave(int n_q, int max_len) {

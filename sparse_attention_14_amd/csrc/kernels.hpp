@@ -19,13 +19,17 @@ struct ScoreBounds {
   uint32_t *bounds;  // [n_q][score_groups_per_row()] or nullptr
   int topk;
 };
+// pairs: rows 2 y and 2 y + 1 belong to one sequence (bf16/fp8 keys, <= 32
+// heads): each key tile is read once for both (decode windows).  n_q must be
+// even.  Bound groups are then laid out for a grid of n_q / 2 workgroup rows:
+// score_groups_per_row / score_group_tokens take that row count.
 hipError_t launch_index_scores(float *scores, int64_t ld, const void *q, int q_dt, const float *w,
                                const CacheDev &keys, int key_dt, const int32_t *q_seq, int seq_ident,
                                const int32_t *q_len, int n_q, int n_heads, int max_len, const ScoreBounds &sb,
-                               hipStream_t stream);
-int score_tiles_per_wave(int n_q, int max_len);
-int score_groups_per_row(int n_q, int max_len);
-int score_group_tokens(int n_q, int max_len);
+                               hipStream_t stream, bool pairs = false);
+int score_tiles_per_wave(int rows, int max_len);
+int score_groups_per_row(int rows, int max_len);
+int score_group_tokens(int rows, int max_len);
 
 // ---- top-k ------------------------------------------------------------------
 struct TopkPlan {
@@ -51,6 +55,7 @@ struct AttendPlan {
   int n_q, n_heads, kv_lora, width, k;
   int splits;          // index-slot splits per query (1: no merge pass)
   int rows_per_split;  // multiple of 64
+  int wide;            // 1: one workgroup per (query, 64 heads, split), else per (query, 16 heads, split)
   size_t off_part_o, off_part_ml, total;
 };
 AttendPlan plan_attend(int n_q, int n_heads, int kv_lora, int width, int k, int dtype);

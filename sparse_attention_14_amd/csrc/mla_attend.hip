@@ -34,6 +34,7 @@ constexpr int kRowBytes = kW * 2 + 16;          // padded LDS row
 constexpr int kChunks = kW * 2 / 16;            // 16-byte chunks per row (72)
 constexpr int kMaxSplits = 32;
 constexpr int kAttTargetWGs = 256;   // workgroups aimed at by the split count
+constexpr int kWideMinRows = 16;     // (query, 64-head block) pairs from which the 64-head kernel is used
 
 struct AttArgs {
   float *out;
@@ -294,6 +295,194 @@ __global__ __launch_bounds__(kAttThreads) void attend_bf16_kernel(AttArgs a) {
   }
 }
 
+// Many queries (decode windows, prefill): a workgroup owns one query, a block
+// of 64 heads and a split of the index slots, so each kept row is gathered
+// once for all 64 heads (the 16-head kernel above spreads few queries over
+// more workgroups, at the price of gathering every row once per head group).
+// Per 64-slot step the rows sit in LDS (8 threads per row, 128 contiguous
+// bytes per load); wavefront w takes head group w / 2 (16 heads) and half
+// w % 2 of the rows for QK^T and of the 512 value columns for PV.  The next
+// step's rows are loaded into registers while a step is computed.
+constexpr int kWideHeads = 64;
+constexpr int kWideStep = 64;
+constexpr int kWideThreads = 512;
+constexpr int kWidePer = kW * 2 / 16 / 8;   // 16-byte chunks per thread and row (9)
+
+template <bool SPLIT>
+__global__ __launch_bounds__(kWideThreads) void attend_wide_kernel(AttArgs a) {
+  __shared__ __align__(16) uint8_t rows[kWideStep * kRowBytes];
+  __shared__ __align__(16) uint16_t lp[4][2][kHG * kWideStep];   // per head group: P hi / lo, [head][row]
+  __shared__ float red[4][2][2][kHG];                             // [head group][max | sum][row half][head]
+  __shared__ uint8_t lvalid[kWideStep];
+
+  const int H = a.n_heads;
+  const int n_hb = H / kWideHeads;
+  const int wg = blockIdx.x;
+  const int qi = wg / (a.splits * n_hb);
+  const int rem = wg - qi * a.splits * n_hb;
+  const int hb = rem / a.splits, sp = rem - (rem / a.splits) * a.splits;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int hg = wave >> 1, wr = wave & 1;
+  const int l16 = lane & 15, g4 = lane >> 4;
+  const int h0 = hb * kWideHeads + hg * kHG;
+  const int seq = seq_of(a.q_seq, qi, a.seq_ident);
+  const int j0 = sp * a.rows_per_split;
+  const int j1 = min(j0 + a.rows_per_split, a.k);
+  const int nsteps = (j1 - j0 + kWideStep - 1) / kWideStep;
+
+  // gather role: row gr of a step, chunks gq + 8 i (i < 9), 128 contiguous bytes per load
+  const int gr = tid >> 3, gq = tid & 7;
+  u32x4 v[kWidePer];
+  bool v_ok;
+  auto load_rows = [&](int step) {
+    const int j = j0 + step * kWideStep + gr;
+    const int raw = a.indices[(int64_t)qi * a.k + (j < a.k ? j : a.k - 1)];
+    const int t = j < j1 ? raw : -1;
+    v_ok = t >= 0;
+    int slot;
+    const int64_t blk = cache_block(a.latent, seq, v_ok ? t : 0, slot);
+    const uint8_t *src = (v_ok ? cache_row(a.latent, blk, slot) : a.latent.rows) + 16 * gq;
+#pragma unroll
+    for (int i = 0; i < kWidePer; ++i) v[i] = load16(src + 128 * i);
+  };
+  load_rows(0);
+
+  // q operand (head h0 + l16, dims 32 ks + 8 g4 + [0, 8))
+  bf16x8 qa[kW / 32];
+  {
+    const uint16_t *qr = a.q + ((int64_t)qi * H + h0 + l16) * kW + 8 * g4;
+#pragma unroll
+    for (int ks = 0; ks < kW / 32; ++ks) qa[ks] = as_bf16x8(load16(qr + 32 * ks));
+  }
+
+  float m_run[4], l_run[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    m_run[i] = -INFINITY;
+    l_run[i] = 0.0f;
+  }
+  constexpr int NT = kL / 2 / 16;   // 16 value-column tiles per wavefront
+  f32x4 o[NT];
+#pragma unroll
+  for (int nt = 0; nt < NT; ++nt) o[nt] = f32x4{0, 0, 0, 0};
+  uint16_t *my_p = lp[hg][0];
+
+  for (int step = 0; step < nsteps; ++step) {
+    {
+      uint8_t *dst = rows + gr * kRowBytes + 16 * gq;
+#pragma unroll
+      for (int i = 0; i < kWidePer; ++i) *reinterpret_cast<u32x4 *>(dst + 128 * i) = v[i];
+      if (gq == 0) lvalid[gr] = v_ok ? 1 : 0;
+    }
+    __syncthreads();
+    load_rows(step + 1);   // past the split's end: empty slots (the cache's first row, unused)
+
+    // QK^T: 16 heads x rows 32 wr + 16 nt + l16
+    float z[2][4];
+#pragma unroll
+    for (int nt = 0; nt < 2; ++nt) {
+      const int row = 32 * wr + 16 * nt + l16;
+      const uint8_t *rp = rows + row * kRowBytes + 16 * g4;
+      f32x4 sacc = {0, 0, 0, 0};
+#pragma unroll
+      for (int ks = 0; ks < kW / 32; ++ks)
+        sacc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+            qa[ks], as_bf16x8(*reinterpret_cast<const u32x4 *>(rp + 64 * ks)), sacc, 0, 0, 0);
+      const bool valid = lvalid[row] != 0;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) z[nt][i] = valid ? sacc[i] * a.scale_log2 : -INFINITY;
+    }
+    float mx[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) mx[i] = row16_max(fmaxf(z[0][i], z[1][i]));
+    if (l16 == 0)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) red[hg][0][wr][4 * g4 + i] = mx[i];
+    __syncthreads();
+
+    float alpha[4], ps[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int h = 4 * g4 + i;
+      const float tm = fmaxf(red[hg][0][0][h], red[hg][0][1][h]);
+      const float m_new = fmaxf(m_run[i], tm);
+      const float mu = m_new == -INFINITY ? 0.0f : m_new;
+      alpha[i] = exp2f(m_run[i] - mu);
+      float pr[2];
+#pragma unroll
+      for (int nt = 0; nt < 2; ++nt) {
+        const int row = 32 * wr + 16 * nt + l16;
+        const float p = exp2f(z[nt][i] - mu);
+        const uint16_t hi = float_to_bf16_bits(p);
+        const uint16_t lo = float_to_bf16_bits(p - bf16_bits_to_float(hi));
+        my_p[h * kWideStep + row] = hi;
+        my_p[kHG * kWideStep + h * kWideStep + row] = lo;
+        pr[nt] = p;
+      }
+      ps[i] = row16_sum(pr[0]) + row16_sum(pr[1]);
+      m_run[i] = m_new;
+    }
+    if (l16 == 0)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) red[hg][1][wr][4 * g4 + i] = ps[i];
+    __syncthreads();
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int h = 4 * g4 + i;
+      l_run[i] = l_run[i] * alpha[i] + (red[hg][1][0][h] + red[hg][1][1][h]);
+    }
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) o[nt][i] *= alpha[i];
+
+    // PV: rows 32 ks2 + 8 g4 + e, columns 256 wr + 16 nt + l16; the V operand
+    // comes from two transposed LDS reads of 4 rows each
+#pragma unroll
+    for (int ks2 = 0; ks2 < kWideStep / 32; ++ks2) {
+      const bf16x8 ahi = as_bf16x8(*reinterpret_cast<const u32x4 *>(&my_p[l16 * kWideStep + 32 * ks2 + 8 * g4]));
+      const bf16x8 alo = as_bf16x8(
+          *reinterpret_cast<const u32x4 *>(&my_p[kHG * kWideStep + l16 * kWideStep + 32 * ks2 + 8 * g4]));
+      const uint8_t *vb = rows + (32 * ks2 + 8 * g4 + (l16 >> 2)) * kRowBytes + (256 * wr + 4 * (l16 & 3)) * 2;
+#pragma unroll
+      for (int nt = 0; nt < NT; ++nt) {
+        const i16x4 v0 = lds_read_tr(vb + 32 * nt);
+        const i16x4 v1 = lds_read_tr(vb + 4 * kRowBytes + 32 * nt);
+        const bf16x8 b = __builtin_bit_cast(
+            bf16x8, (__attribute__((__vector_size__(8 * sizeof(short)))) short){v0[0], v0[1], v0[2], v0[3], v1[0],
+                                                                                 v1[1], v1[2], v1[3]});
+        o[nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ahi, b, o[nt], 0, 0, 0);
+        o[nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(alo, b, o[nt], 0, 0, 0);
+      }
+    }
+    __syncthreads();
+  }
+
+  // epilogue: lane holds heads h0 + 4 g4 + i, columns 256 wr + 16 nt + l16
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int head = h0 + 4 * g4 + i;
+    if (!SPLIT) {
+      const float inv = l_run[i] > 0.0f ? 1.0f / l_run[i] : 0.0f;
+      float *orow = a.out + ((int64_t)qi * H + head) * kL + 256 * wr + l16;
+#pragma unroll
+      for (int nt = 0; nt < NT; ++nt) orow[16 * nt] = o[nt][i] * inv;
+      if (wr == 0 && l16 == 0 && a.lse)
+        a.lse[(int64_t)qi * H + head] = l_run[i] > 0.0f ? (m_run[i] + log2f(l_run[i])) * kLn2 : -INFINITY;
+    } else {
+      const int64_t base = ((int64_t)(qi * a.splits + sp) * H + head);
+      float *orow = a.part_o + base * kL + 256 * wr + l16;
+#pragma unroll
+      for (int nt = 0; nt < NT; ++nt) orow[16 * nt] = o[nt][i];
+      if (wr == 0 && l16 == 0) {
+        a.part_ml[base * 2 + 0] = m_run[i];
+        a.part_ml[base * 2 + 1] = l_run[i];
+      }
+    }
+  }
+}
+
 // Combine split partials in split order.  One workgroup per (query, head), one
 // thread per 4 output columns.  Every thread issues all of its loads at once
 // (the splits' (max, sum) pairs and its 4 columns of every split; padding
@@ -423,8 +612,21 @@ AttendPlan plan_attend(int n_q, int n_heads, int kv_lora, int width, int k, int 
   p.width = width;
   p.k = k;
   p.splits = 1;
+  p.wide = 0;
   p.rows_per_split = (k + kStepRows - 1) / kStepRows * kStepRows;
-  if (dtype == kBF16 && n_heads >= kHG) {
+  if (dtype == kBF16 && n_heads % kWideHeads == 0 && n_q * (n_heads / kWideHeads) >= kWideMinRows) {
+    // one workgroup per (query, 64 heads, split): ~256 workgroups, whole 64-row steps
+    p.wide = 1;
+    const int n_hb = n_heads / kWideHeads;
+    const int steps = (k + kWideStep - 1) / kWideStep;
+    int s = (kAttTargetWGs + n_q * n_hb - 1) / (n_q * n_hb);
+    if (s > steps) s = steps;
+    if (s > kMaxSplits) s = kMaxSplits;
+    if (s < 1) s = 1;
+    const int sps = (steps + s - 1) / s;
+    p.rows_per_split = sps * kWideStep;
+    p.splits = (steps + sps - 1) / sps;
+  } else if (dtype == kBF16 && n_heads >= kHG) {
     const int n_hg = n_heads / kHG;
     const int steps = (k + kStepRows - 1) / kStepRows;
     // ~256 workgroups; each split is a whole number of 128-row steps
@@ -478,10 +680,12 @@ hipError_t launch_attend(float *out, float *lse, const void *q, int dt, const Ca
   uint8_t *ws = static_cast<uint8_t *>(workspace);
   const int groups = (a.pairs + 7) / 8;
   const dim3 grid(groups * 8 * a.n_hg);
+  const dim3 wide_grid(n_q * (n_heads / kWideHeads) * plan.splits);
   if (plan.splits > 1) {
     a.part_o = reinterpret_cast<float *>(ws + plan.off_part_o);
     a.part_ml = reinterpret_cast<float *>(ws + plan.off_part_ml);
-    hipLaunchKernelGGL(attend_bf16_kernel<true>, grid, dim3(kAttThreads), 0, stream, a);
+    if (plan.wide) hipLaunchKernelGGL(attend_wide_kernel<true>, wide_grid, dim3(kWideThreads), 0, stream, a);
+    else hipLaunchKernelGGL(attend_bf16_kernel<true>, grid, dim3(kAttThreads), 0, stream, a);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
 #define DSA_MERGE(NS)                                                                                         \
@@ -492,6 +696,8 @@ hipError_t launch_attend(float *out, float *lse, const void *q, int dt, const Ca
     else if (plan.splits <= 24) DSA_MERGE(24);
     else DSA_MERGE(32);
 #undef DSA_MERGE
+  } else if (plan.wide) {
+    hipLaunchKernelGGL(attend_wide_kernel<false>, wide_grid, dim3(kWideThreads), 0, stream, a);
   } else {
     hipLaunchKernelGGL(attend_bf16_kernel<false>, grid, dim3(kAttThreads), 0, stream, a);
   }

@@ -34,6 +34,10 @@ CASES = {
     "bf16_peaky_q": (S(inputs.DECODE_8K, name="a4", wid=304, batch=2, seq_len=(3000, 3000), q_mla_sigma=20.0), 2048),
     "bf16_one_query_many_splits": (S(inputs.DECODE_8K, name="a5", wid=305, batch=1, seq_len=(8192, 8192)), 2048),
     "bf16_many_queries": (S(inputs.PREFILL_64K, name="a6", wid=306, seq_len=(2500, 2500), prefill_queries=300), 256),
+    # >= 16 (query, 64-head block) pairs: one workgroup per query and 64 heads, split and unsplit
+    "bf16_wide_split": (S(inputs.DECODE_8K, name="a8", wid=308, batch=20, seq_len=(1000, 5000)), 2048),
+    "bf16_wide_h128": (S(inputs.DECODE_8K, name="a9", wid=309, batch=8, seq_len=(3000, 3000), mla_heads=128), 2048),
+    "bf16_wide_short_rows": (S(inputs.PAGED_DECODE, name="a10", wid=310, batch=16, seq_len=(1, 300)), 2048),
     "f32_tiny": (inputs.TINY_FP32, 256),
     "f32_h3_w44": (S(inputs.TINY_FP32, name="a7", wid=307, batch=3, seq_len=(10, 900), mla_heads=3, kv_lora=40,
                      rope=4), 300),
