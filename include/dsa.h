@@ -201,6 +201,37 @@ dsa_status dsa_decode_window(float *out, float *lse, const void *q_idx, dsa_dtyp
 size_t dsa_decode_window_workspace_size(int32_t batch, int32_t window, int32_t max_len, int32_t k,
                                         int32_t mla_heads, int32_t kv_lora);
 
+/*
+ * Cache append: write new tokens into the key and latent caches, the step that
+ * must precede any query that sees them ("GLM on an A100, in Vx", section "The
+ * model": a query scores every earlier token, its own included).  Token i of
+ * the call belongs to sequence seq ? seq[i] : 0 and goes to position pos[i] of
+ * that sequence, addressed exactly as the dsa_cache comment describes (the
+ * block of a paged cache must already be in the block table).
+ *   - keys (NULL: keys untouched), new_keys [n_new][keys->width]:
+ *       fp8 cache (the FP8 format of "INT4, FP8 and BF16": E4M3 bytes with a
+ *       float32 scale), new_keys f32 or bf16: per token, in float32,
+ *           amax  = max_d |k_d|,  s = max(amax / 448, 2^-126),
+ *           byte_d = nearest e4m3fn code of k_d / s (ties to the even code,
+ *                    magnitudes >= 448 saturated to 448, sign kept),
+ *       and s is stored as the token's scale;
+ *       bf16 or f32 cache: new_keys in the cache's dtype, bits copied.
+ *   - latent (NULL: untouched), new_latent [n_new][latent->width] in the latent
+ *     cache's dtype (f32 or bf16), bits copied.
+ * The descriptors' rows and scale pointers are written through (their memory
+ * must be writable; the other entry points only read it).  Only the addressed
+ * rows and scales change.  Two tokens with the same (sequence, position) in one
+ * call leave an unspecified one of them.  Key values must be finite (otherwise
+ * the bytes and scale are unspecified).  seq, pos: device int32 [n_new],
+ * 0 <= pos[i] < the sequence's capacity (trusted).  n_new = 0 returns DSA_OK.
+ * Supported: fp8 key caches up to 128 wide; key and latent copies whose row
+ * size is a multiple of 16 bytes from 16-byte aligned inputs; fp8 latent
+ * caches are DSA_ERR_UNSUPPORTED.
+ */
+dsa_status dsa_cache_append(const dsa_cache *keys, const void *new_keys, dsa_dtype new_keys_dtype,
+                            const dsa_cache *latent, const void *new_latent, const int32_t *seq,
+                            const int32_t *pos, int32_t n_new, void *stream);
+
 /* Zero-fill a workspace on `stream` with a fill kernel (no hipMemset node, so it
  * may be captured in a graph).  bytes must be a multiple of 4. */
 dsa_status dsa_workspace_clear(void *workspace, size_t bytes, void *stream);

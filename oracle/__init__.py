@@ -12,6 +12,8 @@ Functions (each cites its passage in dsa_oracle.c):
   mla_attend                           sparse absorbed-MLA attention over kept rows
   mla_dense                            dense absorbed-MLA attention over all visible rows
   decode_step                          scores -> top-k -> attention for a decode batch
+  e4m3fn_quantize, key_scale           fp8 encoding and the per-token key scale (float32 decisions)
+  cache_append                         new tokens' keys (fp8-quantized or copied) and latent rows into caches
 """
 from __future__ import annotations
 
@@ -68,6 +70,12 @@ def _load():
     lib.oracle_decode_step.argtypes = [P, P, P, i64, P, P, ctypes.c_int, P, P, i32, P, ctypes.c_int, P, i32, i32,
                                        P, i32, i32, dbl]
     lib.oracle_num_threads.restype = ctypes.c_int
+    lib.oracle_e4m3fn_quantize.restype = ctypes.c_uint8
+    lib.oracle_e4m3fn_quantize.argtypes = [ctypes.c_float]
+    lib.oracle_key_scale.restype = ctypes.c_float
+    lib.oracle_key_scale.argtypes = [P, ctypes.c_int]
+    lib.oracle_cache_append.restype = None
+    lib.oracle_cache_append.argtypes = [P, P, ctypes.c_int, P, P, P, P, i32]
     _lib = lib
     return lib
 
@@ -187,3 +195,57 @@ def decode_step(p):
                            _ptr(w), ctypes.byref(ks), p.idx_heads, _ptr(q_mla), _DT[p.q_mla_dtype], ctypes.byref(ls),
                            p.kv_lora, p.mla_heads, _ptr(seq_len), B, p.topk, float(p.softmax_scale))
     return {"out": out, "lse": lse, "scores": scores, "indices": idx}
+
+
+def e4m3fn_quantize(x) -> np.ndarray:
+    """uint8 e4m3fn codes of float32 values (same shape): nearest, ties to even, saturating."""
+    lib = _load()
+    a = _c(x, np.float32)
+    flat = a.reshape(-1)
+    out = np.empty(flat.shape, dtype=np.uint8)
+    for i in range(flat.size):
+        out[i] = lib.oracle_e4m3fn_quantize(ctypes.c_float(float(flat[i])))
+    return out.reshape(a.shape)
+
+
+def key_scale(row) -> np.float32:
+    """float32 per-token scale of one key row given as float32 values."""
+    r = _c(row, np.float32)
+    return np.float32(_load().oracle_key_scale(_ptr(r), int(r.size)))
+
+
+def _copy_cache(cache):
+    import copy
+    out = copy.copy(cache)
+    out.storage = np.array(cache.storage, copy=True)
+    if cache.scale is not None:
+        out.scale = np.array(cache.scale, copy=True)
+    return out
+
+
+def cache_append(keys, new_keys, new_keys_dtype, latent, new_latent, seq, pos):
+    """Append tokens to copies of the given inputs.Cache objects (either may be
+    None) and return the copies (keys, latent).  new_keys: raw bits [n, width]
+    (float32 for f32, uint16 for bf16); new_latent: raw bits [n, width] in the
+    latent cache's dtype; seq (or None: all sequence 0) and pos: int32 [n]."""
+    lib = _load()
+    pos = _c(pos, np.int32)
+    n = int(pos.shape[0])
+    seq = None if seq is None else _c(seq, np.int32)
+    k2 = None if keys is None else _copy_cache(keys)
+    l2 = None if latent is None else _copy_cache(latent)
+    nk = None if new_keys is None else np.ascontiguousarray(new_keys)
+    nl = None if new_latent is None else np.ascontiguousarray(new_latent)
+    ks = ls = None
+    keep = []
+    if k2 is not None:
+        ks, kk = _cache_struct(k2)
+        keep.append(kk)
+        assert kk[0] is k2.storage and (k2.scale is None or kk[1] is k2.scale)
+    if l2 is not None:
+        ls, kl = _cache_struct(l2)
+        keep.append(kl)
+        assert kl[0] is l2.storage
+    lib.oracle_cache_append(None if ks is None else ctypes.byref(ks), _ptr(nk), _DT[new_keys_dtype],
+                            None if ls is None else ctypes.byref(ls), _ptr(nl), _ptr(seq), _ptr(pos), n)
+    return k2, l2

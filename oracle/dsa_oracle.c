@@ -392,6 +392,109 @@ void oracle_decode_step(double *out, double *lse, double *scores_out, int64_t ld
   free(seq);
 }
 
+/* ----------------------------------------------------------- cache append -- */
+
+/* e4m3fn encoding of a float32 value, for writing keys into an fp8 cache
+ * ([GLM-A100] "INT4, FP8 and BF16": FP8 is E4M3 bytes with a float32 scale;
+ * [glm-vx] component list: E4M3FN).  The pages only decode; the reading taken
+ * for encoding is round to nearest with ties to the even code, magnitudes at or
+ * above the largest finite value (448) saturated to it, and the sign bit of x
+ * kept (negative values that round to zero give 0x80).  The code is found by a
+ * plain search: the largest non-negative finite code whose decoded value does
+ * not exceed |x|, then a comparison with the midpoint to the next code (the
+ * midpoint of two neighbouring e4m3fn values is exact in double).  Finite
+ * inputs only. */
+uint8_t oracle_e4m3fn_quantize(float x) {
+  uint32_t bits;
+  memcpy(&bits, &x, sizeof bits);
+  const uint8_t sign = (uint8_t)((bits >> 31) << 7);
+  const double m = fabs((double)x);
+  if (m >= 448.0) return (uint8_t)(sign | 0x7E);
+  int lo = 0;
+  for (int c = 1; c <= 0x7E; ++c)
+    if (oracle_e4m3fn_to_double((uint8_t)c) <= m) lo = c;
+  const double mid = 0.5 * (oracle_e4m3fn_to_double((uint8_t)lo) + oracle_e4m3fn_to_double((uint8_t)(lo + 1)));
+  int c = lo;
+  if (m > mid || (m == mid && (lo & 1))) c = lo + 1;
+  return (uint8_t)(sign | c);
+}
+
+/* Per-token scale of an fp8 key row (reading: the pages give E4M3 with float32
+ * scales but no rule for choosing them).  The row's largest magnitude maps to
+ * the largest finite code: s = amax / 448, floored at the smallest normal
+ * float (2^-126) so an all-zero row gets a usable positive scale.  Computed in
+ * float32, the precision the encoded byte is decided in. */
+float oracle_key_scale(const float *k, int n) {
+  float amax = 0.0f;
+  for (int d = 0; d < n; ++d) {
+    const float a = fabsf(k[d]);
+    if (a > amax) amax = a;
+  }
+  float s = amax / 448.0f;
+  const float floor_s = 0x1p-126f;
+  return s < floor_s ? floor_s : s;
+}
+
+static float input_to_float(const void *src, int64_t i, int dtype) {
+  if (dtype == ORACLE_BF16) {
+    uint16_t b;
+    memcpy(&b, (const uint8_t *)src + i * 2, 2);
+    uint32_t u = (uint32_t)b << 16;
+    float f;
+    memcpy(&f, &u, 4);
+    return f;
+  }
+  float f;
+  memcpy(&f, (const uint8_t *)src + i * 4, 4);
+  return f;
+}
+
+/* Write new tokens into the caches (the step before the path: a token's key
+ * and latent row must be in place before a query sees it, [GLM-A100] "The
+ * model": every earlier token is scored, the query's own included).  Token i
+ * (sequence seq ? seq[i] : 0, position pos[i]):
+ *   - keys (may be NULL): fp8 cache: s = oracle_key_scale(row), byte d =
+ *     oracle_e4m3fn_quantize(k[d] / s) with the division in float32, scale s;
+ *     bf16 or f32 cache: the input bits copied (same dtype).
+ *   - latent (may be NULL): the input row's bits copied (same dtype).
+ * new_keys: [n_new][keys->width] in new_keys_dtype (f32 or bf16);
+ * new_latent: [n_new][latent->width] in the latent cache's dtype. */
+void oracle_cache_append(const oracle_cache *keys, const void *new_keys, int new_keys_dtype,
+                         const oracle_cache *latent, const void *new_latent, const int32_t *seq,
+                         const int32_t *pos, int32_t n_new) {
+  for (int32_t i = 0; i < n_new; ++i) {
+    const int32_t b = seq ? seq[i] : 0;
+    const int64_t t = pos[i];
+    if (keys) {
+      const int D = keys->width;
+      const int64_t block = keys->block_table
+          ? (int64_t)keys->block_table[(int64_t)b * keys->max_blocks + t / keys->block_size] : (int64_t)b;
+      const int64_t slot = t % keys->block_size;
+      uint8_t *row = (uint8_t *)keys->rows + block * keys->block_stride + slot * keys->row_stride;
+      if (keys->dtype == ORACLE_E4M3FN) {
+        float *k = (float *)malloc(sizeof(float) * (size_t)D);
+        for (int d = 0; d < D; ++d) k[d] = input_to_float(new_keys, (int64_t)i * D + d, new_keys_dtype);
+        const float s = oracle_key_scale(k, D);
+        for (int d = 0; d < D; ++d) row[d] = oracle_e4m3fn_quantize(k[d] / s);
+        ((float *)keys->scale)[block * keys->scale_block_stride + slot] = s;
+        free(k);
+      } else {
+        const int eb = elem_bytes(keys->dtype);
+        memcpy(row, (const uint8_t *)new_keys + (int64_t)i * D * eb, (size_t)D * eb);
+      }
+    }
+    if (latent) {
+      const int W = latent->width;
+      const int eb = elem_bytes(latent->dtype);
+      const int64_t block = latent->block_table
+          ? (int64_t)latent->block_table[(int64_t)b * latent->max_blocks + t / latent->block_size] : (int64_t)b;
+      const int64_t slot = t % latent->block_size;
+      uint8_t *row = (uint8_t *)latent->rows + block * latent->block_stride + slot * latent->row_stride;
+      memcpy(row, (const uint8_t *)new_latent + (int64_t)i * W * eb, (size_t)W * eb);
+    }
+  }
+}
+
 int oracle_num_threads(void) {
 #ifdef _OPENMP
   return omp_get_max_threads();

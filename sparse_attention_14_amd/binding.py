@@ -46,7 +46,7 @@ class DsaCache(ctypes.Structure):
 _lib = None
 EXPORTS = ("dsa_index_scores", "dsa_topk", "dsa_topk_workspace_size", "mla_sparse_attend",
            "mla_sparse_attend_workspace_size", "dsa_decode_step", "dsa_decode_step_workspace_size",
-           "dsa_decode_window", "dsa_decode_window_workspace_size",
+           "dsa_decode_window", "dsa_decode_window_workspace_size", "dsa_cache_append",
            "dsa_workspace_clear", "dsa_status_string")
 
 
@@ -73,6 +73,7 @@ def load(path: str = LIB_PATH):
         "dsa_decode_window": (ctypes.c_int, [P, P, P, ctypes.c_int, P, CP, i32, P, ctypes.c_int, CP, i32, i32, P,
                                              i32, i32, i32, i32, f32, P, P, P, sz, P]),
         "dsa_decode_window_workspace_size": (sz, [i32, i32, i32, i32, i32, i32]),
+        "dsa_cache_append": (ctypes.c_int, [CP, P, ctypes.c_int, CP, P, P, P, i32, P]),
         "dsa_workspace_clear": (ctypes.c_int, [P, sz, P]),
         "dsa_status_string": (ctypes.c_char_p, [ctypes.c_int]),
     }
@@ -182,6 +183,18 @@ def dsa_decode_window(out, lse, q_idx, q_idx_dtype, w_idx, keys: DeviceCache, q_
         _p(q_mla), DTYPES[q_mla_dtype], ctypes.byref(latent.desc), kv_lora, q_mla.shape[1], _p(seq_len),
         seq_len.shape[0], window, max_len, k, float(softmax_scale), _p(scores_out), _p(indices_out),
         _p(workspace), ws_bytes, _stream(stream)))
+
+
+def dsa_cache_append(keys: Optional[DeviceCache], new_keys, new_keys_dtype, latent: Optional[DeviceCache],
+                     new_latent, pos, seq=None, stream=None):
+    """Write new tokens (rows of new_keys / new_latent) at positions pos of
+    sequences seq into the caches (see include/dsa.h); either cache may be None."""
+    lib = load()
+    n = pos.shape[0]
+    _check("dsa_cache_append", lib.dsa_cache_append(
+        None if keys is None else ctypes.byref(keys.desc), _p(new_keys), DTYPES[new_keys_dtype],
+        None if latent is None else ctypes.byref(latent.desc), _p(new_latent), _p(seq), _p(pos), n,
+        _stream(stream)))
 
 
 def dsa_workspace_clear(workspace, stream=None):

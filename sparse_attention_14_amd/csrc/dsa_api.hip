@@ -311,4 +311,41 @@ dsa_status dsa_decode_window(float *out, float *lse, const void *q_idx, dsa_dtyp
                      workspace, workspace_bytes, stream);
 }
 
+dsa_status dsa_cache_append(const dsa_cache *keys, const void *new_keys, dsa_dtype new_keys_dtype,
+                            const dsa_cache *latent, const void *new_latent, const int32_t *seq,
+                            const int32_t *pos, int32_t n_new, void *stream) {
+  if (n_new < 0 || !pos || (!keys && !latent)) return DSA_ERR_INVALID_ARGUMENT;
+  CacheDev kd{}, ld{};
+  int key_bytes_in = 0;
+  if (keys) {
+    dsa_status s = check_cache(keys);
+    if (s != DSA_OK) return s;
+    if (!new_keys || !valid_dtype(new_keys_dtype)) return DSA_ERR_INVALID_ARGUMENT;
+    if (keys->dtype == DSA_FP8_E4M3FN) {
+      if (new_keys_dtype != DSA_F32 && new_keys_dtype != DSA_BF16) return DSA_ERR_UNSUPPORTED;
+      if (keys->width > 128) return DSA_ERR_UNSUPPORTED;
+      key_bytes_in = elem_bytes(new_keys_dtype);
+      if (reinterpret_cast<uintptr_t>(new_keys) % key_bytes_in) return DSA_ERR_UNSUPPORTED;
+    } else {
+      if (new_keys_dtype != keys->dtype) return DSA_ERR_UNSUPPORTED;
+      if (((int64_t)keys->width * elem_bytes(keys->dtype)) % 16 || !aligned16(new_keys)) return DSA_ERR_UNSUPPORTED;
+    }
+    kd = to_dev(keys);
+  }
+  int latent_row_bytes = 0;
+  if (latent) {
+    dsa_status s = check_cache(latent);
+    if (s != DSA_OK) return s;
+    if (!new_latent) return DSA_ERR_INVALID_ARGUMENT;
+    if (latent->dtype == DSA_FP8_E4M3FN) return DSA_ERR_UNSUPPORTED;
+    latent_row_bytes = latent->width * elem_bytes(latent->dtype);
+    if (latent_row_bytes % 16 || !aligned16(new_latent)) return DSA_ERR_UNSUPPORTED;
+    ld = to_dev(latent);
+  }
+  if (n_new == 0) return DSA_OK;
+  return from_hip(launch_cache_append(keys ? &kd : nullptr, keys ? (int)keys->dtype : -1, new_keys,
+                                      (int)new_keys_dtype, latent ? &ld : nullptr, latent_row_bytes, new_latent,
+                                      seq, pos, n_new, static_cast<hipStream_t>(stream)));
+}
+
 }  // extern "C"

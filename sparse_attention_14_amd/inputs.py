@@ -29,7 +29,7 @@ _NAN_BITS = {"f32": 0x7FC00000, "bf16": 0x7FC0, "e4m3fn": 0x7F}
 
 _TAGS = {
     "q_idx": 1, "w_idx": 2, "keys": 3, "key_scale": 4, "q_mla": 5, "latent": 6,
-    "lens": 7, "block_perm": 8, "ties": 9, "ties_src": 10,
+    "lens": 7, "block_perm": 8, "ties": 9, "ties_src": 10, "append_keys": 11, "append_latent": 12,
 }
 
 
@@ -420,3 +420,29 @@ def cache_from_values(values, dtype: str, scale=None, paged_block: int = 0, seed
             if sc is not None:
                 sc[p, :t1 - t0] = np.asarray(scale, dtype=np.float32)[b, t0:t1]
     return Cache(storage=storage, dtype=dtype, width=width, block_size=bs, block_table=table, scale=sc)
+
+
+def append_tokens(p: Problem, window: int = 1, key_dtype: str = "bf16"):
+    """New tokens to write into a decode problem's caches at the last `window`
+    positions of each sequence (positions below 0 skipped).
+
+    Returns (new_keys, new_latent, seq, pos): new_keys [n, idx_dim] raw bits in
+    key_dtype ("bf16" -> uint16, "f32" -> float32) drawn N(0, key_sigma);
+    new_latent [n, kv_lora + rope] raw bits in the latent dtype drawn
+    N(0, latent_sigma); seq, pos int32 [n]."""
+    wl = p.meta["workload"]
+    lens = np.asarray(p.meta["seq_lens"], dtype=np.int64)
+    seq, pos = [], []
+    for b, n in enumerate(lens):
+        for j in range(window):
+            t = int(n) - window + j
+            if t >= 0:
+                seq.append(b)
+                pos.append(t)
+    m = len(pos)
+    wid = wl.wid * 1000 + window
+    nk = rng_for(wid, "append_keys").standard_normal((m, wl.idx_dim), dtype=np.float32) * np.float32(wl.key_sigma)
+    W = wl.kv_lora + wl.rope
+    nl = rng_for(wid, "append_latent").standard_normal((m, W), dtype=np.float32) * np.float32(wl.latent_sigma)
+    return (encode(nk, key_dtype), encode(nl, wl.latent_dtype), np.array(seq, dtype=np.int32),
+            np.array(pos, dtype=np.int32))

@@ -1,0 +1,153 @@
+"""Pins for the oracle's cache append: the e4m3fn encoder, the per-token key
+scale and the placement of new tokens in contiguous and paged caches.
+
+The pages give FP8 as E4M3 bytes with float32 scales ("GLM on an A100, in Vx",
+section "INT4, FP8 and BF16"; "Self-contained GLM-5 serving stack", component
+list: E4M3FN) and say every earlier token is scored, the query's own included
+("GLM on an A100, in Vx", "The model"), so a token's row must be written before
+its query runs.  Encoding rule (nearest, ties to even, saturating at 448) and
+the scale rule (amax / 448, floored at 2^-126) are readings; they are pinned
+here against the decoder (itself pinned against torch's cast), torch's own
+float8 cast, closed forms and the format's error bound."""
+import numpy as np
+import pytest
+import torch
+
+from sparse_attention_14_amd import inputs
+
+
+def _finite_codes():
+    return [c for c in range(256) if c not in (0x7F, 0xFF)]
+
+
+def test_quantize_round_trips_every_finite_code(oracle_mod):
+    codes = np.array(_finite_codes(), dtype=np.uint8)
+    vals = np.array([oracle_mod.e4m3fn_to_double(int(c)) for c in codes], dtype=np.float32)
+    assert np.array_equal(oracle_mod.e4m3fn_quantize(vals), codes)
+
+
+def test_quantize_midpoints_go_to_the_even_code(oracle_mod):
+    for c in range(0, 0x7E):
+        lo, hi = oracle_mod.e4m3fn_to_double(c), oracle_mod.e4m3fn_to_double(c + 1)
+        mid = np.float32((lo + hi) / 2)
+        assert float(mid) == (lo + hi) / 2                    # exact in float32
+        even = c if c % 2 == 0 else c + 1
+        below = np.nextafter(mid, np.float32(0))
+        above = np.nextafter(mid, np.float32(np.inf))
+        got = oracle_mod.e4m3fn_quantize(np.array([mid, below, above, -mid], dtype=np.float32))
+        assert list(got) == [even, c, c + 1, 0x80 | even], (c, got)
+
+
+def test_quantize_matches_torch_cast_in_range(oracle_mod):
+    rng = np.random.default_rng(5)
+    x = np.concatenate([
+        rng.uniform(-464, 464, 4000), rng.normal(0, 1, 4000), rng.normal(0, 2.0 ** -7, 2000),
+        rng.normal(0, 2.0 ** -11, 1000)]).astype(np.float32)
+    ref = torch.from_numpy(x).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    assert np.array_equal(oracle_mod.e4m3fn_quantize(x), ref)
+
+
+def test_quantize_saturates_and_keeps_sign(oracle_mod):
+    x = np.array([448, 463.99, 464, 470, 1e6, 3e38, -449, -1e6, 0.0, -0.0, 1e-30, -1e-30], dtype=np.float32)
+    got = list(oracle_mod.e4m3fn_quantize(x))
+    assert got == [0x7E, 0x7E, 0x7E, 0x7E, 0x7E, 0x7E, 0xFE, 0xFE, 0x00, 0x80, 0x00, 0x80]
+
+
+def test_key_scale_closed_forms(oracle_mod):
+    row = np.array([0.5, -3.25, 2.0, 0.0], dtype=np.float32)
+    assert oracle_mod.key_scale(row) == np.float32(3.25) / np.float32(448)
+    assert oracle_mod.key_scale(np.zeros(128, np.float32)) == np.float32(2.0 ** -126)
+    tiny = np.full(8, 1e-40, dtype=np.float32)                # subnormal float32 values
+    assert oracle_mod.key_scale(tiny) == np.float32(2.0 ** -126)
+    # the scale follows the largest magnitude, whatever its sign or position
+    for pos in (0, 63, 127):
+        r = np.zeros(128, np.float32)
+        r[pos] = -7.0
+        assert oracle_mod.key_scale(r) == np.float32(7.0) / np.float32(448)
+
+
+def _append_case(dtype_in, paged, B=3, n=70, W=1, seed=0):
+    rng = np.random.default_rng(seed)
+    lens = np.array([n, n - 5, n - 30])[:B]
+    kv = rng.normal(0, 1, (B, n, 128)).astype(np.float32)
+    keys = inputs.cache_from_values(kv, "e4m3fn", scale=rng.uniform(0.5, 2, (B, n)).astype(np.float32),
+                                    paged_block=64 if paged else 0, seed=seed, capacity_pad=0 if paged else 8)
+    lat = inputs.cache_from_values(rng.normal(0, 0.05, (B, n, 576)).astype(np.float32), "bf16",
+                                   paged_block=64 if paged else 0, seed=seed + 1, capacity_pad=0 if paged else 8)
+    seq = np.repeat(np.arange(B, dtype=np.int32), W)
+    pos = np.concatenate([lens[b] - W + np.arange(W) for b in range(B)]).astype(np.int32)
+    nk = rng.normal(0, 1, (B * W, 128)).astype(np.float32)
+    nk[0, :5] = 0.0
+    nk[-1] *= 1e-3
+    raw = inputs.encode(nk, dtype_in)
+    nl = inputs.encode(rng.normal(0, 0.05, (B * W, 576)).astype(np.float32), "bf16")
+    return keys, lat, raw, nl, seq, pos
+
+
+@pytest.mark.parametrize("dtype_in", ["bf16", "f32"])
+@pytest.mark.parametrize("paged", [False, True])
+def test_cache_append_writes_only_the_new_rows(oracle_mod, dtype_in, paged):
+    keys, lat, raw, nl, seq, pos = _append_case(dtype_in, paged, W=2)
+    k2, l2 = oracle_mod.cache_append(keys, raw, dtype_in, lat, nl, seq, pos)
+    vals = (raw.astype(np.uint32) << 16).view(np.float32) if dtype_in == "bf16" else raw
+    touched_k = np.zeros(keys.storage.shape[:2], bool)
+    for i, (b, t) in enumerate(zip(seq, pos)):
+        p, s = inputs.token_location(keys, int(b), int(t))
+        touched_k[p, s] = True
+        sc = k2.scale[p, s]
+        assert sc == np.float32(np.abs(vals[i]).max()) / np.float32(448) or sc == np.float32(2.0 ** -126)
+        # each byte decodes to within half an e4m3fn step of value / scale
+        dec = np.array([oracle_mod.e4m3fn_to_double(int(c)) for c in k2.storage[p, s]])
+        x = (vals[i] / sc).astype(np.float64)
+        step = np.where(np.abs(x) >= 2.0 ** -6, 2.0 ** (np.floor(np.log2(np.maximum(np.abs(x), 1e-300))) - 3),
+                        2.0 ** -9)
+        assert np.all(np.abs(dec - x) <= step / 2 * (1 + 1e-12))
+        assert np.abs(dec).max() == 448.0                 # the largest magnitude maps to the largest code
+        pl, sl = inputs.token_location(lat, int(b), int(t))
+        assert np.array_equal(l2.storage[pl, sl].view(np.uint16), nl[i])
+    # nothing else changed (NaN-poisoned rows compared bytewise)
+    assert np.array_equal(k2.storage[~touched_k], keys.storage[~touched_k])
+    assert np.array_equal(k2.scale[~touched_k].view(np.uint32), keys.scale[~touched_k].view(np.uint32))
+    touched_l = np.zeros(lat.storage.shape[:2], bool)
+    for b, t in zip(seq, pos):
+        touched_l[inputs.token_location(lat, int(b), int(t))] = True
+    assert np.array_equal(l2.storage[~touched_l], lat.storage[~touched_l])
+    # the inputs were not modified
+    k3, _ = oracle_mod.cache_append(keys, raw, dtype_in, None, None, seq, pos)
+    assert np.array_equal(k3.storage, k2.storage)
+
+
+def test_cache_append_bf16_keys_are_copied(oracle_mod):
+    rng = np.random.default_rng(3)
+    kv = rng.normal(0, 1, (2, 40, 128)).astype(np.float32)
+    keys = inputs.cache_from_values(kv, "bf16", capacity_pad=4)
+    nk = inputs.encode(rng.normal(0, 1, (2, 128)).astype(np.float32), "bf16")
+    k2, _ = oracle_mod.cache_append(keys, nk, "bf16", None, None, np.array([1, 0], np.int32),
+                                    np.array([40, 3], np.int32))
+    assert np.array_equal(k2.storage[1, 40].view(np.uint16), nk[0])
+    assert np.array_equal(k2.storage[0, 3].view(np.uint16), nk[1])
+
+
+def test_appended_fp8_keys_score_within_the_format_bound(oracle_mod):
+    """Scores over keys appended as fp8 stay within the e4m3fn error bound of
+    the scores over the exact float keys: each dequantized element is within
+    2^-4 of its value relative (normal range) or 2^-10 * scale absolute."""
+    rng = np.random.default_rng(11)
+    B, n, D, H = 2, 48, 128, 4
+    kv = rng.normal(0, 1, (B, n, D)).astype(np.float32)
+    empty = inputs.cache_from_values(np.zeros((B, n, D), np.float32), "e4m3fn",
+                                     scale=np.ones((B, n), np.float32))
+    seq = np.repeat(np.arange(B, dtype=np.int32), n)
+    pos = np.tile(np.arange(n, dtype=np.int32), B)
+    k8, _ = oracle_mod.cache_append(empty, kv.reshape(B * n, D), "f32", None, None, seq, pos)
+    exact = inputs.cache_from_values(kv, "f32")
+    q = rng.normal(0, 1, (B, H, D)).astype(np.float32)
+    w = rng.uniform(0, 1, (B, H)).astype(np.float32)
+    q_len = np.full(B, n, np.int32)
+    s8 = oracle_mod.index_scores(q, "f32", w, k8, np.arange(B, dtype=np.int32), q_len)
+    sx = oracle_mod.index_scores(q, "f32", w, exact, np.arange(B, dtype=np.int32), q_len)
+    sc = k8.scale[:, :n].astype(np.float64)                          # [B, n]
+    err = np.abs(kv) * 2.0 ** -4 + sc[..., None] * 2.0 ** -10        # per element bound
+    bound = np.einsum("bh,bhd,bnd->bn", np.abs(w).astype(np.float64), np.abs(q).astype(np.float64), err)
+    assert np.all(np.abs(s8 - sx) <= bound)
+    assert np.abs(s8 - sx).max() > 0                                 # the fp8 path really rounds
