@@ -299,6 +299,25 @@ def main():
     append = {"tokens": n_app, "keys": "bf16 -> e4m3fn + f32 scale", "latent": "bf16 copy",
               "us_per_call": round(t_app * 1e6, 3), "bytes_per_call": app_bytes}
 
+    # ----------------------- shared selection: a layer reusing the indices ---
+    # A layer that shares an earlier layer's DSA selection runs only the sparse
+    # attention over its own latent cache with those indices.
+    sidx = torch.empty(B, k, dtype=torch.int32, device="cuda")
+    dsa.dsa_decode_step(out, lse, dp.q_idx, p.q_idx_dtype, dp.w_idx, dp.keys, dp.q_mla, p.q_mla_dtype, dp.latent, L,
+                        dp.q_len, p.max_len, k, p.softmax_scale, workspaces[0], indices_out=sidx)
+    sws = torch.zeros(max(dsa.dsa_decode_shared_workspace_size(B, 1, k, H, L), 1), dtype=torch.uint8, device="cuda")
+    torch.cuda.synchronize()
+
+    def sstep(ci):
+        _, lat = copies[ci]
+        dsa.dsa_decode_shared(out, lse, dp.q_mla, p.q_mla_dtype, lat, L, sidx, B, 1, p.softmax_scale, workspace=sws)
+
+    t_sh = time_graph_steps(torch, sstep, len(copies), max(args.steps // 2, 60), max(args.warmup, 6))
+    sh_bytes = B * k * (L + p.rope) * 2 + p.q_mla.size * 2 + B * k * 4 + B * H * (L + 1) * 4
+    shared = {"workload": wl.name, "us_per_step": round(t_sh * 1e6, 2), "bytes_per_step": sh_bytes,
+              "GB_per_s": round(sh_bytes / t_sh / 1e9, 1),
+              "what": "sparse MLA over the 2048 kept rows of each of 4 queries with indices from a full layer"}
+
     # ----------------------------------------------------------- prefill ---
     prefill = None
     if not args.no_prefill:
@@ -425,7 +444,7 @@ def main():
         "decode_us_per_step": round(t_step * 1e6, 2), "decode_us_per_step_eager": round(t_eager * 1e6, 2),
         "decode_us_per_step_one_per_launch": round(t_single * 1e6, 2),
         "decode_bytes_per_step": step_bytes, "decode_hbm_frac": round(gbs / HBM_PEAK_GBS, 4),
-        "roofline": roofline, "append": append, "prefill": prefill, "window": window, "cpu_baseline": cpu, "device": dev_name,
+        "roofline": roofline, "append": append, "shared": shared, "prefill": prefill, "window": window, "cpu_baseline": cpu, "device": dev_name,
     }
     print(json.dumps(line))
 

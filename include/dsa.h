@@ -202,6 +202,32 @@ size_t dsa_decode_window_workspace_size(int32_t batch, int32_t window, int32_t m
                                         int32_t mla_heads, int32_t kv_lora);
 
 /*
+ * Decode step of a layer that shares another layer's DSA selection ("Self-
+ * contained GLM-5 serving stack", component list: full/shared DSA indexer
+ * selection).  The pages do not say which layers share; the reading taken is
+ * that a sharing layer reuses the kept token indices an earlier full layer
+ * chose for the same queries and runs only the sparse attention over its own
+ * latent cache: no indexer scores and no top-k.  Query i = b * window + j is
+ * sequence b's j-th window token (window = 1: its newest token), exactly as in
+ * dsa_decode_step / dsa_decode_window, and attends with the definition of
+ * mla_sparse_attend over the slots of indices[i][0..k) that are >= 0.
+ *   indices [batch * window][k] int32: for example the indices_out of the full
+ *           layer's step (ascending, -1 padded); any index must be below the
+ *           query's visible count (trusted).
+ *   q_mla [batch * window][mla_heads][latent->width]; out [batch * window]
+ *   [mla_heads][kv_lora]; lse [batch * window][mla_heads] (nullable).
+ * 1 <= window <= 64, batch * window <= 2^24; supported shapes as for
+ * mla_sparse_attend.  The workspace needs dsa_decode_shared_workspace_size()
+ * bytes (0: none, and workspace may then be NULL).
+ */
+dsa_status dsa_decode_shared(float *out, float *lse, const void *q_mla, dsa_dtype q_mla_dtype,
+                             const dsa_cache *latent, int32_t kv_lora, int32_t mla_heads, const int32_t *indices,
+                             int32_t batch, int32_t window, int32_t k, float softmax_scale, void *workspace,
+                             size_t workspace_bytes, void *stream);
+size_t dsa_decode_shared_workspace_size(int32_t batch, int32_t window, int32_t k, int32_t mla_heads,
+                                        int32_t kv_lora);
+
+/*
  * Cache append: write new tokens into the key and latent caches, the step that
  * must precede any query that sees them ("GLM on an A100, in Vx", section "The
  * model": a query scores every earlier token, its own included).  Token i of

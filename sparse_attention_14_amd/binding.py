@@ -46,7 +46,8 @@ class DsaCache(ctypes.Structure):
 _lib = None
 EXPORTS = ("dsa_index_scores", "dsa_topk", "dsa_topk_workspace_size", "mla_sparse_attend",
            "mla_sparse_attend_workspace_size", "dsa_decode_step", "dsa_decode_step_workspace_size",
-           "dsa_decode_window", "dsa_decode_window_workspace_size", "dsa_cache_append",
+           "dsa_decode_window", "dsa_decode_window_workspace_size", "dsa_decode_shared",
+           "dsa_decode_shared_workspace_size", "dsa_cache_append",
            "dsa_workspace_clear", "dsa_status_string")
 
 
@@ -73,6 +74,8 @@ def load(path: str = LIB_PATH):
         "dsa_decode_window": (ctypes.c_int, [P, P, P, ctypes.c_int, P, CP, i32, P, ctypes.c_int, CP, i32, i32, P,
                                              i32, i32, i32, i32, f32, P, P, P, sz, P]),
         "dsa_decode_window_workspace_size": (sz, [i32, i32, i32, i32, i32, i32]),
+        "dsa_decode_shared": (ctypes.c_int, [P, P, P, ctypes.c_int, CP, i32, i32, P, i32, i32, i32, f32, P, sz, P]),
+        "dsa_decode_shared_workspace_size": (sz, [i32, i32, i32, i32, i32]),
         "dsa_cache_append": (ctypes.c_int, [CP, P, ctypes.c_int, CP, P, P, P, i32, P]),
         "dsa_workspace_clear": (ctypes.c_int, [P, sz, P]),
         "dsa_status_string": (ctypes.c_char_p, [ctypes.c_int]),
@@ -183,6 +186,22 @@ def dsa_decode_window(out, lse, q_idx, q_idx_dtype, w_idx, keys: DeviceCache, q_
         _p(q_mla), DTYPES[q_mla_dtype], ctypes.byref(latent.desc), kv_lora, q_mla.shape[1], _p(seq_len),
         seq_len.shape[0], window, max_len, k, float(softmax_scale), _p(scores_out), _p(indices_out),
         _p(workspace), ws_bytes, _stream(stream)))
+
+
+def dsa_decode_shared_workspace_size(batch, window, k, mla_heads, kv_lora) -> int:
+    return int(load().dsa_decode_shared_workspace_size(batch, window, k, mla_heads, kv_lora))
+
+
+def dsa_decode_shared(out, lse, q_mla, q_mla_dtype, latent: DeviceCache, kv_lora, indices, batch, window,
+                      softmax_scale, workspace=None, stream=None):
+    """Sparse attention of a layer sharing another layer's kept indices
+    (rows b * window + j of q_mla / indices; see include/dsa.h)."""
+    lib = load()
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check("dsa_decode_shared", lib.dsa_decode_shared(
+        _p(out), _p(lse), _p(q_mla), DTYPES[q_mla_dtype], ctypes.byref(latent.desc), kv_lora, q_mla.shape[1],
+        _p(indices), batch, window, indices.shape[1], float(softmax_scale), _p(workspace), ws_bytes,
+        _stream(stream)))
 
 
 def dsa_cache_append(keys: Optional[DeviceCache], new_keys, new_keys_dtype, latent: Optional[DeviceCache],

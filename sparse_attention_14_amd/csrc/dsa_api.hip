@@ -311,6 +311,32 @@ dsa_status dsa_decode_window(float *out, float *lse, const void *q_idx, dsa_dtyp
                      workspace, workspace_bytes, stream);
 }
 
+size_t dsa_decode_shared_workspace_size(int32_t batch, int32_t window, int32_t k, int32_t mla_heads,
+                                        int32_t kv_lora) {
+  if (batch <= 0 || window < 1 || window > kMaxWindow || k < 1 || mla_heads <= 0 || kv_lora <= 0) return 0;
+  return round256(plan_attend(batch * window, mla_heads, kv_lora, 576, k, kBF16).total);
+}
+
+dsa_status dsa_decode_shared(float *out, float *lse, const void *q_mla, dsa_dtype q_mla_dtype,
+                             const dsa_cache *latent, int32_t kv_lora, int32_t mla_heads, const int32_t *indices,
+                             int32_t batch, int32_t window, int32_t k, float softmax_scale, void *workspace,
+                             size_t workspace_bytes, void *stream) {
+  if (batch < 0 || window < 1) return DSA_ERR_INVALID_ARGUMENT;
+  if (window > kMaxWindow) return DSA_ERR_UNSUPPORTED;
+  if (batch == 0) return DSA_OK;
+  if (!out || !indices || k < 1) return DSA_ERR_INVALID_ARGUMENT;
+  dsa_status s = check_attend(q_mla, q_mla_dtype, latent, kv_lora, mla_heads);
+  if (s != DSA_OK) return s;
+  if (k > kMaxTopk || (int64_t)batch * window > (int64_t)1 << 24) return DSA_ERR_UNSUPPORTED;
+  const int32_t n_q = batch * window;
+  // the size query assumes the bf16 plan (the larger one)
+  const size_t need = dsa_decode_shared_workspace_size(batch, window, k, mla_heads, kv_lora);
+  if (need > 0 && (!workspace || workspace_bytes < need)) return DSA_ERR_WORKSPACE_TOO_SMALL;
+  const AttendPlan p = plan_attend(n_q, mla_heads, kv_lora, latent->width, k, q_mla_dtype);
+  return from_hip(launch_attend(out, lse, q_mla, q_mla_dtype, to_dev(latent), kv_lora, indices, k, nullptr, window,
+                                n_q, mla_heads, softmax_scale, p, workspace, static_cast<hipStream_t>(stream)));
+}
+
 dsa_status dsa_cache_append(const dsa_cache *keys, const void *new_keys, dsa_dtype new_keys_dtype,
                             const dsa_cache *latent, const void *new_latent, const int32_t *seq,
                             const int32_t *pos, int32_t n_new, void *stream) {

@@ -59,8 +59,9 @@ struct AttendPlan {
   size_t off_part_o, off_part_ml, total;
 };
 AttendPlan plan_attend(int n_q, int n_heads, int kv_lora, int width, int k, int dtype);
+// Query i belongs to sequence q_seq[i], else i / seq_per (0: all sequence 0).
 hipError_t launch_attend(float *out, float *lse, const void *q, int dt, const CacheDev &latent, int kv_lora,
-                         const int32_t *indices, int k, const int32_t *q_seq, int seq_ident, int n_q, int n_heads,
+                         const int32_t *indices, int k, const int32_t *q_seq, int seq_per, int n_q, int n_heads,
                          float scale, const AttendPlan &plan, void *workspace, hipStream_t stream);
 
 hipError_t launch_fill_zero(uint32_t *p, size_t words, hipStream_t stream);

@@ -25,6 +25,12 @@
 namespace dsa {
 namespace {
 
+// Sequence of query qi: q_seq[qi], else qi / per (per queries per sequence),
+// or 0 when per is 0.
+__device__ __forceinline__ int attend_seq(const int32_t *q_seq, int qi, int per) {
+  return q_seq ? q_seq[qi] : (per > 0 ? qi / per : 0);
+}
+
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 
@@ -45,7 +51,7 @@ struct AttArgs {
   const int32_t *q_seq;
   float *part_o;   // [n_q][S][H][L]
   float *part_ml;  // [n_q][S][H][2]
-  int k, n_q, n_heads, splits, rows_per_split, n_hg, pairs, seq_ident;
+  int k, n_q, n_heads, splits, rows_per_split, n_hg, pairs, seq_per;
   float scale_log2;  // softmax_scale * log2(e)
 };
 
@@ -106,7 +112,7 @@ __global__ __launch_bounds__(kAttThreads) void attend_bf16_kernel(AttArgs a) {
   const int l16 = lane & 15, g4 = lane >> 4;
   const int H = a.n_heads;
   const int h0 = hg * kHG;
-  const int seq = seq_of(a.q_seq, qi, a.seq_ident);
+  const int seq = attend_seq(a.q_seq, qi, a.seq_per);
 
   const int j0 = sp * a.rows_per_split;
   const int j1 = min(j0 + a.rows_per_split, a.k);
@@ -326,7 +332,7 @@ __global__ __launch_bounds__(kWideThreads) void attend_wide_kernel(AttArgs a) {
   const int hg = wave >> 1, wr = wave & 1;
   const int l16 = lane & 15, g4 = lane >> 4;
   const int h0 = hb * kWideHeads + hg * kHG;
-  const int seq = seq_of(a.q_seq, qi, a.seq_ident);
+  const int seq = attend_seq(a.q_seq, qi, a.seq_per);
   const int j0 = sp * a.rows_per_split;
   const int j1 = min(j0 + a.rows_per_split, a.k);
   const int nsteps = (j1 - j0 + kWideStep - 1) / kWideStep;
@@ -553,7 +559,7 @@ __device__ float block_reduce_sum(float v, float *sh) {
 __global__ __launch_bounds__(256) void attend_f32_kernel(float *__restrict__ out, float *__restrict__ lse,
                                                          const float *__restrict__ q, CacheDev latent, int kv_lora,
                                                          const int32_t *__restrict__ indices, int k,
-                                                         const int32_t *__restrict__ q_seq, int seq_ident, int H,
+                                                         const int32_t *__restrict__ q_seq, int seq_per, int H,
                                                          float scale_log2) {
   __shared__ float lq[1024];
   __shared__ float lz[2048];
@@ -561,7 +567,7 @@ __global__ __launch_bounds__(256) void attend_f32_kernel(float *__restrict__ out
   __shared__ float sh[8];
   const int qi = blockIdx.x / H, h = blockIdx.x - (blockIdx.x / H) * H;
   const int W = latent.width;
-  const int seq = seq_of(q_seq, qi, seq_ident);
+  const int seq = attend_seq(q_seq, qi, seq_per);
   for (int c = threadIdx.x; c < W; c += 256) lq[c] = q[((int64_t)qi * H + h) * W + c];
   __syncthreads();
   float mloc = -INFINITY;
@@ -653,11 +659,11 @@ AttendPlan plan_attend(int n_q, int n_heads, int kv_lora, int width, int k, int 
 }
 
 hipError_t launch_attend(float *out, float *lse, const void *q, int dt, const CacheDev &latent, int kv_lora,
-                         const int32_t *indices, int k, const int32_t *q_seq, int seq_ident, int n_q, int n_heads,
+                         const int32_t *indices, int k, const int32_t *q_seq, int seq_per, int n_q, int n_heads,
                          float scale, const AttendPlan &plan, void *workspace, hipStream_t stream) {
   if (dt == kF32) {
     hipLaunchKernelGGL(attend_f32_kernel, dim3(n_q * n_heads), dim3(256), 0, stream, out, lse,
-                       static_cast<const float *>(q), latent, kv_lora, indices, k, q_seq, seq_ident, n_heads,
+                       static_cast<const float *>(q), latent, kv_lora, indices, k, q_seq, seq_per, n_heads,
                        scale * kLog2e);
     return hipGetLastError();
   }
@@ -668,7 +674,7 @@ hipError_t launch_attend(float *out, float *lse, const void *q, int dt, const Ca
   a.latent = latent;
   a.indices = indices;
   a.q_seq = q_seq;
-  a.seq_ident = seq_ident;
+  a.seq_per = seq_per;
   a.k = k;
   a.n_q = n_q;
   a.n_heads = n_heads;

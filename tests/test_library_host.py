@@ -191,3 +191,29 @@ def test_cache_append_validation(lib):
     assert call(latent=odd, n=0) == 2                                 # 200-byte rows are not 16-byte chunks
     noscale = _cache(dtype=2, row_stride=128, block_stride=128 * 1024)
     assert call(keys=noscale, n=0) == 1
+
+
+def test_decode_shared_validation(lib):
+    lat = _cache(width=576, row_stride=1152, block_stride=1152 * 1024)
+    f = lib.dsa_decode_shared
+
+    def call(batch=4, window=1, k=2048, out=16, idx=16, ws=None, wsb=0, heads=64, q=16):
+        return f(out, None, q, 1, ctypes.byref(lat), 512, heads, idx, batch, window, k, 0.04, ws, wsb, None)
+
+    assert call(batch=0) == 0
+    assert call(batch=-1) == 1
+    assert call(window=0) == 1
+    assert call(window=65) == 2
+    assert call(out=None) == 1
+    assert call(idx=None) == 1
+    assert call(k=0) == 1
+    assert call(k=4096) == 2
+    assert call(heads=24) == 2
+    assert call() == 3                                                # a 4-query step splits: needs a workspace
+    need = lib.dsa_decode_shared_workspace_size(4, 1, 2048, 64, 512)
+    assert need > 0 and call(ws=16, wsb=need - 1) == 3
+    # the split partials of the shared step are those of mla_sparse_attend over the same queries
+    assert need >= lib.mla_sparse_attend_workspace_size(4, 64, 512, 2048)
+    assert lib.dsa_decode_shared_workspace_size(4, 4, 2048, 64, 512) >= \
+        lib.mla_sparse_attend_workspace_size(16, 64, 512, 2048)
+    assert lib.dsa_decode_shared_workspace_size(4, 0, 2048, 64, 512) == 0
