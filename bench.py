@@ -318,6 +318,37 @@ def main():
               "GB_per_s": round(sh_bytes / t_sh / 1e9, 1),
               "what": "sparse MLA over the 2048 kept rows of each of 4 queries with indices from a full layer"}
 
+    # ----------------------- absorbed-MLA projections around the attention ---
+    def time_absorb(aw, reps):
+        x = inputs.make_absorb(aw)
+        dev = {k: None if v is None else torch.from_numpy(v.view(np.int16) if v.dtype == np.uint16 else v).cuda()
+               for k, v in x.items()}
+        qo = torch.empty(aw.n_q, aw.heads, aw.kv_lora + aw.rope, dtype=torch.int16, device="cuda")
+        oo = torch.empty(aw.n_q, aw.heads, aw.d_v, device="cuda")
+        torch.cuda.synchronize()
+        res = {}
+        for name, fn in (("q", lambda: dsa.mla_absorb_q(qo, dev["q_nope"], dev["q_rope"], dev["w_uk"])),
+                         ("out", lambda: dsa.mla_absorb_out(oo, dev["o_lat"], dev["w_uv"]))):
+            for _ in range(5):
+                fn()
+            e0 = torch.cuda.Event(enable_timing=True)
+            e1 = torch.cuda.Event(enable_timing=True)
+            e0.record()
+            for _ in range(reps):
+                fn()
+            e1.record()
+            e1.synchronize()
+            t = e0.elapsed_time(e1) / 1e3 / reps
+            K, N = (aw.d_nope, aw.kv_lora) if name == "q" else (aw.kv_lora, aw.d_v)
+            flops = 2 * aw.n_q * aw.heads * K * N
+            wbytes = aw.heads * K * N * 2
+            res[name] = {"us": round(t * 1e6, 2), "tflops": round(flops / t / 1e12, 1),
+                         "weight_GB_per_s": round(wbytes / t / 1e9, 1)}
+        return {"queries": aw.n_q, "heads": aw.heads, "d_nope": aw.d_nope, "kv_lora": aw.kv_lora, "d_v": aw.d_v,
+                "q_absorb": res["q"], "out_proj": res["out"]}
+
+    absorb = {"decode": time_absorb(inputs.ABSORB_DECODE, 100), "prefill": time_absorb(inputs.ABSORB_PREFILL, 30)}
+
     # ----------------------------------------------------------- prefill ---
     prefill = None
     if not args.no_prefill:
@@ -444,7 +475,7 @@ def main():
         "decode_us_per_step": round(t_step * 1e6, 2), "decode_us_per_step_eager": round(t_eager * 1e6, 2),
         "decode_us_per_step_one_per_launch": round(t_single * 1e6, 2),
         "decode_bytes_per_step": step_bytes, "decode_hbm_frac": round(gbs / HBM_PEAK_GBS, 4),
-        "roofline": roofline, "append": append, "shared": shared, "prefill": prefill, "window": window, "cpu_baseline": cpu, "device": dev_name,
+        "roofline": roofline, "append": append, "shared": shared, "absorb": absorb, "prefill": prefill, "window": window, "cpu_baseline": cpu, "device": dev_name,
     }
     print(json.dumps(line))
 

@@ -228,6 +228,43 @@ size_t dsa_decode_shared_workspace_size(int32_t batch, int32_t window, int32_t k
                                         int32_t kv_lora);
 
 /*
+ * Absorbed-MLA projections around the sparse attention ("Self-contained GLM-5
+ * serving stack", component list: absorbed MLA decode; "GLM on an A100, in Vx",
+ * "The model": one compressed latent row per token serves as key and value).
+ * A head's key and value are up-projections of the latent row c (key
+ * W_UK^T c[0..kv_lora) beside the rope part, value W_UV^T c[0..kv_lora)); the
+ * projections are moved onto the query and the output instead, so attention
+ * runs on the latent rows themselves (mla_sparse_attend and the decode steps).
+ *
+ * mla_absorb_q: the MLA query of mla_sparse_attend from the query's no-rope and
+ * rope parts, per query i and head h:
+ *     q_out[i][h][c]           = bf16( sum_d q_nope[i][h][d] * w_uk[h][d][c] ),  c < kv_lora
+ *     q_out[i][h][kv_lora + r] = q_rope[i][h][r],                                r < rope
+ * float32 accumulation, rounded to nearest even once.
+ *   q_nope [n_q][n_heads][d_nope] bf16; q_rope [n_q][n_heads][rope] bf16 (NULL
+ *   iff rope = 0); w_uk [n_heads][d_nope][kv_lora] bf16;
+ *   q_out [n_q][n_heads][kv_lora + rope] bf16.
+ * Supported: bf16; d_nope a multiple of 32 up to 4096, kv_lora a multiple of 64
+ * up to 4096, rope a multiple of 8 up to 1024, n_heads <= 1024; 16-byte
+ * aligned arrays.
+ *
+ * mla_absorb_out: a head's output in value space from the attention output
+ * over latent rows:
+ *     out[i][h][e] = sum_c o_lat[i][h][c] * w_uv[h][c][e],   e < d_v
+ * o_lat is split into bf16 high and low parts (about 16 significant bits) for
+ * the matrix cores; float32 accumulation.
+ *   o_lat [n_q][n_heads][kv_lora] float32 (the out of mla_sparse_attend);
+ *   w_uv [n_heads][kv_lora][d_v] bf16; out [n_q][n_heads][d_v] float32.
+ * Supported: kv_lora a multiple of 32 up to 4096, d_v a multiple of 64 up to
+ * 4096, n_heads <= 1024; 16-byte aligned arrays.
+ * n_q = 0 returns DSA_OK for both.
+ */
+dsa_status mla_absorb_q(void *q_out, const void *q_nope, const void *q_rope, dsa_dtype q_dtype, const void *w_uk,
+                        int32_t n_q, int32_t n_heads, int32_t d_nope, int32_t kv_lora, int32_t rope, void *stream);
+dsa_status mla_absorb_out(float *out, const float *o_lat, const void *w_uv, int32_t n_q, int32_t n_heads,
+                          int32_t kv_lora, int32_t d_v, void *stream);
+
+/*
  * Cache append: write new tokens into the key and latent caches, the step that
  * must precede any query that sees them ("GLM on an A100, in Vx", section "The
  * model": a query scores every earlier token, its own included).  Token i of

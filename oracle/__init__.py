@@ -14,6 +14,7 @@ Functions (each cites its passage in dsa_oracle.c):
   decode_step                          scores -> top-k -> attention for a decode batch
   e4m3fn_quantize, key_scale           fp8 encoding and the per-token key scale (float32 decisions)
   cache_append                         new tokens' keys (fp8-quantized or copied) and latent rows into caches
+  mla_absorb_q, mla_absorb_out         absorbed-MLA query absorption (q_nope . W_UK) and output projection (o . W_UV)
 """
 from __future__ import annotations
 
@@ -74,6 +75,10 @@ def _load():
     lib.oracle_e4m3fn_quantize.argtypes = [ctypes.c_float]
     lib.oracle_key_scale.restype = ctypes.c_float
     lib.oracle_key_scale.argtypes = [P, ctypes.c_int]
+    lib.oracle_mla_absorb_q.restype = None
+    lib.oracle_mla_absorb_q.argtypes = [P, P, P, ctypes.c_int, P, i32, i32, i32, i32, i32]
+    lib.oracle_mla_absorb_out.restype = None
+    lib.oracle_mla_absorb_out.argtypes = [P, P, P, i32, i32, i32, i32]
     lib.oracle_cache_append.restype = None
     lib.oracle_cache_append.argtypes = [P, P, ctypes.c_int, P, P, P, P, i32]
     _lib = lib
@@ -249,3 +254,32 @@ def cache_append(keys, new_keys, new_keys_dtype, latent, new_latent, seq, pos):
     lib.oracle_cache_append(None if ks is None else ctypes.byref(ks), _ptr(nk), _DT[new_keys_dtype],
                             None if ls is None else ctypes.byref(ls), _ptr(nl), _ptr(seq), _ptr(pos), n)
     return k2, l2
+
+
+def mla_absorb_q(q_nope, q_rope, q_dtype, w_uk):
+    """float64 [n_q, H, kv_lora + rope]: q_nope [n_q, H, d_nope] and q_rope
+    [n_q, H, rope] (raw bits of q_dtype, q_rope may be None), w_uk [H, d_nope,
+    kv_lora] bf16 bits (uint16)."""
+    lib = _load()
+    q_nope = np.ascontiguousarray(q_nope)
+    n_q, H, d_nope = q_nope.shape
+    w_uk = _c(w_uk, np.uint16)
+    kv_lora = w_uk.shape[2]
+    rope = 0 if q_rope is None else q_rope.shape[2]
+    q_rope = None if q_rope is None else np.ascontiguousarray(q_rope)
+    out = np.empty((n_q, H, kv_lora + rope), dtype=np.float64)
+    lib.oracle_mla_absorb_q(_ptr(out), _ptr(q_nope), _ptr(q_rope), _DT[q_dtype], _ptr(w_uk), n_q, H, d_nope,
+                            kv_lora, rope)
+    return out
+
+
+def mla_absorb_out(o_lat, w_uv):
+    """float64 [n_q, H, d_v]: o_lat [n_q, H, kv_lora] float32, w_uv [H, kv_lora, d_v] bf16 bits."""
+    lib = _load()
+    o_lat = _c(o_lat, np.float32)
+    n_q, H, kv_lora = o_lat.shape
+    w_uv = _c(w_uv, np.uint16)
+    d_v = w_uv.shape[2]
+    out = np.empty((n_q, H, d_v), dtype=np.float64)
+    lib.oracle_mla_absorb_out(_ptr(out), _ptr(o_lat), _ptr(w_uv), n_q, H, kv_lora, d_v)
+    return out

@@ -392,6 +392,63 @@ void oracle_decode_step(double *out, double *lse, double *scores_out, int64_t ld
   free(seq);
 }
 
+/* ------------------------------------------------------ absorption GEMMs -- */
+
+/* Query absorption of absorbed MLA ([glm-vx] component list: absorbed MLA
+ * decode; [GLM-A100] "The model": keys and values are kept as one compressed
+ * latent row per token).  The key a head would see is the up-projection of
+ * the latent row, k_h = W_UK[h]^T latent[0..kv_lora); absorbing W_UK into the
+ * query gives the same logit from the latent row directly:
+ *     q_out[i][h][c] = sum_d q_nope[i][h][d] * w_uk[h][d][c],   c < kv_lora
+ *     q_out[i][h][kv_lora + r] = q_rope[i][h][r],              r < rope
+ * (the rope part of the row is compared against the query's rope part as is).
+ * q_nope [n_q][H][d_nope] and q_rope [n_q][H][rope] (may be NULL when rope =
+ * 0) in q_dtype; w_uk [H][d_nope][kv_lora] bf16; q_out [n_q][H][kv_lora + rope]
+ * double. */
+void oracle_mla_absorb_q(double *q_out, const void *q_nope, const void *q_rope, int q_dtype, const uint16_t *w_uk,
+                         int32_t n_q, int32_t H, int32_t d_nope, int32_t kv_lora, int32_t rope) {
+  const int W = kv_lora + rope;
+  for (int32_t i = 0; i < n_q; ++i) {
+    for (int32_t h = 0; h < H; ++h) {
+      double *dst = q_out + ((int64_t)i * H + h) * W;
+      for (int c = 0; c < kv_lora; ++c) {
+        double acc = 0.0;
+        for (int d = 0; d < d_nope; ++d) {
+          const double qv = decode_elem((const uint8_t *)q_nope + (((int64_t)i * H + h) * d_nope + d) * elem_bytes(q_dtype),
+                                        q_dtype);
+          acc += qv * oracle_bf16_to_double(w_uk[((int64_t)h * d_nope + d) * kv_lora + c]);
+        }
+        dst[c] = acc;
+      }
+      for (int r = 0; r < rope; ++r)
+        dst[kv_lora + r] = decode_elem((const uint8_t *)q_rope + (((int64_t)i * H + h) * rope + r) * elem_bytes(q_dtype),
+                                       q_dtype);
+    }
+  }
+}
+
+/* Output up-projection of absorbed MLA: the attention over latent rows gives
+ * o_lat[i][h] = sum_j p_j latent_j[0..kv_lora), and the head's output in value
+ * space is its projection by W_UV (the value of row j is W_UV[h]^T latent_j, so
+ * the projection of the weighted sum equals the weighted sum of the values):
+ *     out[i][h][e] = sum_c o_lat[i][h][c] * w_uv[h][c][e],   e < d_v
+ * o_lat [n_q][H][kv_lora] float32; w_uv [H][kv_lora][d_v] bf16; out double. */
+void oracle_mla_absorb_out(double *out, const float *o_lat, const uint16_t *w_uv, int32_t n_q, int32_t H,
+                           int32_t kv_lora, int32_t d_v) {
+  for (int32_t i = 0; i < n_q; ++i) {
+    for (int32_t h = 0; h < H; ++h) {
+      const float *src = o_lat + ((int64_t)i * H + h) * kv_lora;
+      double *dst = out + ((int64_t)i * H + h) * d_v;
+      for (int e = 0; e < d_v; ++e) {
+        double acc = 0.0;
+        for (int c = 0; c < kv_lora; ++c)
+          acc += (double)src[c] * oracle_bf16_to_double(w_uv[((int64_t)h * kv_lora + c) * d_v + e]);
+        dst[e] = acc;
+      }
+    }
+  }
+}
+
 /* ----------------------------------------------------------- cache append -- */
 
 /* e4m3fn encoding of a float32 value, for writing keys into an fp8 cache

@@ -47,7 +47,7 @@ _lib = None
 EXPORTS = ("dsa_index_scores", "dsa_topk", "dsa_topk_workspace_size", "mla_sparse_attend",
            "mla_sparse_attend_workspace_size", "dsa_decode_step", "dsa_decode_step_workspace_size",
            "dsa_decode_window", "dsa_decode_window_workspace_size", "dsa_decode_shared",
-           "dsa_decode_shared_workspace_size", "dsa_cache_append",
+           "dsa_decode_shared_workspace_size", "dsa_cache_append", "mla_absorb_q", "mla_absorb_out",
            "dsa_workspace_clear", "dsa_status_string")
 
 
@@ -76,6 +76,8 @@ def load(path: str = LIB_PATH):
         "dsa_decode_window_workspace_size": (sz, [i32, i32, i32, i32, i32, i32]),
         "dsa_decode_shared": (ctypes.c_int, [P, P, P, ctypes.c_int, CP, i32, i32, P, i32, i32, i32, f32, P, sz, P]),
         "dsa_decode_shared_workspace_size": (sz, [i32, i32, i32, i32, i32]),
+        "mla_absorb_q": (ctypes.c_int, [P, P, P, ctypes.c_int, P, i32, i32, i32, i32, i32, P]),
+        "mla_absorb_out": (ctypes.c_int, [P, P, P, i32, i32, i32, i32, P]),
         "dsa_cache_append": (ctypes.c_int, [CP, P, ctypes.c_int, CP, P, P, P, i32, P]),
         "dsa_workspace_clear": (ctypes.c_int, [P, sz, P]),
         "dsa_status_string": (ctypes.c_char_p, [ctypes.c_int]),
@@ -202,6 +204,25 @@ def dsa_decode_shared(out, lse, q_mla, q_mla_dtype, latent: DeviceCache, kv_lora
         _p(out), _p(lse), _p(q_mla), DTYPES[q_mla_dtype], ctypes.byref(latent.desc), kv_lora, q_mla.shape[1],
         _p(indices), batch, window, indices.shape[1], float(softmax_scale), _p(workspace), ws_bytes,
         _stream(stream)))
+
+
+def mla_absorb_q(q_out, q_nope, q_rope, w_uk, q_dtype="bf16", stream=None):
+    """q_out [n_q, H, kv_lora + rope] bf16 from q_nope [n_q, H, d_nope], q_rope
+    [n_q, H, rope] (or None) and w_uk [H, d_nope, kv_lora] (see include/dsa.h)."""
+    lib = load()
+    n_q, H, d_nope = q_nope.shape
+    kv_lora = w_uk.shape[2]
+    rope = 0 if q_rope is None else q_rope.shape[2]
+    _check("mla_absorb_q", lib.mla_absorb_q(_p(q_out), _p(q_nope), _p(q_rope), DTYPES[q_dtype], _p(w_uk), n_q, H,
+                                            d_nope, kv_lora, rope, _stream(stream)))
+
+
+def mla_absorb_out(out, o_lat, w_uv, stream=None):
+    """out [n_q, H, d_v] float32 from o_lat [n_q, H, kv_lora] float32 and w_uv [H, kv_lora, d_v]."""
+    lib = load()
+    n_q, H, kv_lora = o_lat.shape
+    d_v = w_uv.shape[2]
+    _check("mla_absorb_out", lib.mla_absorb_out(_p(out), _p(o_lat), _p(w_uv), n_q, H, kv_lora, d_v, _stream(stream)))
 
 
 def dsa_cache_append(keys: Optional[DeviceCache], new_keys, new_keys_dtype, latent: Optional[DeviceCache],

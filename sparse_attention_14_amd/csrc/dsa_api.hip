@@ -337,6 +337,34 @@ dsa_status dsa_decode_shared(float *out, float *lse, const void *q_mla, dsa_dtyp
                                 n_q, mla_heads, softmax_scale, p, workspace, static_cast<hipStream_t>(stream)));
 }
 
+dsa_status mla_absorb_q(void *q_out, const void *q_nope, const void *q_rope, dsa_dtype q_dtype, const void *w_uk,
+                        int32_t n_q, int32_t n_heads, int32_t d_nope, int32_t kv_lora, int32_t rope, void *stream) {
+  if (n_q < 0 || n_heads <= 0 || d_nope <= 0 || kv_lora <= 0 || rope < 0) return DSA_ERR_INVALID_ARGUMENT;
+  if (!q_out || !q_nope || !w_uk || (rope > 0 && !q_rope) || !valid_dtype(q_dtype)) return DSA_ERR_INVALID_ARGUMENT;
+  if (q_dtype != DSA_BF16 || d_nope % 32 || d_nope > 4096 || kv_lora % 64 || kv_lora > 4096 || rope % 8 ||
+      rope > 1024 || n_heads > 1024)
+    return DSA_ERR_UNSUPPORTED;
+  if (!aligned16(q_out) || !aligned16(q_nope) || !aligned16(w_uk) || (rope > 0 && !aligned16(q_rope)))
+    return DSA_ERR_UNSUPPORTED;
+  if (n_q == 0) return DSA_OK;
+  if ((int64_t)((n_q + 63) / 64) * n_heads * (kv_lora / 64) > (int64_t)1 << 24) return DSA_ERR_UNSUPPORTED;
+  return from_hip(launch_absorb(q_out, 1, kv_lora + rope, q_nope, 0, static_cast<const uint16_t *>(w_uk), n_q,
+                                n_heads, d_nope, kv_lora, rope > 0 ? static_cast<const uint16_t *>(q_rope) : nullptr,
+                                rope, static_cast<hipStream_t>(stream)));
+}
+
+dsa_status mla_absorb_out(float *out, const float *o_lat, const void *w_uv, int32_t n_q, int32_t n_heads,
+                          int32_t kv_lora, int32_t d_v, void *stream) {
+  if (n_q < 0 || n_heads <= 0 || kv_lora <= 0 || d_v <= 0) return DSA_ERR_INVALID_ARGUMENT;
+  if (!out || !o_lat || !w_uv) return DSA_ERR_INVALID_ARGUMENT;
+  if (kv_lora % 32 || kv_lora > 4096 || d_v % 64 || d_v > 4096 || n_heads > 1024) return DSA_ERR_UNSUPPORTED;
+  if (!aligned16(out) || !aligned16(o_lat) || !aligned16(w_uv)) return DSA_ERR_UNSUPPORTED;
+  if (n_q == 0) return DSA_OK;
+  if ((int64_t)((n_q + 63) / 64) * n_heads * (d_v / 64) > (int64_t)1 << 24) return DSA_ERR_UNSUPPORTED;
+  return from_hip(launch_absorb(out, 0, d_v, o_lat, 1, static_cast<const uint16_t *>(w_uv), n_q, n_heads, kv_lora,
+                                d_v, nullptr, 0, static_cast<hipStream_t>(stream)));
+}
+
 dsa_status dsa_cache_append(const dsa_cache *keys, const void *new_keys, dsa_dtype new_keys_dtype,
                             const dsa_cache *latent, const void *new_latent, const int32_t *seq,
                             const int32_t *pos, int32_t n_new, void *stream) {

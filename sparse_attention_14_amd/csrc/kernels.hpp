@@ -78,4 +78,12 @@ hipError_t launch_cache_append(const CacheDev *keys, int key_dt, const void *new
                                const CacheDev *latent, int latent_row_bytes, const void *new_latent,
                                const int32_t *seq, const int32_t *pos, int n_new, hipStream_t stream);
 
+// ---- absorbed-MLA projections -------------------------------------------------
+// Per head h: C[m][h][n] = sum_k A[m][h][k] * B[h][k][n] for n < N (C rows are
+// ldc wide); A bf16 (c_bf16: C bf16, rounded to nearest even) or f32 (C f32);
+// rope (nullable): [M][H][R] bf16 copied to C columns [N, N + R).
+// K a multiple of 32, N a multiple of 64.
+hipError_t launch_absorb(void *c, int c_bf16, int ldc, const void *a, int a_f32, const uint16_t *b, int M, int H,
+                         int K, int N, const uint16_t *rope, int R, hipStream_t stream);
+
 }  // namespace dsa

@@ -30,6 +30,7 @@ _NAN_BITS = {"f32": 0x7FC00000, "bf16": 0x7FC0, "e4m3fn": 0x7F}
 _TAGS = {
     "q_idx": 1, "w_idx": 2, "keys": 3, "key_scale": 4, "q_mla": 5, "latent": 6,
     "lens": 7, "block_perm": 8, "ties": 9, "ties_src": 10, "append_keys": 11, "append_latent": 12,
+    "q_nope": 13, "q_rope": 14, "w_uk": 15, "w_uv": 16, "o_lat": 17,
 }
 
 
@@ -446,3 +447,42 @@ def append_tokens(p: Problem, window: int = 1, key_dtype: str = "bf16"):
     nl = rng_for(wid, "append_latent").standard_normal((m, W), dtype=np.float32) * np.float32(wl.latent_sigma)
     return (encode(nk, key_dtype), encode(nl, wl.latent_dtype), np.array(seq, dtype=np.int32),
             np.array(pos, dtype=np.int32))
+
+
+@dataclass(frozen=True)
+class AbsorbWorkload:
+    """Shapes of the absorbed-MLA projections around the attention.  The pages
+    give kv_lora 512 + rope 64 and 64 heads but not the per-head no-rope and
+    value widths; 128 each is taken (kv_lora = 4 x 128)."""
+    name: str
+    wid: int
+    n_q: int
+    heads: int = 64
+    d_nope: int = 128
+    kv_lora: int = 512
+    rope: int = 64
+    d_v: int = 128
+
+
+def make_absorb(aw: AbsorbWorkload) -> dict:
+    """Seeded inputs: q_nope, q_rope ~ N(0, 1) bf16 bits; w_uk [H, d_nope, kv_lora]
+    ~ N(0, 1/sqrt(d_nope)) and w_uv [H, kv_lora, d_v] ~ N(0, 1/sqrt(kv_lora)) bf16
+    bits (random initialisation); o_lat [n_q, H, kv_lora] ~ N(0, 0.01) float32
+    (the attention output, a weighted mean of N(0, 0.05) latent rows)."""
+    H = aw.heads
+    f32 = np.float32
+
+    def normal(tag, shape, sigma):
+        return rng_for(aw.wid, tag).standard_normal(shape, dtype=f32) * f32(sigma)
+
+    return {
+        "q_nope": encode(normal("q_nope", (aw.n_q, H, aw.d_nope), 1.0), "bf16"),
+        "q_rope": encode(normal("q_rope", (aw.n_q, H, aw.rope), 1.0), "bf16") if aw.rope else None,
+        "w_uk": encode(normal("w_uk", (H, aw.d_nope, aw.kv_lora), 1.0 / np.sqrt(aw.d_nope)), "bf16"),
+        "w_uv": encode(normal("w_uv", (H, aw.kv_lora, aw.d_v), 1.0 / np.sqrt(aw.kv_lora)), "bf16"),
+        "o_lat": normal("o_lat", (aw.n_q, H, aw.kv_lora), 0.01),
+    }
+
+
+ABSORB_DECODE = AbsorbWorkload(name="absorb_decode_4q", wid=20, n_q=4)
+ABSORB_PREFILL = AbsorbWorkload(name="absorb_prefill_2048q", wid=21, n_q=2048)

@@ -1,0 +1,131 @@
+"""GPU parity of the absorbed-MLA projections (mla_absorb_q, mla_absorb_out)
+against the oracle.  The float32 output projection: per (query, head) row,
+relative error within the bf16-input tolerance (2e-3).  The absorbed query is
+a bf16 output (the attention takes bf16 queries): each element is the fp32
+sum rounded once to nearest, so it must lie within half a bf16 step of the
+exact value plus the fp32 accumulation bound, and rows within the bf16 unit
+roundoff 2^-8 normwise; the rope part is copied bit for bit.
+Shapes span several 64-row and 64-column tiles, ragged row counts and other
+head widths; at 2048 queries sampled rows are checked.  A chain test feeds
+the absorbed query through the sparse attention and projects the output."""
+import dataclasses
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import sparse_attention_14_amd as dsa
+from sparse_attention_14_amd import device, inputs
+
+from gpu_util import TOL, check_attention
+
+pytestmark = pytest.mark.gpu
+
+A = inputs.ABSORB_DECODE
+CASES = {
+    "decode_4q": A,
+    "one_query_two_heads": dataclasses.replace(A, name="x1", wid=701, n_q=1, heads=2),
+    "ragged_70q": dataclasses.replace(A, name="x2", wid=702, n_q=70, heads=8),
+    "nope192_v256": dataclasses.replace(A, name="x3", wid=703, n_q=33, heads=4, d_nope=192, d_v=256),
+    "no_rope_small": dataclasses.replace(A, name="x4", wid=704, n_q=130, heads=3, d_nope=32, kv_lora=128, rope=0,
+                                         d_v=64),
+}
+
+
+def _dev(a):
+    a = np.ascontiguousarray(a)
+    return torch.from_numpy(a.view(np.int16) if a.dtype == np.uint16 else a).cuda()
+
+
+def _bf16_to_f64(bits):
+    return (bits.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+
+
+def _rel_rows(got, ref):
+    num = np.linalg.norm(got - ref, axis=-1)
+    den = np.maximum(np.linalg.norm(ref, axis=-1), 1e-30)
+    return float((num / den).max())
+
+
+def _check_query(got, ref, x, aw, rows=None):
+    """got: the GPU's bf16 query values; ref: the oracle's exact values."""
+    qn = _bf16_to_f64(x["q_nope"] if rows is None else x["q_nope"][rows])
+    wk = _bf16_to_f64(x["w_uk"])
+    cond = np.einsum("ihd,hdc->ihc", np.abs(qn), np.abs(wk))          # sum_d |q w|: the sum's condition
+    ulp = 2.0 ** (np.floor(np.log2(np.maximum(np.abs(ref), 1e-300))) - 7)
+    bound = 0.5 * ulp * (1 + 2.0 ** -7) + 2.0 ** -22 * cond
+    assert np.all(np.abs(got - ref) <= bound)
+    eq = _rel_rows(got, ref)
+    print(f"  worst row error: query {eq:.3g}")
+    assert eq <= 2.0 ** -8
+
+
+def _gpu_absorb(x, aw):
+    qo = torch.empty(aw.n_q, aw.heads, aw.kv_lora + aw.rope, dtype=torch.int16, device="cuda")
+    qo.fill_(0x7FC0)                                              # NaN bits: every element must be written
+    oo = torch.full((aw.n_q, aw.heads, aw.d_v), float("nan"), device="cuda")
+    dsa.mla_absorb_q(qo, _dev(x["q_nope"]), None if x["q_rope"] is None else _dev(x["q_rope"]), _dev(x["w_uk"]))
+    dsa.mla_absorb_out(oo, _dev(x["o_lat"]), _dev(x["w_uv"]))
+    torch.cuda.synchronize()
+    return qo.cpu().numpy().view(np.uint16), oo.cpu().numpy()
+
+
+@pytest.mark.parametrize("name", sorted(CASES))
+def test_absorb_matches_oracle(name):
+    aw = CASES[name]
+    x = inputs.make_absorb(aw)
+    print(f"case {name}: {aw}", flush=True)
+    q_bits, out = _gpu_absorb(x, aw)
+    ref_q = oracle.mla_absorb_q(x["q_nope"], x["q_rope"], "bf16", x["w_uk"])
+    ref_o = oracle.mla_absorb_out(x["o_lat"], x["w_uv"])
+    got_q = _bf16_to_f64(q_bits)
+    L = aw.kv_lora
+    _check_query(got_q[..., :L], ref_q[..., :L], x, aw)
+    eo = _rel_rows(out.astype(np.float64), ref_o)
+    print(f"  worst row error: output {eo:.3g}")
+    assert eo <= TOL["bf16"]
+    if aw.rope:
+        assert np.array_equal(q_bits[..., L:], x["q_rope"])
+
+
+def test_absorb_prefill_sampled_rows():
+    aw = inputs.ABSORB_PREFILL
+    x = inputs.make_absorb(aw)
+    q_bits, out = _gpu_absorb(x, aw)
+    rows = np.array([0, 1, 63, 64, 1000, 2046, 2047])
+    ref_q = oracle.mla_absorb_q(x["q_nope"][rows], x["q_rope"][rows], "bf16", x["w_uk"])
+    ref_o = oracle.mla_absorb_out(x["o_lat"][rows], x["w_uv"])
+    _check_query(_bf16_to_f64(q_bits[rows])[..., :aw.kv_lora], ref_q[..., :aw.kv_lora], x, aw, rows=rows)
+    assert np.array_equal(q_bits[rows][..., aw.kv_lora:], x["q_rope"][rows])
+    assert _rel_rows(out[rows].astype(np.float64), ref_o) <= TOL["bf16"]
+
+
+def test_absorbed_query_feeds_attention_and_projection():
+    """q_nope/q_rope -> absorbed query -> sparse attention over kept latent
+    rows -> output projection, against the oracle's chain on the same indices."""
+    wl = inputs.small(inputs.DECODE_8K, name="x5", wid=705, batch=2, seq_len=(3000, 5000))
+    p = inputs.make_problem(wl)
+    aw = dataclasses.replace(A, name="x5a", wid=706, n_q=p.n_q)
+    x = inputs.make_absorb(aw)
+    dp = device.upload(p)
+    qo = torch.empty(p.n_q, aw.heads, aw.kv_lora + aw.rope, dtype=torch.int16, device="cuda")
+    dsa.mla_absorb_q(qo, _dev(x["q_nope"]), _dev(x["q_rope"]), _dev(x["w_uk"]))
+    idx = torch.from_numpy(np.stack([np.sort(np.random.default_rng(b).choice(int(p.q_len[b]), p.topk, replace=False))
+                                     for b in range(p.n_q)]).astype(np.int32)).cuda()
+    o_lat = torch.empty(p.n_q, aw.heads, aw.kv_lora, device="cuda")
+    lse = torch.empty(p.n_q, aw.heads, device="cuda")
+    ws = torch.zeros(max(dsa.mla_sparse_attend_workspace_size(p.n_q, aw.heads, aw.kv_lora, p.topk), 1),
+                     dtype=torch.uint8, device="cuda")
+    dsa.mla_sparse_attend(o_lat, lse, qo, "bf16", dp.latent, aw.kv_lora, idx, p.softmax_scale, q_seq=dp.q_seq,
+                          workspace=ws)
+    out = torch.empty(p.n_q, aw.heads, aw.d_v, device="cuda")
+    dsa.mla_absorb_out(out, o_lat, _dev(x["w_uv"]))
+    torch.cuda.synchronize()
+    # the oracle's chain on the GPU's bf16 query (its own rounding is covered above)
+    q_bits = qo.cpu().numpy().view(np.uint16)
+    ref_lat, ref_lse, _ = oracle.mla_attend(q_bits, "bf16", p.latent, aw.kv_lora, idx.cpu().numpy(), p.q_seq,
+                                            p.softmax_scale)
+    check_attention(o_lat.cpu().numpy(), lse.cpu().numpy(), ref_lat, ref_lse, TOL["bf16"])
+    ref_out = oracle.mla_absorb_out(o_lat.cpu().numpy(), x["w_uv"])
+    assert _rel_rows(out.cpu().numpy().astype(np.float64), ref_out) <= TOL["bf16"]

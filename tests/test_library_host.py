@@ -217,3 +217,26 @@ def test_decode_shared_validation(lib):
     assert lib.dsa_decode_shared_workspace_size(4, 4, 2048, 64, 512) >= \
         lib.mla_sparse_attend_workspace_size(16, 64, 512, 2048)
     assert lib.dsa_decode_shared_workspace_size(4, 0, 2048, 64, 512) == 0
+
+
+def test_absorb_validation(lib):
+    fq, fo = lib.mla_absorb_q, lib.mla_absorb_out
+
+    def q(out=16, qn=16, qr=16, dt=1, w=16, n_q=4, H=64, dn=128, L=512, R=64):
+        return fq(out, qn, qr, dt, w, n_q, H, dn, L, R, None)
+
+    def o(out=16, ol=16, w=16, n_q=4, H=64, L=512, dv=128):
+        return fo(out, ol, w, n_q, H, L, dv, None)
+
+    assert q(n_q=0) == 0 and o(n_q=0) == 0
+    assert q(n_q=-1) == 1 and o(n_q=-1) == 1
+    assert q(out=None) == 1 and q(qn=None) == 1 and q(w=None) == 1
+    assert q(qr=None) == 1                                            # rope > 0 needs its part
+    assert q(qr=None, R=0, n_q=0) == 0
+    assert q(dt=0) == 2                                               # bf16 only
+    assert q(dt=9) == 1
+    assert q(dn=100) == 2 and q(L=500) == 2 and q(R=60) == 2
+    assert q(qn=24) == 2                                              # 16-byte alignment
+    assert o(out=None) == 1 and o(ol=None) == 1 and o(w=None) == 1
+    assert o(L=500) == 2 and o(dv=100) == 2 and o(ol=8) == 2
+    assert o(H=0) == 1 and o(H=2000) == 2
