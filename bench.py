@@ -329,16 +329,8 @@ def main():
         res = {}
         for name, fn in (("q", lambda: dsa.mla_absorb_q(qo, dev["q_nope"], dev["q_rope"], dev["w_uk"])),
                          ("out", lambda: dsa.mla_absorb_out(oo, dev["o_lat"], dev["w_uv"]))):
-            for _ in range(5):
-                fn()
-            e0 = torch.cuda.Event(enable_timing=True)
-            e1 = torch.cuda.Event(enable_timing=True)
-            e0.record()
-            for _ in range(reps):
-                fn()
-            e1.record()
-            e1.synchronize()
-            t = e0.elapsed_time(e1) / 1e3 / reps
+            # launches captured in one graph, so the host's call overhead is not timed
+            t = time_graph_steps(torch, lambda ci: fn(), 10, reps, 20)
             K, N = (aw.d_nope, aw.kv_lora) if name == "q" else (aw.kv_lora, aw.d_v)
             flops = 2 * aw.n_q * aw.heads * K * N
             wbytes = aw.heads * K * N * 2

@@ -5,8 +5,9 @@ a bf16 output (the attention takes bf16 queries): each element is the fp32
 sum rounded once to nearest, so it must lie within half a bf16 step of the
 exact value plus the fp32 accumulation bound, and rows within the bf16 unit
 roundoff 2^-8 normwise; the rope part is copied bit for bit.
-Shapes span several 64-row and 64-column tiles, ragged row counts and other
-head widths; at 2048 queries sampled rows are checked.  A chain test feeds
+Shapes cover the few-row kernel (up to 8 queries, 64- and 32-column blocks),
+the 128 x 128 tile kernel and the 64 x 64 one (widths not a multiple of 128),
+ragged row counts and other head widths; at 2048 queries sampled rows are checked.  A chain test feeds
 the absorbed query through the sparse attention and projects the output."""
 import dataclasses
 
@@ -30,6 +31,12 @@ CASES = {
     "nope192_v256": dataclasses.replace(A, name="x3", wid=703, n_q=33, heads=4, d_nope=192, d_v=256),
     "no_rope_small": dataclasses.replace(A, name="x4", wid=704, n_q=130, heads=3, d_nope=32, kv_lora=128, rope=0,
                                          d_v=64),
+    "eight_queries_narrow": dataclasses.replace(A, name="x6", wid=707, n_q=8, heads=4, d_nope=32, kv_lora=128,
+                                                rope=16, d_v=64),
+    "window_16q": dataclasses.replace(A, name="x7", wid=708, n_q=16),
+    "k256_both": dataclasses.replace(A, name="x8", wid=709, n_q=40, heads=2, d_nope=256, kv_lora=256, d_v=128),
+    "lora192_rolled": dataclasses.replace(A, name="x9", wid=710, n_q=20, heads=2, d_nope=64, kv_lora=192, rope=0,
+                                          d_v=128),
 }
 
 
