@@ -46,6 +46,7 @@ def parse():
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--no-prefill", action="store_true")
     ap.add_argument("--no-window", action="store_true", help="skip the multi-token decode window leg")
+    ap.add_argument("--no-latent8", action="store_true", help="skip the fp8-latent decode leg")
     ap.add_argument("--copy-probe", action="store_true",
                     help="only run a plain 1 GiB device copy three times (calibrates HBM byte counters) and exit")
     return ap.parse_args()
@@ -58,7 +59,7 @@ def decode_algorithmic_bytes(p) -> int:
     n_tok = int(p.q_len.astype("int64").sum())
     kept = int(sum(min(int(n), p.topk) for n in p.q_len))
     keys = n_tok * p.idx_dim * eb[p.keys.dtype] + (n_tok * 4 if p.keys.dtype == "e4m3fn" else 0)
-    latent = kept * (p.kv_lora + p.rope) * eb[p.latent.dtype]
+    latent = kept * ((p.kv_lora + p.rope) * eb[p.latent.dtype] + (4 if p.latent.dtype == "e4m3fn" else 0))
     q = p.q_idx.size * eb[p.q_idx_dtype] + p.w_idx.size * 4 + p.q_mla.size * eb[p.q_mla_dtype]
     out = p.n_q * p.mla_heads * (p.kv_lora + 1) * 4
     return keys + latent + q + out
@@ -71,7 +72,7 @@ def window_algorithmic_bytes(p) -> int:
     n_tok = int(sum(int(n) for n in p.meta["seq_lens"]))
     kept = int(sum(min(int(n), p.topk) for n in p.q_len))
     keys = n_tok * p.idx_dim * eb[p.keys.dtype] + (n_tok * 4 if p.keys.dtype == "e4m3fn" else 0)
-    latent = kept * (p.kv_lora + p.rope) * eb[p.latent.dtype]
+    latent = kept * ((p.kv_lora + p.rope) * eb[p.latent.dtype] + (4 if p.latent.dtype == "e4m3fn" else 0))
     q = p.q_idx.size * eb[p.q_idx_dtype] + p.w_idx.size * 4 + p.q_mla.size * eb[p.q_mla_dtype]
     out = p.n_q * p.mla_heads * (p.kv_lora + 1) * 4
     return keys + latent + q + out
@@ -440,6 +441,40 @@ def main():
                   "bytes_per_step": wbytes, "GB_per_s": round(wbytes / t_w / 1e9, 1),
                   "hbm_frac": round(wbytes / t_w / 1e9 / HBM_PEAK_GBS, 4), "cache_copies": n_wc}
 
+    # ------------------------------- fp8 latent rows (the memory-halving variant) ---
+    latent8 = None
+    if not args.no_latent8:
+        if window is not None:
+            del wcopies, wws, dpw
+        torch.cuda.empty_cache()
+        w8 = inputs.DECODE_128K_FP8_LAT8
+        t0 = time.time()
+        p8 = inputs.make_problem(w8)
+        dp8 = device.upload(p8)
+        print(f"[bench] generated and uploaded {w8.name} in {time.time() - t0:.1f}s", file=sys.stderr, flush=True)
+        n8c = 3
+        copies8 = [(dp8.keys, dp8.latent)] + [(clone_cache(dp8.keys), clone_cache(dp8.latent)) for _ in range(n8c - 1)]
+        o8 = torch.empty(p8.n_q, H, L, device="cuda")
+        l8 = torch.empty(p8.n_q, H, device="cuda")
+        ws8 = [torch.zeros(dsa.dsa_decode_step_workspace_size(p8.n_q, p8.max_len, k, H, L), dtype=torch.uint8,
+                           device="cuda") for _ in copies8]
+
+        def step8(ci):
+            keys, lat = copies8[ci]
+            dsa.dsa_decode_step(o8, l8, dp8.q_idx, p8.q_idx_dtype, dp8.w_idx, keys, dp8.q_mla, p8.q_mla_dtype, lat,
+                                L, dp8.q_len, p8.max_len, k, p8.softmax_scale, ws8[ci])
+
+        for i in range(3):
+            step8(i % n8c)
+        torch.cuda.synchronize()
+        assert torch.isfinite(o8).all().item(), "non-finite fp8-latent decode output"
+        t8 = time_graph_steps(torch, step8, n8c, max(args.steps // 2, 30), max(args.warmup, 6))
+        b8 = decode_algorithmic_bytes(p8)
+        latent8 = {"workload": w8.name, "latent": "512+64 e4m3fn + f32 scale per token", "us_per_step": round(t8 * 1e6, 2),
+                   "bytes_per_step": b8, "GB_per_s": round(b8 / t8 / 1e9, 1),
+                   "hbm_frac": round(b8 / t8 / 1e9 / HBM_PEAK_GBS, 4), "cache_copies": n8c}
+        del copies8, ws8, dp8
+
     # ------------------------------------------------------ CPU baseline ---
     cpu = None
     if not args.no_cpu:
@@ -467,7 +502,7 @@ def main():
         "decode_us_per_step": round(t_step * 1e6, 2), "decode_us_per_step_eager": round(t_eager * 1e6, 2),
         "decode_us_per_step_one_per_launch": round(t_single * 1e6, 2),
         "decode_bytes_per_step": step_bytes, "decode_hbm_frac": round(gbs / HBM_PEAK_GBS, 4),
-        "roofline": roofline, "append": append, "shared": shared, "absorb": absorb, "prefill": prefill, "window": window, "cpu_baseline": cpu, "device": dev_name,
+        "roofline": roofline, "append": append, "shared": shared, "absorb": absorb, "prefill": prefill, "window": window, "latent_fp8": latent8, "cpu_baseline": cpu, "device": dev_name,
     }
     print(json.dumps(line))
 

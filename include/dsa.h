@@ -138,11 +138,16 @@ size_t dsa_topk_workspace_size(int32_t n_q, int32_t k, int32_t max_len);
  *     lse[i][h]    = ln sum_j exp(z_j)
  * The key is the whole latent row (kv_lora latent + rope), the value its
  * first kv_lora entries.  No kept slot: out = 0, lse = -inf.
- *   q       [n_q][n_heads][W], dtype q_dtype (same as latent->dtype)
+ *   q       [n_q][n_heads][W], dtype q_dtype (the latent dtype, or bf16 for an
+ *           fp8 latent cache)
  *   out     [n_q][n_heads][kv_lora] float32;  lse [n_q][n_heads] float32 (nullable)
- * Supported: bf16 with W = 576, kv_lora = 512, n_heads a multiple of 16 up to 128;
- *   f32 with W <= 1024 a multiple of 4, kv_lora <= W a multiple of 4, n_heads <= 128;
- *   1 <= k <= 2048.
+ * An fp8 latent cache holds e4m3fn rows with one float32 scale per token
+ * (row_j = e4m3fn(bytes) * scale[token], the dsa_cache fp8 convention): the
+ * memory-halving variant of the FP8 E4M3 + float32-scale format of "GLM on an
+ * A100, in Vx", "INT4, FP8 and BF16"; dsa_cache_append writes it.
+ * Supported: bf16 q with bf16 or fp8 latent rows, W = 576, kv_lora = 512,
+ *   n_heads a multiple of 16 up to 128; f32 with W <= 1024 a multiple of 4,
+ *   kv_lora <= W a multiple of 4, n_heads <= 128; 1 <= k <= 2048.
  */
 dsa_status mla_sparse_attend(float *out, float *lse, const void *q, dsa_dtype q_dtype, const dsa_cache *latent,
                              int32_t kv_lora, const int32_t *indices, int32_t k, const int32_t *q_seq, int32_t n_q,
@@ -271,29 +276,29 @@ dsa_status mla_absorb_out(float *out, const float *o_lat, const void *w_uv, int3
  * the call belongs to sequence seq ? seq[i] : 0 and goes to position pos[i] of
  * that sequence, addressed exactly as the dsa_cache comment describes (the
  * block of a paged cache must already be in the block table).
- *   - keys (NULL: keys untouched), new_keys [n_new][keys->width]:
+ *   - keys (NULL: keys untouched), new_keys [n_new][keys->width] in
+ *     new_keys_dtype, and latent (NULL: untouched), new_latent [n_new]
+ *     [latent->width] in new_latent_dtype, each written the same way:
  *       fp8 cache (the FP8 format of "INT4, FP8 and BF16": E4M3 bytes with a
- *       float32 scale), new_keys f32 or bf16: per token, in float32,
- *           amax  = max_d |k_d|,  s = max(amax / 448, 2^-126),
- *           byte_d = nearest e4m3fn code of k_d / s (ties to the even code,
+ *       float32 scale), input f32 or bf16: per token, in float32,
+ *           amax  = max_d |x_d|,  s = max(amax / 448, 2^-126),
+ *           byte_d = nearest e4m3fn code of x_d / s (ties to the even code,
  *                    magnitudes >= 448 saturated to 448, sign kept),
  *       and s is stored as the token's scale;
- *       bf16 or f32 cache: new_keys in the cache's dtype, bits copied.
- *   - latent (NULL: untouched), new_latent [n_new][latent->width] in the latent
- *     cache's dtype (f32 or bf16), bits copied.
+ *       bf16 or f32 cache: input in the cache's dtype, bits copied.
  * The descriptors' rows and scale pointers are written through (their memory
  * must be writable; the other entry points only read it).  Only the addressed
  * rows and scales change.  Two tokens with the same (sequence, position) in one
- * call leave an unspecified one of them.  Key values must be finite (otherwise
- * the bytes and scale are unspecified).  seq, pos: device int32 [n_new],
- * 0 <= pos[i] < the sequence's capacity (trusted).  n_new = 0 returns DSA_OK.
- * Supported: fp8 key caches up to 128 wide; key and latent copies whose row
- * size is a multiple of 16 bytes from 16-byte aligned inputs; fp8 latent
- * caches are DSA_ERR_UNSUPPORTED.
+ * call leave an unspecified one of them.  Values quantized to fp8 must be finite
+ * (otherwise the bytes and scale are unspecified).  seq, pos: device int32
+ * [n_new], 0 <= pos[i] < the sequence's capacity (trusted).  n_new = 0 returns
+ * DSA_OK.
+ * Supported: fp8 caches up to 1024 wide; copies whose row size is a multiple of
+ * 16 bytes from 16-byte aligned inputs.
  */
 dsa_status dsa_cache_append(const dsa_cache *keys, const void *new_keys, dsa_dtype new_keys_dtype,
-                            const dsa_cache *latent, const void *new_latent, const int32_t *seq,
-                            const int32_t *pos, int32_t n_new, void *stream);
+                            const dsa_cache *latent, const void *new_latent, dsa_dtype new_latent_dtype,
+                            const int32_t *seq, const int32_t *pos, int32_t n_new, void *stream);
 
 /* Zero-fill a workspace on `stream` with a fill kernel (no hipMemset node, so it
  * may be captured in a graph).  bytes must be a multiple of 4. */

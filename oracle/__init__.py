@@ -80,7 +80,7 @@ def _load():
     lib.oracle_mla_absorb_out.restype = None
     lib.oracle_mla_absorb_out.argtypes = [P, P, P, i32, i32, i32, i32]
     lib.oracle_cache_append.restype = None
-    lib.oracle_cache_append.argtypes = [P, P, ctypes.c_int, P, P, P, P, i32]
+    lib.oracle_cache_append.argtypes = [P, P, ctypes.c_int, P, P, ctypes.c_int, P, P, i32]
     _lib = lib
     return lib
 
@@ -228,15 +228,18 @@ def _copy_cache(cache):
     return out
 
 
-def cache_append(keys, new_keys, new_keys_dtype, latent, new_latent, seq, pos):
+def cache_append(keys, new_keys, new_keys_dtype, latent, new_latent, seq, pos, new_latent_dtype=None):
     """Append tokens to copies of the given inputs.Cache objects (either may be
-    None) and return the copies (keys, latent).  new_keys: raw bits [n, width]
-    (float32 for f32, uint16 for bf16); new_latent: raw bits [n, width] in the
-    latent cache's dtype; seq (or None: all sequence 0) and pos: int32 [n]."""
+    None) and return the copies (keys, latent).  new_keys / new_latent: raw bits
+    [n, width] (float32 for f32, uint16 for bf16) in new_keys_dtype /
+    new_latent_dtype (default: the latent cache's dtype, bf16 for fp8 caches);
+    seq (or None: all sequence 0) and pos: int32 [n]."""
     lib = _load()
     pos = _c(pos, np.int32)
     n = int(pos.shape[0])
     seq = None if seq is None else _c(seq, np.int32)
+    if new_latent_dtype is None:
+        new_latent_dtype = "bf16" if latent is None or latent.dtype == "e4m3fn" else latent.dtype
     k2 = None if keys is None else _copy_cache(keys)
     l2 = None if latent is None else _copy_cache(latent)
     nk = None if new_keys is None else np.ascontiguousarray(new_keys)
@@ -250,9 +253,10 @@ def cache_append(keys, new_keys, new_keys_dtype, latent, new_latent, seq, pos):
     if l2 is not None:
         ls, kl = _cache_struct(l2)
         keep.append(kl)
-        assert kl[0] is l2.storage
+        assert kl[0] is l2.storage and (l2.scale is None or kl[1] is l2.scale)
     lib.oracle_cache_append(None if ks is None else ctypes.byref(ks), _ptr(nk), _DT[new_keys_dtype],
-                            None if ls is None else ctypes.byref(ls), _ptr(nl), _ptr(seq), _ptr(pos), n)
+                            None if ls is None else ctypes.byref(ls), _ptr(nl), _DT[new_latent_dtype], _ptr(seq),
+                            _ptr(pos), n)
     return k2, l2
 
 
@@ -283,3 +287,4 @@ def mla_absorb_out(o_lat, w_uv):
     out = np.empty((n_q, H, d_v), dtype=np.float64)
     lib.oracle_mla_absorb_out(_ptr(out), _ptr(o_lat), _ptr(w_uv), n_q, H, kv_lora, d_v)
     return out
+

@@ -506,49 +506,44 @@ static float input_to_float(const void *src, int64_t i, int dtype) {
   return f;
 }
 
+/* Token i's row into one cache: fp8 caches get s = oracle_key_scale(row) and
+ * byte d = oracle_e4m3fn_quantize(x[d] / s) (float32 division) with scale s;
+ * other caches get the input bits copied (the input is in the cache's dtype). */
+static void append_row(const oracle_cache *c, const void *src, int src_dtype, int32_t i, int32_t b, int64_t t) {
+  const int W = c->width;
+  const int64_t block = c->block_table ? (int64_t)c->block_table[(int64_t)b * c->max_blocks + t / c->block_size]
+                                       : (int64_t)b;
+  const int64_t slot = t % c->block_size;
+  uint8_t *row = (uint8_t *)c->rows + block * c->block_stride + slot * c->row_stride;
+  if (c->dtype == ORACLE_E4M3FN) {
+    float *x = (float *)calloc((size_t)(W > 0 ? W : 1), sizeof(float));
+    for (int d = 0; d < W; ++d) x[d] = input_to_float(src, (int64_t)i * W + d, src_dtype);
+    const float s = oracle_key_scale(x, W);
+    for (int d = 0; d < W; ++d) row[d] = oracle_e4m3fn_quantize(x[d] / s);
+    ((float *)c->scale)[block * c->scale_block_stride + slot] = s;
+    free(x);
+  } else {
+    const int eb = elem_bytes(c->dtype);
+    memcpy(row, (const uint8_t *)src + (int64_t)i * W * eb, (size_t)W * eb);
+  }
+}
+
 /* Write new tokens into the caches (the step before the path: a token's key
  * and latent row must be in place before a query sees it, [GLM-A100] "The
  * model": every earlier token is scored, the query's own included).  Token i
- * (sequence seq ? seq[i] : 0, position pos[i]):
- *   - keys (may be NULL): fp8 cache: s = oracle_key_scale(row), byte d =
- *     oracle_e4m3fn_quantize(k[d] / s) with the division in float32, scale s;
- *     bf16 or f32 cache: the input bits copied (same dtype).
- *   - latent (may be NULL): the input row's bits copied (same dtype).
- * new_keys: [n_new][keys->width] in new_keys_dtype (f32 or bf16);
- * new_latent: [n_new][latent->width] in the latent cache's dtype. */
+ * (sequence seq ? seq[i] : 0, position pos[i]) goes to both caches (either may
+ * be NULL) through append_row: fp8 caches, keys or latent rows, are quantized
+ * with the row's own float32 scale; others are copied.
+ * new_keys: [n_new][keys->width] in new_keys_dtype; new_latent: [n_new]
+ * [latent->width] in new_latent_dtype (f32 or bf16). */
 void oracle_cache_append(const oracle_cache *keys, const void *new_keys, int new_keys_dtype,
-                         const oracle_cache *latent, const void *new_latent, const int32_t *seq,
-                         const int32_t *pos, int32_t n_new) {
+                         const oracle_cache *latent, const void *new_latent, int new_latent_dtype,
+                         const int32_t *seq, const int32_t *pos, int32_t n_new) {
   for (int32_t i = 0; i < n_new; ++i) {
     const int32_t b = seq ? seq[i] : 0;
     const int64_t t = pos[i];
-    if (keys) {
-      const int D = keys->width;
-      const int64_t block = keys->block_table
-          ? (int64_t)keys->block_table[(int64_t)b * keys->max_blocks + t / keys->block_size] : (int64_t)b;
-      const int64_t slot = t % keys->block_size;
-      uint8_t *row = (uint8_t *)keys->rows + block * keys->block_stride + slot * keys->row_stride;
-      if (keys->dtype == ORACLE_E4M3FN) {
-        float *k = (float *)malloc(sizeof(float) * (size_t)D);
-        for (int d = 0; d < D; ++d) k[d] = input_to_float(new_keys, (int64_t)i * D + d, new_keys_dtype);
-        const float s = oracle_key_scale(k, D);
-        for (int d = 0; d < D; ++d) row[d] = oracle_e4m3fn_quantize(k[d] / s);
-        ((float *)keys->scale)[block * keys->scale_block_stride + slot] = s;
-        free(k);
-      } else {
-        const int eb = elem_bytes(keys->dtype);
-        memcpy(row, (const uint8_t *)new_keys + (int64_t)i * D * eb, (size_t)D * eb);
-      }
-    }
-    if (latent) {
-      const int W = latent->width;
-      const int eb = elem_bytes(latent->dtype);
-      const int64_t block = latent->block_table
-          ? (int64_t)latent->block_table[(int64_t)b * latent->max_blocks + t / latent->block_size] : (int64_t)b;
-      const int64_t slot = t % latent->block_size;
-      uint8_t *row = (uint8_t *)latent->rows + block * latent->block_stride + slot * latent->row_stride;
-      memcpy(row, (const uint8_t *)new_latent + (int64_t)i * W * eb, (size_t)W * eb);
-    }
+    if (keys) append_row(keys, new_keys, new_keys_dtype, i, b, t);
+    if (latent) append_row(latent, new_latent, new_latent_dtype, i, b, t);
   }
 }
 

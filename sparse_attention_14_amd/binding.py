@@ -78,7 +78,7 @@ def load(path: str = LIB_PATH):
         "dsa_decode_shared_workspace_size": (sz, [i32, i32, i32, i32, i32]),
         "mla_absorb_q": (ctypes.c_int, [P, P, P, ctypes.c_int, P, i32, i32, i32, i32, i32, P]),
         "mla_absorb_out": (ctypes.c_int, [P, P, P, i32, i32, i32, i32, P]),
-        "dsa_cache_append": (ctypes.c_int, [CP, P, ctypes.c_int, CP, P, P, P, i32, P]),
+        "dsa_cache_append": (ctypes.c_int, [CP, P, ctypes.c_int, CP, P, ctypes.c_int, P, P, i32, P]),
         "dsa_workspace_clear": (ctypes.c_int, [P, sz, P]),
         "dsa_status_string": (ctypes.c_char_p, [ctypes.c_int]),
     }
@@ -226,15 +226,18 @@ def mla_absorb_out(out, o_lat, w_uv, stream=None):
 
 
 def dsa_cache_append(keys: Optional[DeviceCache], new_keys, new_keys_dtype, latent: Optional[DeviceCache],
-                     new_latent, pos, seq=None, stream=None):
+                     new_latent, pos, seq=None, new_latent_dtype=None, stream=None):
     """Write new tokens (rows of new_keys / new_latent) at positions pos of
-    sequences seq into the caches (see include/dsa.h); either cache may be None."""
+    sequences seq into the caches (see include/dsa.h); either cache may be None.
+    new_latent_dtype defaults to the latent cache's dtype (bf16 for fp8 caches)."""
     lib = load()
     n = pos.shape[0]
+    if new_latent_dtype is None:
+        new_latent_dtype = "bf16" if latent is None or latent.dtype == "e4m3fn" else latent.dtype
     _check("dsa_cache_append", lib.dsa_cache_append(
         None if keys is None else ctypes.byref(keys.desc), _p(new_keys), DTYPES[new_keys_dtype],
-        None if latent is None else ctypes.byref(latent.desc), _p(new_latent), _p(seq), _p(pos), n,
-        _stream(stream)))
+        None if latent is None else ctypes.byref(latent.desc), _p(new_latent), DTYPES[new_latent_dtype], _p(seq),
+        _p(pos), n, _stream(stream)))
 
 
 def dsa_workspace_clear(workspace, stream=None):

@@ -1,10 +1,11 @@
 // Cache append: the new tokens' indexer keys and latent rows written into
 // contiguous or paged caches, the step that puts a token in place before any
 // query sees it ("GLM on an A100, in Vx", section "The model": a query scores
-// every earlier token, its own included).  fp8 key caches receive e4m3fn bytes
-// with a float32 scale per token ("INT4, FP8 and BF16": FP8 is E4M3 with float32
-// scales): s = max(amax / 448, 2^-126), byte = nearest e4m3fn code of k / s
-// (ties to even, saturating at 448), every decision in float32.
+// every earlier token, its own included).  fp8 caches (keys, or latent rows)
+// receive e4m3fn bytes with a float32 scale per token ("INT4, FP8 and BF16":
+// FP8 is E4M3 with float32 scales): s = max(amax / 448, 2^-126) over the row,
+// byte = nearest e4m3fn code of x / s (ties to even, saturating at 448), every
+// decision in float32.
 #include "kernels.hpp"
 
 namespace dsa {
@@ -52,82 +53,82 @@ __device__ __forceinline__ uint8_t *row_ptr(const CacheDev &c, int seq, int t, i
   return const_cast<uint8_t *>(cache_row(c, block, slot));
 }
 
+struct AppendCache {
+  CacheDev c;
+  int dt;              // cache dtype; -1: this cache is not written
+  const uint8_t *src;  // [n_new][width] new rows
+  int src_dt;          // dtype of the new rows (kF32 or kBF16; the cache's own dtype for copies)
+};
+
 struct AppendArgs {
-  CacheDev keys;
-  int key_dt;          // -1: no key cache
-  const uint8_t *new_keys;
-  int new_key_dt;      // kF32 or kBF16
-  CacheDev latent;
-  int has_latent;
-  const uint8_t *new_latent;
-  int latent_row_bytes;
+  AppendCache cache[2];   // keys, latent
   const int32_t *seq;
   const int32_t *pos;
 };
+
+constexpr int kMaxQuantWidth = 1024;   // elements of an fp8 row quantized by one wavefront
+
+// Token i's row into cache slot (b, t): fp8 caches quantized with the row's
+// own scale, other caches copied as 16-byte chunks.
+__device__ __forceinline__ void write_row(const AppendCache &w, int i, int b, int t, int lane) {
+  const int W = w.c.width;
+  int64_t block;
+  int slot;
+  uint8_t *dst = row_ptr(w.c, b, t, block, slot);
+  if (w.dt == kFP8) {
+    // lane l holds elements l + 64 j
+    float v[kMaxQuantWidth / 64];
+    float am = 0.0f;
+#pragma unroll
+    for (int j = 0; j < kMaxQuantWidth / 64; ++j) {
+      const int d = lane + 64 * j;
+      float x = 0.0f;
+      if (d < W) {
+        const int64_t e = (int64_t)i * W + d;
+        x = w.src_dt == kBF16 ? bf16_bits_to_float(reinterpret_cast<const uint16_t *>(w.src)[e])
+                              : reinterpret_cast<const float *>(w.src)[e];
+      }
+      v[j] = x;
+      am = fmaxf(am, fabsf(x));
+    }
+    const float s = fmaxf(wave_max(am) / 448.0f, 0x1p-126f);
+#pragma unroll
+    for (int j = 0; j < kMaxQuantWidth / 64; ++j) {
+      const int d = lane + 64 * j;
+      if (d < W) dst[d] = (uint8_t)e4m3fn_code(v[j] / s);
+    }
+    if (lane == 0) const_cast<float *>(w.c.scale)[block * w.c.scale_block_stride + slot] = s;
+  } else {
+    const int eb = w.dt == kF32 ? 4 : 2;
+    const int chunks = W * eb / 16;
+    const u32x4 *src = reinterpret_cast<const u32x4 *>(w.src + (int64_t)i * W * eb);
+    for (int c = lane; c < chunks; c += kAppendThreads) reinterpret_cast<u32x4 *>(dst)[c] = src[c];
+  }
+}
 
 __global__ __launch_bounds__(kAppendThreads) void append_kernel(AppendArgs a) {
   const int i = blockIdx.x;
   const int lane = threadIdx.x;
   const int b = a.seq ? a.seq[i] : 0;
   const int t = a.pos[i];
-  if (a.key_dt >= 0) {
-    const int D = a.keys.width;
-    int64_t block;
-    int slot;
-    uint8_t *dst = row_ptr(a.keys, b, t, block, slot);
-    if (a.key_dt == kFP8) {
-      // Lane l holds elements l and l + 64 (widths up to 128).
-      float v[2];
-#pragma unroll
-      for (int j = 0; j < 2; ++j) {
-        const int d = lane + 64 * j;
-        float x = 0.0f;
-        if (d < D) {
-          const int64_t e = (int64_t)i * D + d;
-          x = a.new_key_dt == kBF16 ? bf16_bits_to_float(reinterpret_cast<const uint16_t *>(a.new_keys)[e])
-                                    : reinterpret_cast<const float *>(a.new_keys)[e];
-        }
-        v[j] = x;
-      }
-      const float amax = wave_max(fmaxf(fabsf(v[0]), fabsf(v[1])));
-      const float s = fmaxf(amax / 448.0f, 0x1p-126f);
-#pragma unroll
-      for (int j = 0; j < 2; ++j) {
-        const int d = lane + 64 * j;
-        if (d < D) dst[d] = (uint8_t)e4m3fn_code(v[j] / s);
-      }
-      if (lane == 0) const_cast<float *>(a.keys.scale)[block * a.keys.scale_block_stride + slot] = s;
-    } else {
-      const int eb = a.key_dt == kF32 ? 4 : 2;
-      const int chunks = D * eb / 16;
-      const u32x4 *src = reinterpret_cast<const u32x4 *>(a.new_keys + (int64_t)i * D * eb);
-      for (int c = lane; c < chunks; c += kAppendThreads) reinterpret_cast<u32x4 *>(dst)[c] = src[c];
-    }
-  }
-  if (a.has_latent) {
-    int64_t block;
-    int slot;
-    uint8_t *dst = row_ptr(a.latent, b, t, block, slot);
-    const int chunks = a.latent_row_bytes / 16;
-    const u32x4 *src = reinterpret_cast<const u32x4 *>(a.new_latent + (int64_t)i * a.latent_row_bytes);
-    for (int c = lane; c < chunks; c += kAppendThreads) reinterpret_cast<u32x4 *>(dst)[c] = src[c];
-  }
+  if (a.cache[0].dt >= 0) write_row(a.cache[0], i, b, t, lane);
+  if (a.cache[1].dt >= 0) write_row(a.cache[1], i, b, t, lane);
 }
 
 }  // namespace
 
 hipError_t launch_cache_append(const CacheDev *keys, int key_dt, const void *new_keys, int new_key_dt,
-                               const CacheDev *latent, int latent_row_bytes, const void *new_latent,
+                               const CacheDev *latent, int latent_dt, const void *new_latent, int new_latent_dt,
                                const int32_t *seq, const int32_t *pos, int n_new, hipStream_t stream) {
   AppendArgs a{};
-  a.key_dt = keys ? key_dt : -1;
-  if (keys) a.keys = *keys;
-  a.new_keys = static_cast<const uint8_t *>(new_keys);
-  a.new_key_dt = new_key_dt;
-  a.has_latent = latent != nullptr;
-  if (latent) a.latent = *latent;
-  a.new_latent = static_cast<const uint8_t *>(new_latent);
-  a.latent_row_bytes = latent_row_bytes;
+  a.cache[0].dt = keys ? key_dt : -1;
+  if (keys) a.cache[0].c = *keys;
+  a.cache[0].src = static_cast<const uint8_t *>(new_keys);
+  a.cache[0].src_dt = new_key_dt;
+  a.cache[1].dt = latent ? latent_dt : -1;
+  if (latent) a.cache[1].c = *latent;
+  a.cache[1].src = static_cast<const uint8_t *>(new_latent);
+  a.cache[1].src_dt = new_latent_dt;
   a.seq = seq;
   a.pos = pos;
   hipLaunchKernelGGL(append_kernel, dim3(n_new), dim3(kAppendThreads), 0, stream, a);

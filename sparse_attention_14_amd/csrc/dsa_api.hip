@@ -78,7 +78,8 @@ dsa_status check_attend(const void *q, dsa_dtype q_dtype, const dsa_cache *laten
   dsa_status s = check_cache(latent);
   if (s != DSA_OK) return s;
   if (n_heads <= 0 || kv_lora <= 0 || kv_lora > latent->width) return DSA_ERR_INVALID_ARGUMENT;
-  if (q_dtype != latent->dtype) return DSA_ERR_UNSUPPORTED;
+  // bf16 queries read bf16 latent rows or e4m3fn rows with per-token scales
+  if (q_dtype != latent->dtype && !(q_dtype == DSA_BF16 && latent->dtype == DSA_FP8_E4M3FN)) return DSA_ERR_UNSUPPORTED;
   if (q_dtype == DSA_BF16) {
     if (latent->width != 576 || kv_lora != 512 || (n_heads % 16) || n_heads > 128) return DSA_ERR_UNSUPPORTED;
   } else if (q_dtype == DSA_F32) {
@@ -91,6 +92,12 @@ dsa_status check_attend(const void *q, dsa_dtype q_dtype, const dsa_cache *laten
 }
 
 dsa_status from_hip(hipError_t e) { return e == hipSuccess ? DSA_OK : DSA_ERR_DEVICE; }
+
+// What the attention kernels take as their dtype: the query's, or kFP8 for
+// bf16 queries over an fp8 latent cache (the split plan is the bf16 one).
+int attend_dtype(dsa_dtype q_dtype, const dsa_cache *latent) {
+  return latent->dtype == DSA_FP8_E4M3FN ? (int)kFP8 : (int)q_dtype;
+}
 
 size_t round256(size_t b) { return (b + 255) / 256 * 256; }
 
@@ -204,7 +211,7 @@ dsa_status mla_sparse_attend(float *out, float *lse, const void *q, dsa_dtype q_
   if (k > kMaxTopk) return DSA_ERR_UNSUPPORTED;
   const AttendPlan p = plan_attend(n_q, n_heads, kv_lora, latent->width, k, q_dtype);
   if (p.total > 0 && (!workspace || workspace_bytes < p.total)) return DSA_ERR_WORKSPACE_TOO_SMALL;
-  return from_hip(launch_attend(out, lse, q, q_dtype, to_dev(latent), kv_lora, indices, k, q_seq, 0, n_q, n_heads,
+  return from_hip(launch_attend(out, lse, q, attend_dtype(q_dtype, latent), to_dev(latent), kv_lora, indices, k, q_seq, 0, n_q, n_heads,
                                 softmax_scale, p, workspace, static_cast<hipStream_t>(stream)));
 }
 
@@ -281,7 +288,7 @@ dsa_status decode_impl(float *out, float *lse, const void *q_idx, dsa_dtype q_id
   e = launch_topk(idx, nullptr, scores, ld, q_len, L.tp, ws_topk, bounds, L.n_bounds,
                   score_group_tokens(score_rows, max_len), st);
   if (e != hipSuccess) return DSA_ERR_DEVICE;
-  e = launch_attend(out, lse, q_mla, q_mla_dtype, to_dev(latent), kv_lora, idx, k, q_seq, seq_ident, n_q,
+  e = launch_attend(out, lse, q_mla, attend_dtype(q_mla_dtype, latent), to_dev(latent), kv_lora, idx, k, q_seq, seq_ident, n_q,
                     mla_heads, softmax_scale, A.ap, ws_att, st);
   return from_hip(e);
 }
@@ -333,7 +340,7 @@ dsa_status dsa_decode_shared(float *out, float *lse, const void *q_mla, dsa_dtyp
   const size_t need = dsa_decode_shared_workspace_size(batch, window, k, mla_heads, kv_lora);
   if (need > 0 && (!workspace || workspace_bytes < need)) return DSA_ERR_WORKSPACE_TOO_SMALL;
   const AttendPlan p = plan_attend(n_q, mla_heads, kv_lora, latent->width, k, q_mla_dtype);
-  return from_hip(launch_attend(out, lse, q_mla, q_mla_dtype, to_dev(latent), kv_lora, indices, k, nullptr, window,
+  return from_hip(launch_attend(out, lse, q_mla, attend_dtype(q_mla_dtype, latent), to_dev(latent), kv_lora, indices, k, nullptr, window,
                                 n_q, mla_heads, softmax_scale, p, workspace, static_cast<hipStream_t>(stream)));
 }
 
@@ -366,40 +373,40 @@ dsa_status mla_absorb_out(float *out, const float *o_lat, const void *w_uv, int3
 }
 
 dsa_status dsa_cache_append(const dsa_cache *keys, const void *new_keys, dsa_dtype new_keys_dtype,
-                            const dsa_cache *latent, const void *new_latent, const int32_t *seq,
-                            const int32_t *pos, int32_t n_new, void *stream) {
+                            const dsa_cache *latent, const void *new_latent, dsa_dtype new_latent_dtype,
+                            const int32_t *seq, const int32_t *pos, int32_t n_new, void *stream) {
   if (n_new < 0 || !pos || (!keys && !latent)) return DSA_ERR_INVALID_ARGUMENT;
-  CacheDev kd{}, ld{};
-  int key_bytes_in = 0;
-  if (keys) {
-    dsa_status s = check_cache(keys);
+  // one cache's checks: fp8 caches quantize f32 / bf16 rows up to 1024 wide;
+  // others copy rows of their own dtype (16-byte multiples, aligned input)
+  auto check = [](const dsa_cache *c, const void *src, dsa_dtype src_dt, CacheDev &dev) -> dsa_status {
+    dsa_status s = check_cache(c);
     if (s != DSA_OK) return s;
-    if (!new_keys || !valid_dtype(new_keys_dtype)) return DSA_ERR_INVALID_ARGUMENT;
-    if (keys->dtype == DSA_FP8_E4M3FN) {
-      if (new_keys_dtype != DSA_F32 && new_keys_dtype != DSA_BF16) return DSA_ERR_UNSUPPORTED;
-      if (keys->width > 128) return DSA_ERR_UNSUPPORTED;
-      key_bytes_in = elem_bytes(new_keys_dtype);
-      if (reinterpret_cast<uintptr_t>(new_keys) % key_bytes_in) return DSA_ERR_UNSUPPORTED;
+    if (!src || !valid_dtype(src_dt)) return DSA_ERR_INVALID_ARGUMENT;
+    if (c->dtype == DSA_FP8_E4M3FN) {
+      if (src_dt != DSA_F32 && src_dt != DSA_BF16) return DSA_ERR_UNSUPPORTED;
+      if (c->width > 1024) return DSA_ERR_UNSUPPORTED;
+      if (reinterpret_cast<uintptr_t>(src) % elem_bytes(src_dt)) return DSA_ERR_UNSUPPORTED;
     } else {
-      if (new_keys_dtype != keys->dtype) return DSA_ERR_UNSUPPORTED;
-      if (((int64_t)keys->width * elem_bytes(keys->dtype)) % 16 || !aligned16(new_keys)) return DSA_ERR_UNSUPPORTED;
+      if (src_dt != c->dtype) return DSA_ERR_UNSUPPORTED;
+      if (((int64_t)c->width * elem_bytes(c->dtype)) % 16 || !aligned16(src)) return DSA_ERR_UNSUPPORTED;
     }
-    kd = to_dev(keys);
-  }
-  int latent_row_bytes = 0;
-  if (latent) {
-    dsa_status s = check_cache(latent);
+    dev = to_dev(c);
+    return DSA_OK;
+  };
+  CacheDev kd{}, ld{};
+  if (keys) {
+    dsa_status s = check(keys, new_keys, new_keys_dtype, kd);
     if (s != DSA_OK) return s;
-    if (!new_latent) return DSA_ERR_INVALID_ARGUMENT;
-    if (latent->dtype == DSA_FP8_E4M3FN) return DSA_ERR_UNSUPPORTED;
-    latent_row_bytes = latent->width * elem_bytes(latent->dtype);
-    if (latent_row_bytes % 16 || !aligned16(new_latent)) return DSA_ERR_UNSUPPORTED;
-    ld = to_dev(latent);
+  }
+  if (latent) {
+    dsa_status s = check(latent, new_latent, new_latent_dtype, ld);
+    if (s != DSA_OK) return s;
   }
   if (n_new == 0) return DSA_OK;
   return from_hip(launch_cache_append(keys ? &kd : nullptr, keys ? (int)keys->dtype : -1, new_keys,
-                                      (int)new_keys_dtype, latent ? &ld : nullptr, latent_row_bytes, new_latent,
-                                      seq, pos, n_new, static_cast<hipStream_t>(stream)));
+                                      (int)new_keys_dtype, latent ? &ld : nullptr, latent ? (int)latent->dtype : -1,
+                                      new_latent, (int)new_latent_dtype, seq, pos, n_new,
+                                      static_cast<hipStream_t>(stream)));
 }
 
 }  // extern "C"

@@ -72,10 +72,10 @@ hipError_t launch_window_rows(const int32_t *seq_len, int batch, int window, int
 
 // ---- cache append -----------------------------------------------------------
 // Token i (sequence seq ? seq[i] : 0, position pos[i]) of new_keys / new_latent
-// is written into the caches; fp8 key caches are quantized with a per-token
-// scale.  Either cache may be null.  latent_row_bytes: the latent input row.
+// is written into the caches; fp8 caches (up to 1024 wide) are quantized with a
+// per-token scale, others copied.  Either cache may be null.
 hipError_t launch_cache_append(const CacheDev *keys, int key_dt, const void *new_keys, int new_key_dt,
-                               const CacheDev *latent, int latent_row_bytes, const void *new_latent,
+                               const CacheDev *latent, int latent_dt, const void *new_latent, int new_latent_dt,
                                const int32_t *seq, const int32_t *pos, int n_new, hipStream_t stream);
 
 // ---- absorbed-MLA projections -------------------------------------------------

@@ -89,12 +89,16 @@ constexpr int kTeams = 2;
 constexpr int kStepRows = kTile * kTeams;    // 128
 constexpr int kAttThreads = 256 * kTeams;    // 512
 
-template <bool SPLIT>
+// F8: e4m3fn latent rows with a float32 scale per token.  The bytes are
+// decoded exactly to bf16 on their way into LDS; the token's scale multiplies
+// its logit (after the QK^T MFMA) and its probability as a PV weight.
+template <bool SPLIT, bool F8>
 __global__ __launch_bounds__(kAttThreads) void attend_bf16_kernel(AttArgs a) {
   __shared__ __align__(16) uint8_t lrows[kTeams][kTile * kRowBytes];
   __shared__ __align__(16) uint16_t lp[kTeams][2][kHG * kTile];  // P hi / lo, [head][row]
   __shared__ float red[kTeams][2][4][kHG];
   __shared__ uint8_t lvalid[kStepRows];
+  __shared__ float lscale[F8 ? kStepRows : 1];
 
   // XCD-aware mapping: workgroup ids i, i+8, i+16, ... run on one XCD; give the
   // n_hg head groups of a (query, split) pair ids 8 apart.
@@ -144,25 +148,42 @@ __global__ __launch_bounds__(kAttThreads) void attend_bf16_kernel(AttArgs a) {
     {
       const int j = j0 + step * kStepRows + gr;
       const int t = j < j1 ? a.indices[(int64_t)qi * a.k + j] : -1;
-      u32x4 v[kPer];
+      constexpr int NV = F8 ? kPer / 2 : kPer;   // fp8 rows are half as wide
+      u32x4 v[NV];
+      float sc = 0.0f;
       if (t >= 0) {
         int slot;
         const int64_t blk = cache_block(a.latent, seq, t, slot);
         const uint8_t *p = cache_row(a.latent, blk, slot) + 16 * gq;
 #pragma unroll
-        for (int i = 0; i < kPer; ++i) v[i] = load16(p + 64 * i);
+        for (int i = 0; i < NV; ++i) v[i] = load16(p + 64 * i);
+        if (F8) sc = a.latent.scale[blk * a.latent.scale_block_stride + slot];
       } else {
 #pragma unroll
-        for (int i = 0; i < kPer; ++i) v[i] = u32x4{0, 0, 0, 0};
+        for (int i = 0; i < NV; ++i) v[i] = u32x4{0, 0, 0, 0};
       }
       if (step == 0) {
 #pragma unroll
         for (int ks = 0; ks < kW / 32; ++ks) qa[ks] = as_bf16x8(load16(qr + 32 * ks));
       }
-      if (gq == 0) lvalid[gr] = t >= 0 ? 1 : 0;
-      uint8_t *dst = lrows[gr / kTile] + (gr % kTile) * kRowBytes + 16 * gq;
+      if (gq == 0) {
+        lvalid[gr] = t >= 0 ? 1 : 0;
+        if (F8) lscale[gr] = sc;
+      }
+      uint8_t *row_base = lrows[gr / kTile] + (gr % kTile) * kRowBytes;
+      if (F8) {
+        // fp8 chunk gq + 4 i (bytes 16 (gq + 4 i) ..) -> 16 bf16 at LDS bytes 32 (gq + 4 i) ..
 #pragma unroll
-      for (int i = 0; i < kPer; ++i) *reinterpret_cast<u32x4 *>(dst + 64 * i) = v[i];
+        for (int i = 0; i < NV; ++i) {
+          uint8_t *dst = row_base + 32 * gq + 128 * i;
+          *reinterpret_cast<bf16x8 *>(dst) = fp8x8_to_bf16x8(v[i][0], v[i][1]);
+          *reinterpret_cast<bf16x8 *>(dst + 16) = fp8x8_to_bf16x8(v[i][2], v[i][3]);
+        }
+      } else {
+        uint8_t *dst = row_base + 16 * gq;
+#pragma unroll
+        for (int i = 0; i < NV; ++i) *reinterpret_cast<u32x4 *>(dst + 64 * i) = v[i];
+      }
     }
     __syncthreads();
 
@@ -178,10 +199,11 @@ __global__ __launch_bounds__(kAttThreads) void attend_bf16_kernel(AttArgs a) {
       }
     }
     const bool valid = lvalid[team * kTile + row] != 0;
+    const float rs = F8 ? lscale[team * kTile + row] : 1.0f;   // the row's dequantization scale
     float z[4], mx[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      z[i] = valid ? sacc[i] * a.scale_log2 : -INFINITY;
+      z[i] = valid ? (F8 ? sacc[i] * rs : sacc[i]) * a.scale_log2 : -INFINITY;
       mx[i] = row16_max(z[i]);
     }
     if (l16 == 0)
@@ -199,8 +221,9 @@ __global__ __launch_bounds__(kAttThreads) void attend_bf16_kernel(AttArgs a) {
       const float mu = m_new[i] == -INFINITY ? 0.0f : m_new[i];
       alpha[i] = exp2f(m_run[i] - mu);
       const float p = exp2f(z[i] - mu);
-      const uint16_t hi = float_to_bf16_bits(p);
-      const uint16_t lo = float_to_bf16_bits(p - bf16_bits_to_float(hi));
+      const float pv = F8 ? p * rs : p;       // weight of the decoded (unscaled) row
+      const uint16_t hi = float_to_bf16_bits(pv);
+      const uint16_t lo = float_to_bf16_bits(pv - bf16_bits_to_float(hi));
       my_p[h * kTile + row] = hi;
       my_p[kHG * kTile + h * kTile + row] = lo;
       ps[i] = row16_sum(p);
@@ -314,12 +337,13 @@ constexpr int kWideStep = 64;
 constexpr int kWideThreads = 512;
 constexpr int kWidePer = kW * 2 / 16 / 8;   // 16-byte chunks per thread and row (9)
 
-template <bool SPLIT>
+template <bool SPLIT, bool F8>
 __global__ __launch_bounds__(kWideThreads) void attend_wide_kernel(AttArgs a) {
   __shared__ __align__(16) uint8_t rows[kWideStep * kRowBytes];
   __shared__ __align__(16) uint16_t lp[4][2][kHG * kWideStep];   // per head group: P hi / lo, [head][row]
   __shared__ float red[4][2][2][kHG];                             // [head group][max | sum][row half][head]
   __shared__ uint8_t lvalid[kWideStep];
+  __shared__ float lscale[F8 ? kWideStep : 1];
 
   const int H = a.n_heads;
   const int n_hb = H / kWideHeads;
@@ -338,8 +362,11 @@ __global__ __launch_bounds__(kWideThreads) void attend_wide_kernel(AttArgs a) {
   const int nsteps = (j1 - j0 + kWideStep - 1) / kWideStep;
 
   // gather role: row gr of a step, chunks gq + 8 i (i < 9), 128 contiguous bytes per load
+  // (fp8 rows: 36 chunks, i < 5, the last only for gq < 4)
   const int gr = tid >> 3, gq = tid & 7;
-  u32x4 v[kWidePer];
+  constexpr int NV = F8 ? 5 : kWidePer;
+  u32x4 v[NV];
+  float v_sc = 0.0f;
   bool v_ok;
   auto load_rows = [&](int step) {
     const int j = j0 + step * kWideStep + gr;
@@ -348,9 +375,10 @@ __global__ __launch_bounds__(kWideThreads) void attend_wide_kernel(AttArgs a) {
     v_ok = t >= 0;
     int slot;
     const int64_t blk = cache_block(a.latent, seq, v_ok ? t : 0, slot);
-    const uint8_t *src = (v_ok ? cache_row(a.latent, blk, slot) : a.latent.rows) + 16 * gq;
+    const uint8_t *src = v_ok ? cache_row(a.latent, blk, slot) : a.latent.rows;
 #pragma unroll
-    for (int i = 0; i < kWidePer; ++i) v[i] = load16(src + 128 * i);
+    for (int i = 0; i < NV; ++i) v[i] = load16(src + (F8 ? min(16 * gq + 128 * i, kW - 16) : 16 * gq + 128 * i));
+    if (F8) v_sc = v_ok ? a.latent.scale[blk * a.latent.scale_block_stride + slot] : 0.0f;
   };
   load_rows(0);
 
@@ -376,9 +404,22 @@ __global__ __launch_bounds__(kWideThreads) void attend_wide_kernel(AttArgs a) {
 
   for (int step = 0; step < nsteps; ++step) {
     {
-      uint8_t *dst = rows + gr * kRowBytes + 16 * gq;
+      if (F8) {
+        // fp8 chunk gq + 8 i -> 16 bf16 at LDS bytes 32 (gq + 8 i) ..
+        uint8_t *dst = rows + gr * kRowBytes + 32 * gq;
 #pragma unroll
-      for (int i = 0; i < kWidePer; ++i) *reinterpret_cast<u32x4 *>(dst + 128 * i) = v[i];
+        for (int i = 0; i < NV; ++i) {
+          if (i < NV - 1 || gq < 4) {
+            *reinterpret_cast<bf16x8 *>(dst + 256 * i) = fp8x8_to_bf16x8(v[i][0], v[i][1]);
+            *reinterpret_cast<bf16x8 *>(dst + 256 * i + 16) = fp8x8_to_bf16x8(v[i][2], v[i][3]);
+          }
+        }
+        if (gq == 0) lscale[gr] = v_sc;
+      } else {
+        uint8_t *dst = rows + gr * kRowBytes + 16 * gq;
+#pragma unroll
+        for (int i = 0; i < NV; ++i) *reinterpret_cast<u32x4 *>(dst + 128 * i) = v[i];
+      }
       if (gq == 0) lvalid[gr] = v_ok ? 1 : 0;
     }
     __syncthreads();
@@ -396,8 +437,9 @@ __global__ __launch_bounds__(kWideThreads) void attend_wide_kernel(AttArgs a) {
         sacc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
             qa[ks], as_bf16x8(*reinterpret_cast<const u32x4 *>(rp + 64 * ks)), sacc, 0, 0, 0);
       const bool valid = lvalid[row] != 0;
+      const float rs = F8 ? lscale[row] : 1.0f;
 #pragma unroll
-      for (int i = 0; i < 4; ++i) z[nt][i] = valid ? sacc[i] * a.scale_log2 : -INFINITY;
+      for (int i = 0; i < 4; ++i) z[nt][i] = valid ? (F8 ? sacc[i] * rs : sacc[i]) * a.scale_log2 : -INFINITY;
     }
     float mx[4];
 #pragma unroll
@@ -420,8 +462,9 @@ __global__ __launch_bounds__(kWideThreads) void attend_wide_kernel(AttArgs a) {
       for (int nt = 0; nt < 2; ++nt) {
         const int row = 32 * wr + 16 * nt + l16;
         const float p = exp2f(z[nt][i] - mu);
-        const uint16_t hi = float_to_bf16_bits(p);
-        const uint16_t lo = float_to_bf16_bits(p - bf16_bits_to_float(hi));
+        const float pv = F8 ? p * lscale[row] : p;   // weight of the decoded (unscaled) row
+        const uint16_t hi = float_to_bf16_bits(pv);
+        const uint16_t lo = float_to_bf16_bits(pv - bf16_bits_to_float(hi));
         my_p[h * kWideStep + row] = hi;
         my_p[kHG * kWideStep + h * kWideStep + row] = lo;
         pr[nt] = p;
@@ -687,11 +730,21 @@ hipError_t launch_attend(float *out, float *lse, const void *q, int dt, const Ca
   const int groups = (a.pairs + 7) / 8;
   const dim3 grid(groups * 8 * a.n_hg);
   const dim3 wide_grid(n_q * (n_heads / kWideHeads) * plan.splits);
+  const bool f8 = dt == kFP8;
+#define DSA_ATTEND(SP)                                                                                        \
+  do {                                                                                                        \
+    if (plan.wide) {                                                                                          \
+      if (f8) hipLaunchKernelGGL((attend_wide_kernel<SP, true>), wide_grid, dim3(kWideThreads), 0, stream, a); \
+      else hipLaunchKernelGGL((attend_wide_kernel<SP, false>), wide_grid, dim3(kWideThreads), 0, stream, a);   \
+    } else {                                                                                                  \
+      if (f8) hipLaunchKernelGGL((attend_bf16_kernel<SP, true>), grid, dim3(kAttThreads), 0, stream, a);       \
+      else hipLaunchKernelGGL((attend_bf16_kernel<SP, false>), grid, dim3(kAttThreads), 0, stream, a);         \
+    }                                                                                                         \
+  } while (0)
   if (plan.splits > 1) {
     a.part_o = reinterpret_cast<float *>(ws + plan.off_part_o);
     a.part_ml = reinterpret_cast<float *>(ws + plan.off_part_ml);
-    if (plan.wide) hipLaunchKernelGGL(attend_wide_kernel<true>, wide_grid, dim3(kWideThreads), 0, stream, a);
-    else hipLaunchKernelGGL(attend_bf16_kernel<true>, grid, dim3(kAttThreads), 0, stream, a);
+    DSA_ATTEND(true);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
 #define DSA_MERGE(NS)                                                                                         \
@@ -702,11 +755,10 @@ hipError_t launch_attend(float *out, float *lse, const void *q, int dt, const Ca
     else if (plan.splits <= 24) DSA_MERGE(24);
     else DSA_MERGE(32);
 #undef DSA_MERGE
-  } else if (plan.wide) {
-    hipLaunchKernelGGL(attend_wide_kernel<false>, wide_grid, dim3(kWideThreads), 0, stream, a);
   } else {
-    hipLaunchKernelGGL(attend_bf16_kernel<false>, grid, dim3(kAttThreads), 0, stream, a);
+    DSA_ATTEND(false);
   }
+#undef DSA_ATTEND
   return hipGetLastError();
 }
 

@@ -201,6 +201,24 @@ def _fill_cache_rows(storage_rows: np.ndarray, dtype: str, rng: np.random.Genera
         done += m
 
 
+def _fill_quantized_rows(storage_rows: np.ndarray, rng: np.random.Generator, sigma: float, count: int, width: int,
+                         chunk: int = 1 << 20) -> np.ndarray:
+    """fp8 rows of N(0, sigma) values stored the way a cache writer stores them:
+    per row s = max(max |x| / 448, 2^-126) in float32 and bytes = e4m3fn(x / s)
+    (torch's round-to-nearest-even cast).  Returns the float32 scales [count]."""
+    scales = np.empty(count, dtype=np.float32)
+    done = 0
+    rows_per_chunk = max(1, chunk // width)
+    while done < count:
+        m = min(rows_per_chunk, count - done)
+        x = rng.standard_normal((m, width), dtype=np.float32) * np.float32(sigma)
+        s = np.maximum(np.abs(x).max(axis=1) / np.float32(448), np.float32(2.0 ** -126)).astype(np.float32)
+        storage_rows[done:done + m] = to_e4m3fn_bits((x / s[:, None]).astype(np.float32))
+        scales[done:done + m] = s
+        done += m
+    return scales
+
+
 def _poison(storage: np.ndarray, dtype: str) -> None:
     eb = ELEM_BYTES[dtype]
     pat = np.array([_NAN_BITS[dtype]], dtype={1: np.uint8, 2: np.uint16, 4: np.uint32}[eb]).view(np.uint8)
@@ -257,10 +275,13 @@ def _make_cache(wl: Workload, lens, dtype, width, sigma, tag, layout, scale_rang
         if n == 0:
             continue
         logical = np.empty((n, width * eb), dtype=np.uint8)
-        _fill_cache_rows(logical, dtype, rng, sigma, n, width)
-        if scale is not None:
-            lo, hi = scale_range
-            sc = rng_s.uniform(lo, hi, size=n).astype(np.float32)
+        if dtype == "e4m3fn" and scale_range is None:
+            sc = _fill_quantized_rows(logical, rng, sigma, n, width)
+        else:
+            _fill_cache_rows(logical, dtype, rng, sigma, n, width)
+            if scale is not None:
+                lo, hi = scale_range
+                sc = rng_s.uniform(lo, hi, size=n).astype(np.float32)
         for (p, s0, t0, cnt) in runs:
             storage[p, s0:s0 + cnt] = logical[t0:t0 + cnt]
             if scale is not None:
@@ -371,6 +392,11 @@ PREFILL_64K = dataclasses.replace(DECODE_8K, name="prefill_chunk_2048_at_64k", w
 DECODE_128K_FP8_W4 = dataclasses.replace(DECODE_128K_FP8, name="decode_128k_fp8_window4", wid=5, window=4)
 PAGED_DECODE_W4 = dataclasses.replace(PAGED_DECODE, name="paged_decode_16x16k_32k_window4", wid=6, window=4)
 
+# fp8 latent rows (e4m3fn with a float32 scale per token, as the cache append
+# writes them): the memory-halving variant of the 128K batch
+DECODE_128K_FP8_LAT8 = dataclasses.replace(DECODE_128K_FP8, name="decode_128k_fp8_latent8", wid=7,
+                                           latent_dtype="e4m3fn")
+
 FULL_WORKLOADS = {w.name: w for w in (TINY_FP32, DECODE_8K, PAGED_DECODE, DECODE_128K_FP8, PREFILL_64K)}
 WINDOW_WORKLOADS = {w.name: w for w in (DECODE_128K_FP8_W4, PAGED_DECODE_W4)}
 
@@ -429,8 +455,8 @@ def append_tokens(p: Problem, window: int = 1, key_dtype: str = "bf16"):
 
     Returns (new_keys, new_latent, seq, pos): new_keys [n, idx_dim] raw bits in
     key_dtype ("bf16" -> uint16, "f32" -> float32) drawn N(0, key_sigma);
-    new_latent [n, kv_lora + rope] raw bits in the latent dtype drawn
-    N(0, latent_sigma); seq, pos int32 [n]."""
+    new_latent [n, kv_lora + rope] raw bits in the latent dtype (bf16 for an
+    fp8 latent cache) drawn N(0, latent_sigma); seq, pos int32 [n]."""
     wl = p.meta["workload"]
     lens = np.asarray(p.meta["seq_lens"], dtype=np.int64)
     seq, pos = [], []
@@ -445,7 +471,8 @@ def append_tokens(p: Problem, window: int = 1, key_dtype: str = "bf16"):
     nk = rng_for(wid, "append_keys").standard_normal((m, wl.idx_dim), dtype=np.float32) * np.float32(wl.key_sigma)
     W = wl.kv_lora + wl.rope
     nl = rng_for(wid, "append_latent").standard_normal((m, W), dtype=np.float32) * np.float32(wl.latent_sigma)
-    return (encode(nk, key_dtype), encode(nl, wl.latent_dtype), np.array(seq, dtype=np.int32),
+    latent_in = "bf16" if wl.latent_dtype == "e4m3fn" else wl.latent_dtype   # fp8 caches quantize bf16 rows
+    return (encode(nk, key_dtype), encode(nl, latent_in), np.array(seq, dtype=np.int32),
             np.array(pos, dtype=np.int32))
 
 

@@ -24,6 +24,8 @@ CASES = {
                               tie_fraction=0.0), 4, "f32"),
     "bf16_paged_w2": (S(inputs.PAGED_DECODE, name="a3", wid=503, batch=5, seq_len=(1, 700)), 2, "bf16"),
     "f32_tiny": (inputs.TINY_FP32, 1, "f32"),
+    "fp8_keys_fp8_latent_paged_w2": (S(inputs.DECODE_128K_FP8_LAT8, name="a4", wid=504, batch=3, seq_len=(10, 1000),
+                                       paged=True, tie_fraction=0.0), 2, "bf16"),
 }
 
 

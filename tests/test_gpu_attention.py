@@ -38,6 +38,18 @@ CASES = {
     "bf16_wide_split": (S(inputs.DECODE_8K, name="a8", wid=308, batch=20, seq_len=(1000, 5000)), 2048),
     "bf16_wide_h128": (S(inputs.DECODE_8K, name="a9", wid=309, batch=8, seq_len=(3000, 3000), mla_heads=128), 2048),
     "bf16_wide_short_rows": (S(inputs.PAGED_DECODE, name="a10", wid=310, batch=16, seq_len=(1, 300)), 2048),
+    # e4m3fn latent rows with a float32 scale per token: 16-head kernel (split), 64-head kernel (split, paged;
+    # unsplit, many queries)
+    "fp8lat_h64": (S(inputs.DECODE_128K_FP8_LAT8, name="a11", wid=311, batch=3, seq_len=(500, 4000),
+                     tie_fraction=0.0), 2048),
+    "fp8lat_one_query_many_splits": (S(inputs.DECODE_128K_FP8_LAT8, name="a12", wid=312, batch=1,
+                                       seq_len=(8192, 8192), tie_fraction=0.0), 2048),
+    "fp8lat_paged_wide_split": (S(inputs.DECODE_128K_FP8_LAT8, name="a13", wid=313, batch=20, seq_len=(100, 3000),
+                                  paged=True, tie_fraction=0.0), 2048),
+    "fp8lat_many_queries": (S(inputs.PREFILL_64K, name="a14", wid=314, seq_len=(2500, 2500), prefill_queries=300,
+                              latent_dtype="e4m3fn"), 256),
+    "fp8lat_peaky_q": (S(inputs.DECODE_128K_FP8_LAT8, name="a15", wid=315, batch=2, seq_len=(3000, 3000),
+                         q_mla_sigma=20.0, tie_fraction=0.0), 2048),
     "f32_tiny": (inputs.TINY_FP32, 256),
     "f32_h3_w44": (S(inputs.TINY_FP32, name="a7", wid=307, batch=3, seq_len=(10, 900), mla_heads=3, kv_lora=40,
                      rope=4), 300),

@@ -30,6 +30,7 @@ CASES = {
     "fp8_w4": S(inputs.DECODE_128K_FP8_W4, name="s3", wid=603, batch=2, seq_len=(3000, 12000)),
     "bf16_paged_w3_short": S(inputs.PAGED_DECODE_W4, name="s4", wid=604, batch=3, seq_len=(2, 2500), window=3),
     "f32_tiny": inputs.TINY_FP32,
+    "fp8_latent8_w1": S(inputs.DECODE_128K_FP8_LAT8, name="s5", wid=605, batch=3, seq_len=(2000, 9000)),
 }
 
 

@@ -25,6 +25,7 @@ CASES = {
     # long enough (n > the 12288-candidate buffer) for the score kernel's bounds to filter
     "fp8_long_bounded": S(inputs.DECODE_128K_FP8, name="d5", wid=405, batch=2, seq_len=(30000, 40000)),
     "bf16_paged_long_bounded": S(inputs.PAGED_DECODE, name="d6", wid=406, batch=3, seq_len=(13000, 26000)),
+    "fp8_latent8": S(inputs.DECODE_128K_FP8_LAT8, name="d8", wid=408, batch=2, seq_len=(5000, 20000)),
 }
 
 

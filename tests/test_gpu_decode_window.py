@@ -33,6 +33,7 @@ CASES = {
     "bf16_w8_short": S(inputs.DECODE_8K, name="w4", wid=504, batch=3, seq_len=(2, 2100), window=8),
     "bf16_w8_tiny": S(inputs.DECODE_8K, name="w6", wid=506, batch=2, seq_len=(3, 3), window=8),
     "bf16_paged_w4_bounded": S(inputs.PAGED_DECODE_W4, name="w5", wid=505, batch=2, seq_len=(13000, 26000)),
+    "fp8_latent8_w4": S(inputs.DECODE_128K_FP8_LAT8, name="w7", wid=507, batch=4, seq_len=(3000, 9000), window=4),
 }
 
 

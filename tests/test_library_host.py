@@ -167,9 +167,9 @@ def test_cache_append_validation(lib):
     lat = _cache(width=576, row_stride=1152, block_stride=1152 * 1024)
     f = lib.dsa_cache_append
 
-    def call(keys=keys8, nk=16, nk_dt=1, latent=lat, nl=16, pos=16, n=4):
+    def call(keys=keys8, nk=16, nk_dt=1, latent=lat, nl=16, nl_dt=1, pos=16, n=4):
         return f(None if keys is None else ctypes.byref(keys), nk, nk_dt,
-                 None if latent is None else ctypes.byref(latent), nl, None, pos, n, None)
+                 None if latent is None else ctypes.byref(latent), nl, nl_dt, None, pos, n, None)
 
     assert call(n=0) == 0                                             # nothing to do, no device call
     assert call(keys=None, n=0) == 0
@@ -179,14 +179,18 @@ def test_cache_append_validation(lib):
     assert call(nk=None) == 1
     assert call(nl=None) == 1
     assert call(nk_dt=7) == 1
+    assert call(nl_dt=7) == 1
     assert call(nk_dt=2) == 2                                         # fp8 input for an fp8 cache
     assert call(nk=17) == 2                                           # misaligned bf16 input
     assert call(keys=keys16, nk_dt=0) == 2                            # a bf16 cache takes bf16 input only
     assert call(keys=keys16, nk=8, n=0) == 2                          # copies need 16-byte aligned input
-    wide8 = _cache(dtype=2, width=256, row_stride=256, block_stride=256 * 1024, scale=16, sbs=1024)
-    assert call(keys=wide8) == 2                                      # fp8 keys up to 128 wide
+    assert call(nl_dt=0) == 2                                         # a bf16 latent cache copies bf16 rows
+    wide8 = _cache(dtype=2, width=2048, row_stride=2048, block_stride=2048 * 1024, scale=16, sbs=1024)
+    assert call(keys=wide8) == 2                                      # fp8 rows up to 1024 wide
     lat8 = _cache(dtype=2, width=576, row_stride=576, block_stride=576 * 1024, scale=16, sbs=1024)
-    assert call(latent=lat8, n=0) == 2
+    assert call(latent=lat8, n=0) == 0                                # fp8 latent rows quantized from bf16
+    assert call(latent=lat8, nl_dt=0, n=0) == 0                       # ... or from f32
+    assert call(latent=lat8, nl_dt=2, n=0) == 2
     odd = _cache(width=100, row_stride=208, block_stride=208 * 1024)
     assert call(latent=odd, n=0) == 2                                 # 200-byte rows are not 16-byte chunks
     noscale = _cache(dtype=2, row_stride=128, block_stride=128 * 1024)

@@ -151,3 +151,38 @@ def test_appended_fp8_keys_score_within_the_format_bound(oracle_mod):
     bound = np.einsum("bh,bhd,bnd->bn", np.abs(w).astype(np.float64), np.abs(q).astype(np.float64), err)
     assert np.all(np.abs(s8 - sx) <= bound)
     assert np.abs(s8 - sx).max() > 0                                 # the fp8 path really rounds
+
+
+def test_fp8_latent_append_and_attention(oracle_mod):
+    """A 576-wide latent row appended to an fp8 latent cache is quantized with
+    its own scale (largest magnitude -> 448, every byte within half a step);
+    attention over kept rows that are all that one row returns exactly the
+    decoded row's first kv_lora entries (e4m3fn(byte) * scale), and lse =
+    ln(count) + its logit."""
+    rng = np.random.default_rng(21)
+    W, L, n = 576, 512, 6
+    base = inputs.cache_from_values(np.zeros((1, n, W), np.float32), "e4m3fn", scale=np.ones((1, n), np.float32),
+                                    capacity_pad=2)
+    row = rng.normal(0, 0.05, W).astype(np.float32)
+    raw = inputs.encode(row[None, :], "bf16")
+    vals = (raw[0].astype(np.uint32) << 16).view(np.float32)
+    seq = np.zeros(n, np.int32)
+    pos = np.arange(n, dtype=np.int32)
+    _, lat = oracle_mod.cache_append(None, None, "bf16", base, np.repeat(raw, n, axis=0), seq, pos)
+    s = lat.scale[0, 0]
+    assert s == np.float32(np.abs(vals).max()) / np.float32(448)
+    dec = np.array([oracle_mod.e4m3fn_to_double(int(c)) for c in lat.storage[0, 0]])
+    assert np.abs(dec).max() == 448.0
+    x = (vals / s).astype(np.float64)
+    step = np.where(np.abs(x) >= 2.0 ** -6, 2.0 ** (np.floor(np.log2(np.maximum(np.abs(x), 1e-300))) - 3), 2.0 ** -9)
+    assert np.all(np.abs(dec - x) <= step / 2 * (1 + 1e-12))
+    for t in range(1, n):
+        assert np.array_equal(lat.storage[0, t], lat.storage[0, 0]) and lat.scale[0, t] == s
+    q = rng.normal(0, 1, (1, 4, W)).astype(np.float32)
+    idx = np.array([[0, 2, 3, 5, -1, -1]], np.int32)
+    scale = 1 / np.sqrt(W)
+    o, lse, _ = oracle_mod.mla_attend(q, "f32", lat, L, idx, np.zeros(1, np.int32), scale)
+    decoded = dec * np.float64(s)
+    assert np.allclose(o[0], np.broadcast_to(decoded[:L], (4, L)), rtol=1e-12, atol=1e-15)
+    z = scale * (q[0].astype(np.float64) @ decoded)
+    assert np.allclose(lse[0], np.log(4) + z, rtol=1e-12, atol=1e-12)
