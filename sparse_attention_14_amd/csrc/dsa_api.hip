@@ -252,9 +252,15 @@ dsa_status decode_impl(float *out, float *lse, const void *q_idx, dsa_dtype q_id
   if (s != DSA_OK) return s;
   if (k > kMaxTopk || max_len > kMaxLenTopk) return DSA_ERR_UNSUPPORTED;
   const int32_t n_q = batch * window;
-  // neighbouring queries of a window share each key load (bf16/fp8 keys, up to 32 heads)
-  const bool pairs = window % 2 == 0 && idx_heads <= 32 && q_idx_dtype != DSA_F32 && keys->width == 128;
-  const int32_t score_rows = pairs ? n_q / 2 : n_q;
+  // neighbouring queries of a window share each key load (bf16/fp8 keys, 128 wide, up to 32 heads):
+  // pairs of queries per wavefront (groups of 4 need more registers than leave two wavefronts per
+  // SIMD and were slower)
+  const bool shareable = idx_heads <= 32 && q_idx_dtype != DSA_F32 && keys->width == 128;
+  const int qw = shareable && window % 2 == 0 ? 2 : 1;
+  const int32_t score_rows = n_q / qw;
+  // bf16 queries: the score kernel derives a window's rows from the sequence
+  // lengths itself and hands their visible counts on; f32: a separate kernel
+  const bool rows_in_scores = window > 1 && q_idx_dtype != DSA_F32;
   // The workspace size query assumes the bf16 latent plan, which is the larger one.
   const StepLayout L = step_layout(n_q, max_len, k, mla_heads, kv_lora, kBF16, 576, window, score_rows);
   const StepLayout A = step_layout(n_q, max_len, k, mla_heads, kv_lora, q_mla_dtype, latent->width, window,
@@ -267,29 +273,36 @@ dsa_status decode_impl(float *out, float *lse, const void *q_idx, dsa_dtype q_id
   int32_t *idx = indices_out ? indices_out : reinterpret_cast<int32_t *>(ws + L.off_idx);
   void *ws_topk = ws + L.off_topk;
   void *ws_att = ws + L.off_att;
-  // the queries' sequences and visible counts
+  // the queries' sequences and visible counts: query i of a window belongs to
+  // sequence i / window (the attention takes that divisor)
   const int32_t *q_seq = nullptr;
-  const int32_t *q_len = seq_len;
+  const int32_t *q_len = seq_len;       // per query (single-token steps: per sequence)
   int seq_ident = 1;
+  int32_t *rl = reinterpret_cast<int32_t *>(ws + L.off_rows + round256((size_t)n_q * 4));
   if (window > 1) {
-    int32_t *rs = reinterpret_cast<int32_t *>(ws + L.off_rows);
-    int32_t *rl = reinterpret_cast<int32_t *>(ws + L.off_rows + round256((size_t)n_q * 4));
-    if (launch_window_rows(seq_len, batch, window, rs, rl, st) != hipSuccess) return DSA_ERR_DEVICE;
-    q_seq = rs;
+    if (!rows_in_scores) {
+      int32_t *rs = reinterpret_cast<int32_t *>(ws + L.off_rows);
+      if (launch_window_rows(seq_len, batch, window, rs, rl, st) != hipSuccess) return DSA_ERR_DEVICE;
+      q_seq = rs;
+      seq_ident = 0;
+    }
     q_len = rl;
-    seq_ident = 0;
   }
   // bf16/fp8 keys: the score kernel also reports the top-k's candidate bounds
   uint32_t *bounds = (L.tp.chunks > 1 && q_idx_dtype != DSA_F32)
                          ? reinterpret_cast<uint32_t *>(ws + L.off_bounds) : nullptr;
-  hipError_t e = launch_index_scores(scores, ld, q_idx, q_idx_dtype, w_idx, to_dev(keys), keys->dtype, q_seq,
-                                     seq_ident, q_len, n_q, idx_heads, max_len, ScoreBounds{bounds, k}, st, pairs);
+  hipError_t e =
+      rows_in_scores
+          ? launch_index_scores(scores, ld, q_idx, q_idx_dtype, w_idx, to_dev(keys), keys->dtype, nullptr, 0, seq_len,
+                                n_q, idx_heads, max_len, ScoreBounds{bounds, k}, st, qw, window, rl)
+          : launch_index_scores(scores, ld, q_idx, q_idx_dtype, w_idx, to_dev(keys), keys->dtype, q_seq, seq_ident,
+                                q_len, n_q, idx_heads, max_len, ScoreBounds{bounds, k}, st, qw);
   if (e != hipSuccess) return DSA_ERR_DEVICE;
   e = launch_topk(idx, nullptr, scores, ld, q_len, L.tp, ws_topk, bounds, L.n_bounds,
                   score_group_tokens(score_rows, max_len), st);
   if (e != hipSuccess) return DSA_ERR_DEVICE;
-  e = launch_attend(out, lse, q_mla, attend_dtype(q_mla_dtype, latent), to_dev(latent), kv_lora, idx, k, q_seq, seq_ident, n_q,
-                    mla_heads, softmax_scale, A.ap, ws_att, st);
+  e = launch_attend(out, lse, q_mla, attend_dtype(q_mla_dtype, latent), to_dev(latent), kv_lora, idx, k, q_seq,
+                    window > 1 ? (q_seq ? 0 : window) : seq_ident, n_q, mla_heads, softmax_scale, A.ap, ws_att, st);
   return from_hip(e);
 }
 

@@ -46,17 +46,23 @@ constexpr int kPrefillMinQueries = 64;   // the GEMM-shaped kernel takes over fr
 // base addresses are wavefront-uniform (scalar); a lane adds one precomputed
 // 32-bit offset per load.
 //
-// PAIR: the two M tiles are two queries of one sequence (rows 2 y and 2 y + 1,
+// QW = 2: the M tiles are two queries of one sequence (rows 2 y and 2 y + 1,
 // up to 32 heads each), e.g. neighbouring queries of a multi-token decode
 // window: every key tile is loaded once for both, each query keeps its own
-// visible count, score row and candidate bounds.  Otherwise the M tiles are
+// visible count, score row and candidate bounds.  QW = 1: the M tiles are
 // heads 0-31 and 32-63 of one query (row y).
-template <bool FP8, int D, int MT, int TPW, bool PAIR>
+//
+// window > 0: rows are the queries of multi-token windows, row i the (i % window)-th
+// of sequence i / window, whose visible count is q_len[i / window] - window + 1 +
+// i % window (at least 0; q_len then holds the sequences' lengths).  The
+// workgroups of the first key range write each row's count to row_len_out.
+template <bool FP8, int D, int MT, int TPW, int QW>
 __global__ __launch_bounds__(256) void scores_mfma_kernel(float *__restrict__ scores, int64_t ld,
                                                           const uint16_t *__restrict__ q, const float *__restrict__ w,
                                                           CacheDev keys, const int32_t *__restrict__ q_seq,
                                                           int seq_ident, const int32_t *__restrict__ q_len,
-                                                          int n_heads, uint32_t *__restrict__ bounds, int topk) {
+                                                          int n_heads, uint32_t *__restrict__ bounds, int topk,
+                                                          int window, int32_t *__restrict__ row_len_out) {
   constexpr int KS = D / 16;            // 32x32x16 K-steps
   constexpr int HALF = D / 2;           // dims held by one lane half
   constexpr int EB = FP8 ? 1 : 2;       // key element bytes
@@ -67,8 +73,9 @@ __global__ __launch_bounds__(256) void scores_mfma_kernel(float *__restrict__ sc
   constexpr int NLD = TILEB / 1024;     // 1 KB wavefront loads per tile
   constexpr int P = TPW < 2 ? TPW : 2;  // tiles in flight ahead of the one being scored
   static_assert(64 % CPR == 0, "a 1 KB load must cover whole rows");
-  static_assert(!PAIR || MT == 2, "a query pair uses both M tiles");
-  constexpr int NQ = PAIR ? 2 : 1;      // queries (score rows) of the wavefront
+  static_assert(QW == 1 || MT == QW, "a group of queries uses one M tile each");
+  constexpr bool MULTI = QW > 1;
+  constexpr int NQ = QW;                // queries (score rows) of the wavefront
   __shared__ __align__(16) uint8_t stage_all[4][TILEB];
 
   // Fetch every kernel argument at once: the compiler would otherwise load each
@@ -81,15 +88,24 @@ __global__ __launch_bounds__(256) void scores_mfma_kernel(float *__restrict__ sc
       : "=s"(zero)
       : "s"(scores), "s"(ld), "s"(q), "s"(w), "s"(keys.rows), "s"(keys.scale), "s"(keys.row_stride),
         "s"(keys.block_stride), "s"(keys.scale_block_stride), "s"(keys.table), "s"(keys.block_size),
-        "s"(keys.max_blocks), "s"(q_seq), "s"(seq_ident), "s"(q_len), "s"(n_heads), "s"(bounds), "s"(topk));
-  const int qi = PAIR ? 2 * blockIdx.y : blockIdx.y;   // first score row
+        "s"(keys.max_blocks), "s"(q_seq), "s"(seq_ident), "s"(q_len), "s"(n_heads), "s"(bounds), "s"(topk),
+        "s"(window), "s"(row_len_out));
+  const int qi = QW * blockIdx.y;   // first score row
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int half = lane >> 5, col = lane & 31;
   int nq[NQ];   // visible tokens of each row
+  if (window > 0) {
+    const int sl = q_len[qi / window], j0 = qi % window;
 #pragma unroll
-  for (int u = 0; u < NQ; ++u) nq[u] = q_len[qi + u];
-  const int n = PAIR ? (nq[0] > nq[NQ - 1] ? nq[0] : nq[NQ - 1]) : nq[0];
+    for (int u = 0; u < NQ; ++u) nq[u] = max(sl - window + 1 + j0 + u, 0);
+  } else {
+#pragma unroll
+    for (int u = 0; u < NQ; ++u) nq[u] = q_len[qi + u];
+  }
+  int n = nq[0];
+#pragma unroll
+  for (int u = 1; u < NQ; ++u) n = max(n, nq[u]);
   const int ntile = (n + 31) / 32;
   const int wid = blockIdx.x * 4 + wave + zero;
   const int tile_begin = wid * TPW;
@@ -98,7 +114,7 @@ __global__ __launch_bounds__(256) void scores_mfma_kernel(float *__restrict__ sc
   for (int u = 0; u < NQ; ++u) lane_best[u] = -__builtin_inff();
 
   if (tile_begin < ntile) {
-    const int seq = seq_of(q_seq, qi, seq_ident);
+    const int seq = window > 0 ? qi / window : seq_of(q_seq, qi, seq_ident);
     uint8_t *stage = stage_all[wave];
     // First row, first scale and last visible row of every tile (a 32-key tile
     // never straddles a block).  All of it is wavefront-uniform; the block
@@ -167,8 +183,8 @@ __global__ __launch_bounds__(256) void scores_mfma_kernel(float *__restrict__ sc
     float wr[MT][16];
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt) {
-      const int qm = PAIR ? qi + mt : qi;          // the tile's query
-      const int head = PAIR ? col : 32 * mt + col;
+      const int qm = MULTI ? qi + mt : qi;         // the tile's query
+      const int head = MULTI ? col : 32 * mt + col;
       const uint16_t *qrow = q + ((int64_t)qm * n_heads + (head < n_heads ? head : n_heads - 1)) * D + half * HALF;
 #pragma unroll
       for (int ks = 0; ks < KS; ++ks) {
@@ -176,10 +192,10 @@ __global__ __launch_bounds__(256) void scores_mfma_kernel(float *__restrict__ sc
         if (head >= n_heads) v = u32x4{0, 0, 0, 0};
         a[mt][ks] = as_bf16x8(v);
       }
-      // Accumulator element r of this lane is head (PAIR ? 0 : 32*mt) + 8*(r/4) + 4*half + r%4.
+      // Accumulator element r of this lane is head (MULTI ? 0 : 32*mt) + 8*(r/4) + 4*half + r%4.
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
-        const int m = (PAIR ? 0 : 32 * mt) + 8 * (r >> 2) + 4 * half + (r & 3);
+        const int m = (MULTI ? 0 : 32 * mt) + 8 * (r >> 2) + 4 * half + (r & 3);
         const float x = w[(int64_t)qm * n_heads + (m < n_heads ? m : n_heads - 1)];
         wr[mt][r] = m < n_heads ? x : 0.0f;
       }
@@ -225,7 +241,7 @@ __global__ __launch_bounds__(256) void scores_mfma_kernel(float *__restrict__ sc
         f32x16 acc = {};
 #pragma unroll
         for (int ks = 0; ks < KS; ++ks) acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[mt][ks], b[ks], acc, 0, 0, 0);
-        float &su = s[PAIR ? mt : 0];
+        float &su = s[MULTI ? mt : 0];
 #pragma unroll
         for (int r = 0; r < 16; ++r) su = fmaf(wr[mt][r], relu(__uint_as_float(__float_as_uint(acc[r]) ^ flip)), su);
       }
@@ -265,6 +281,14 @@ __global__ __launch_bounds__(256) void scores_mfma_kernel(float *__restrict__ sc
       }
       if (lane == 0) bounds[(int64_t)(qi + u) * gridDim.x * 4 + wid] = T;
     }
+  }
+  // window rows: the visible counts for the kernels that follow (last, so that
+  // no lane-dependent branch precedes the scalar code above)
+  if (window > 0 && row_len_out && blockIdx.x == 0 && wave == 0) {
+    int v = nq[0];
+#pragma unroll
+    for (int u = 1; u < NQ; ++u) v = lane == u ? nq[u] : v;
+    if (lane < NQ) row_len_out[qi + lane] = v;
   }
 }
 
@@ -522,19 +546,19 @@ __global__ __launch_bounds__(256) void scores_f32_kernel(float *__restrict__ sco
   }
 }
 
-template <bool FP8, int D, int MT, bool PAIR>
+template <bool FP8, int D, int MT, int QW>
 hipError_t run_mfma(float *scores, int64_t ld, const void *q, const float *w, const CacheDev &keys,
                     const int32_t *q_seq, int seq_ident, const int32_t *q_len, int n_q, int n_heads, int max_len,
-                    const ScoreBounds &sb, hipStream_t stream) {
-  const int rows = PAIR ? n_q / 2 : n_q;   // workgroup rows of the grid
+                    const ScoreBounds &sb, int window, int32_t *row_len_out, hipStream_t stream) {
+  const int rows = n_q / QW;   // workgroup rows of the grid
   const int tiles = (max_len + 31) / 32;
   const int tpw = score_tiles_per_wave(rows, max_len);
   const int gx = (tiles + 4 * tpw - 1) / (4 * tpw);
   dim3 grid(gx, rows);
   const uint16_t *qb = static_cast<const uint16_t *>(q);
 #define DSA_SK(T)                                                                                                  \
-  hipLaunchKernelGGL((scores_mfma_kernel<FP8, D, MT, T, PAIR>), grid, dim3(256), 0, stream, scores, ld, qb, w, keys, \
-                     q_seq, seq_ident, q_len, n_heads, sb.bounds, sb.topk)
+  hipLaunchKernelGGL((scores_mfma_kernel<FP8, D, MT, T, QW>), grid, dim3(256), 0, stream, scores, ld, qb, w, keys, \
+                     q_seq, seq_ident, q_len, n_heads, sb.bounds, sb.topk, window, row_len_out)
   switch (tpw) {
     case 1: DSA_SK(1); break;
     case 2: DSA_SK(2); break;
@@ -557,7 +581,7 @@ hipError_t run_f32(float *scores, int64_t ld, const void *q, const float *w, con
 
 hipError_t dispatch(float *scores, int64_t ld, const void *q, int q_dt, const float *w, const CacheDev &keys,
                     int key_dt, const int32_t *q_seq, int seq_ident, const int32_t *q_len, int n_q, int n_heads,
-                    int max_len, const ScoreBounds &sb, bool pairs, hipStream_t s) {
+                    int max_len, const ScoreBounds &sb, int qw, int window, int32_t *row_len_out, hipStream_t s) {
   const int D = keys.width;
   if (q_dt == kF32) {
     switch (D) {
@@ -570,7 +594,7 @@ hipError_t dispatch(float *scores, int64_t ld, const void *q, int q_dt, const fl
   }
   const bool fp8 = key_dt == kFP8;
   const bool two = n_heads > 32;
-  if (!fp8 && D == 128 && !two && n_q >= kPrefillMinQueries && !sb.bounds && !seq_ident) {
+  if (!fp8 && D == 128 && !two && n_q >= kPrefillMinQueries && !sb.bounds && !seq_ident && window == 0) {
     const int blocks = (n_q + kPQ - 1) / kPQ;
     // split the keys so that about 512 workgroups run
     int splits = (512 + blocks - 1) / blocks;
@@ -581,21 +605,23 @@ hipError_t dispatch(float *scores, int64_t ld, const void *q, int q_dt, const fl
                        static_cast<const uint16_t *>(q), w, keys, q_seq, q_len, n_q, n_heads, per);
     return hipGetLastError();
   }
-#define DSA_SC(F, DD, M, PR)                                                                                \
-  return run_mfma<F, DD, M, PR>(scores, ld, q, w, keys, q_seq, seq_ident, q_len, n_q, n_heads, max_len, sb, s)
-  if (pairs && !two && D == 128) {
-    if (fp8) DSA_SC(true, 128, 2, true);
-    DSA_SC(false, 128, 2, true);
+#define DSA_SC(F, DD, M, QWV)                                                                              \
+  return run_mfma<F, DD, M, QWV>(scores, ld, q, w, keys, q_seq, seq_ident, q_len, n_q, n_heads, max_len, sb, window, \
+                                 row_len_out, s)
+  if (qw == 2 && !two && D == 128) {
+    if (fp8) DSA_SC(true, 128, 2, 2);
+    DSA_SC(false, 128, 2, 2);
   }
+  if (qw != 1) return hipErrorInvalidValue;
   if (D == 128) {
-    if (fp8) { if (two) DSA_SC(true, 128, 2, false); DSA_SC(true, 128, 1, false); }
-    if (two) DSA_SC(false, 128, 2, false);
-    DSA_SC(false, 128, 1, false);
+    if (fp8) { if (two) DSA_SC(true, 128, 2, 1); DSA_SC(true, 128, 1, 1); }
+    if (two) DSA_SC(false, 128, 2, 1);
+    DSA_SC(false, 128, 1, 1);
   }
   if (D == 64) {
-    if (fp8) { if (two) DSA_SC(true, 64, 2, false); DSA_SC(true, 64, 1, false); }
-    if (two) DSA_SC(false, 64, 2, false);
-    DSA_SC(false, 64, 1, false);
+    if (fp8) { if (two) DSA_SC(true, 64, 2, 1); DSA_SC(true, 64, 1, 1); }
+    if (two) DSA_SC(false, 64, 2, 1);
+    DSA_SC(false, 64, 1, 1);
   }
 #undef DSA_SC
   return hipErrorInvalidValue;
@@ -606,10 +632,12 @@ hipError_t dispatch(float *scores, int64_t ld, const void *q, int q_dt, const fl
 hipError_t launch_index_scores(float *scores, int64_t ld, const void *q, int q_dt, const float *w,
                                const CacheDev &keys, int key_dt, const int32_t *q_seq, int seq_ident,
                                const int32_t *q_len, int n_q, int n_heads, int max_len, const ScoreBounds &sb,
-                               hipStream_t stream, bool pairs) {
-  if (pairs && ((n_q & 1) || keys.width != 128 || n_heads > 32 || q_dt == kF32)) return hipErrorInvalidValue;
-  return dispatch(scores, ld, q, q_dt, w, keys, key_dt, q_seq, seq_ident, q_len, n_q, n_heads, max_len, sb, pairs,
-                  stream);
+                               hipStream_t stream, int qw, int window, int32_t *row_len_out) {
+  if (qw != 1 && qw != 2) return hipErrorInvalidValue;
+  if (qw > 1 && (n_q % qw || keys.width != 128 || n_heads > 32 || q_dt == kF32)) return hipErrorInvalidValue;
+  if (window > 0 && (q_dt == kF32 || q_seq || n_q % window || window % qw)) return hipErrorInvalidValue;
+  return dispatch(scores, ld, q, q_dt, w, keys, key_dt, q_seq, seq_ident, q_len, n_q, n_heads, max_len, sb, qw,
+                  window, row_len_out, stream);
 }
 
 int score_tiles_per_wave(int n_q, int max_len) {

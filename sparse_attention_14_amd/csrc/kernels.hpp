@@ -19,14 +19,20 @@ struct ScoreBounds {
   uint32_t *bounds;  // [n_q][score_groups_per_row()] or nullptr
   int topk;
 };
-// pairs: rows 2 y and 2 y + 1 belong to one sequence (bf16/fp8 keys, <= 32
-// heads): each key tile is read once for both (decode windows).  n_q must be
-// even.  Bound groups are then laid out for a grid of n_q / 2 workgroup rows:
-// score_groups_per_row / score_group_tokens take that row count.
+// qw (1 or 2): rows 2 y and 2 y + 1 belong to one sequence when qw = 2 (bf16/fp8
+// keys, 128 wide, <= 32 heads): each key tile is read once for both (decode
+// windows).  n_q must be a multiple of qw.  Bound groups are then laid
+// out for a grid of n_q / qw workgroup rows: score_groups_per_row /
+// score_group_tokens take that row count.
+// window > 0 (bf16 q, q_seq null, n_q a multiple of window, window a multiple
+// of qw): row i is query i % window of sequence i / window, q_len holds the
+// sequence lengths [n_q / window] and the row's visible count is
+// max(q_len[i / window] - window + 1 + i % window, 0); row_len_out (nullable)
+// receives the counts [n_q].
 hipError_t launch_index_scores(float *scores, int64_t ld, const void *q, int q_dt, const float *w,
                                const CacheDev &keys, int key_dt, const int32_t *q_seq, int seq_ident,
                                const int32_t *q_len, int n_q, int n_heads, int max_len, const ScoreBounds &sb,
-                               hipStream_t stream, bool pairs = false);
+                               hipStream_t stream, int qw = 1, int window = 0, int32_t *row_len_out = nullptr);
 int score_tiles_per_wave(int rows, int max_len);
 int score_groups_per_row(int rows, int max_len);
 int score_group_tokens(int rows, int max_len);
