@@ -151,7 +151,7 @@ def main():
     args = parse()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported (the path is single-GPU; "
-              "multi-GPU sharding is described in DESIGN.md but not built)", file=sys.stderr)
+              "sharding across GPUs is not built)", file=sys.stderr)
         sys.exit(2)
 
     import numpy as np

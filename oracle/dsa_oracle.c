@@ -21,8 +21,7 @@
  *              decode, compressed request-local KV, stable softmax, FP8 E4M3FN
  *              decoding) and GPU section (split online-softmax compressed MLA).
  *
- * Readings where the pages leave a step open (each one is listed with its
- * reason in the design notes):
+ * Readings where the pages leave a step open:
  *   - score[s] = sum_h w[h] * max(0, sum_d q[h][d] * khat[s][d]); one key row per
  *     token shared by all indexer heads; no extra scale inside the indexer.
  *   - fp8 keys: khat = e4m3fn(byte) * scale[token] (float32 per-token scale).

@@ -97,3 +97,34 @@ def test_prefill_chunk_full_size_sampled():
                                         p.q_seq[srows], p.softmax_scale)
     worst = check_attention(out.cpu().numpy()[srows], lse.cpu().numpy()[srows], ref_o, ref_l, TOL[p.latent.dtype])
     print(f"  sampled rows {len(rows)} (indices), {len(srows)} (scores, attention); attention worst {worst:.3g}")
+
+
+@pytest.mark.parametrize("name", ["decode_128k_fp8_window4", "paged_decode_16x16k_32k_window4"])
+def test_decode_window_full_size(name):
+    """The multi-token window workloads in full, as bench.py runs the first:
+    every score, index and attention row against the oracle."""
+    from gpu_util import gpu_decode_window
+    wl = inputs.WINDOW_WORKLOADS[name]
+    print(f"case {name}: full size", flush=True)
+    p = inputs.make_problem(wl)
+    dp = device.upload(p)
+    out, lse, scores, idx, ws = gpu_decode_window(dp)
+    g_scores = scores.cpu().numpy()
+    ref_scores = oracle.index_scores(p.q_idx, p.q_idx_dtype, p.w_idx, p.keys, p.q_seq, p.q_len,
+                                     ld=g_scores.shape[1])
+    worst_s = check_scores(p, g_scores, ref_scores)
+    g_idx = idx.cpu().numpy()
+    ref_idx, _ = oracle.topk(g_scores.astype(np.float64), p.q_len, p.topk)
+    assert np.array_equal(g_idx, ref_idx)
+    ref_o, ref_l, _ = oracle.mla_attend(p.q_mla, p.q_mla_dtype, p.latent, p.kv_lora, g_idx, p.q_seq, p.softmax_scale)
+    worst_a = check_attention(out.cpu().numpy(), lse.cpu().numpy(), ref_o, ref_l, TOL[p.latent.dtype])
+    print(f"  worst score error / condition {worst_s:.3g}, worst attention relative error {worst_a:.3g}", flush=True)
+
+
+def test_decode_fp8_latent_full_size():
+    """The fp8-latent 128K batch in full, as bench.py runs it."""
+    wl = inputs.DECODE_128K_FP8_LAT8
+    print(f"case {wl.name}: full size", flush=True)
+    p = inputs.make_problem(wl)
+    dp = device.upload(p)
+    _check_decode(p, dp)
