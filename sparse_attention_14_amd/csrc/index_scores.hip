@@ -321,7 +321,9 @@ __global__ __launch_bounds__(kPThreads) void scores_prefill_kernel(float *__rest
   __shared__ int32_t groups[kPQ + 1];
 
   const int qb = blockIdx.x, split = blockIdx.y;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  // the wavefront index as a scalar: everything derived from it (the wavefront's
+  // queries, their lengths, score rows) stays in scalar registers
+  const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int half = lane >> 5, col = lane & 31;
   const int qbase = qb * kPQ;
   if (tid < kPQ) {
