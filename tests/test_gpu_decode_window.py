@@ -34,6 +34,8 @@ CASES = {
     "bf16_w8_tiny": S(inputs.DECODE_8K, name="w6", wid=506, batch=2, seq_len=(3, 3), window=8),
     "bf16_paged_w4_bounded": S(inputs.PAGED_DECODE_W4, name="w5", wid=505, batch=2, seq_len=(13000, 26000)),
     "fp8_latent8_w4": S(inputs.DECODE_128K_FP8_LAT8, name="w7", wid=507, batch=4, seq_len=(3000, 9000), window=4),
+    # fp32 indexer queries: the window rows come from their own kernel
+    "f32_w3": S(inputs.TINY_FP32, name="w8", wid=508, batch=3, seq_len=(2, 900), window=3),
 }
 
 
