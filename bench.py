@@ -231,6 +231,18 @@ def main():
     torch.cuda.synchronize()
     t_step = (time.perf_counter() - t0) / args.steps
 
+    # spread: events around each graph launch (n_c steps) of a second pass
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(max(args.steps // n_c, 10))]
+    for e0, e1 in ev:
+        e0.record()
+        seq_graph.replay()
+        e1.record()
+    torch.cuda.synchronize()
+    per_step = np.array([e0.elapsed_time(e1) * 1e3 / n_c for e0, e1 in ev])
+    spread = {"p10": round(float(np.percentile(per_step, 10)), 2), "median": round(float(np.median(per_step)), 2),
+              "p90": round(float(np.percentile(per_step, 90)), 2), "launches": len(ev)}
+
     # one graph launch per step, for reference
     n_single = max(args.steps // 4, 10)
     torch.cuda.synchronize()
@@ -280,6 +292,38 @@ def main():
                 "frac": round(k_gbs / HBM_PEAK_GBS, 4), "traffic": traffic,
                 "kernel": "scores_mfma_kernel (fp8 keys, 128-wide, 32 heads)", "bytes_per_launch": kbytes,
                 "avg_launch_us": round(t_kernel * 1e6, 3)}
+
+    # ------------------------------------------------- measured peaks ---
+    # What this GPU reaches on plain work, as context for the fractions of the
+    # datasheet peaks: a device-to-device copy (HBM) and a large bf16 GEMM
+    # (matrix cores, through the vendor library).
+    cp_src = torch.empty(COPY_PROBE_BYTES, dtype=torch.uint8, device="cuda")
+    cp_dst = torch.empty_like(cp_src)
+    cp_src.fill_(1)
+    for _ in range(3):
+        cp_dst.copy_(cp_src)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(10):
+        cp_dst.copy_(cp_src)
+    e1.record()
+    e1.synchronize()
+    copy_gbs = 2 * COPY_PROBE_BYTES * 10 / (e0.elapsed_time(e1) / 1e3) / 1e9
+    del cp_src, cp_dst
+    ga = torch.randn(8192, 8192, device="cuda", dtype=torch.bfloat16)
+    gb = torch.randn(8192, 8192, device="cuda", dtype=torch.bfloat16)
+    for _ in range(5):
+        torch.mm(ga, gb)
+    e0.record()
+    for _ in range(20):
+        torch.mm(ga, gb)
+    e1.record()
+    e1.synchronize()
+    gemm_tf = 2 * 8192 ** 3 * 20 / (e0.elapsed_time(e1) / 1e3) / 1e12
+    del ga, gb
+    torch.cuda.empty_cache()
+    measured = {"hbm_copy_GB_per_s": round(copy_gbs, 1), "bf16_gemm_8192_TFLOP_per_s": round(gemm_tf, 1),
+                "score_kernel_frac_of_copy": round(k_gbs / copy_gbs, 4)}
 
     # ------------------------------------- cache append (the step before) ---
     # The new token of every sequence written at its last position: key
@@ -500,9 +544,10 @@ def main():
                    "indexer": f"{p.idx_heads}x{p.idx_dim} e4m3fn keys + f32 scale", "mla_heads": H,
                    "latent": f"{L}+{p.rope} bf16", "graph": f"{args.copies} steps per graph launch", "cache_copies": args.copies},
         "decode_us_per_step": round(t_step * 1e6, 2), "decode_us_per_step_eager": round(t_eager * 1e6, 2),
-        "decode_us_per_step_one_per_launch": round(t_single * 1e6, 2),
+        "decode_us_per_step_one_per_launch": round(t_single * 1e6, 2), "decode_us_per_step_spread": spread,
         "decode_bytes_per_step": step_bytes, "decode_hbm_frac": round(gbs / HBM_PEAK_GBS, 4),
-        "roofline": roofline, "append": append, "shared": shared, "absorb": absorb, "prefill": prefill, "window": window, "latent_fp8": latent8, "cpu_baseline": cpu, "device": dev_name,
+        "roofline": roofline, "append": append, "shared": shared, "absorb": absorb, "prefill": prefill, "window": window, "latent_fp8": latent8, "cpu_baseline": cpu, "measured_peaks": measured, "device": dev_name,
+        "rocm": torch.version.hip,
     }
     print(json.dumps(line))
 
