@@ -38,6 +38,9 @@ CASES = {
     "bf16_wide_split": (S(inputs.DECODE_8K, name="a8", wid=308, batch=20, seq_len=(1000, 5000)), 2048),
     "bf16_wide_h128": (S(inputs.DECODE_8K, name="a9", wid=309, batch=8, seq_len=(3000, 3000), mla_heads=128), 2048),
     "bf16_wide_short_rows": (S(inputs.PAGED_DECODE, name="a10", wid=310, batch=16, seq_len=(1, 300)), 2048),
+    "bf16_wide_k100": (S(inputs.DECODE_8K, name="a16", wid=316, batch=20, seq_len=(50, 600)), 100),
+    "fp8lat_wide_k100_h128": (S(inputs.DECODE_128K_FP8_LAT8, name="a17", wid=317, batch=9, seq_len=(50, 600),
+                                mla_heads=128, tie_fraction=0.0), 100),
     # e4m3fn latent rows with a float32 scale per token: 16-head kernel (split), 64-head kernel (split, paged;
     # unsplit, many queries)
     "fp8lat_h64": (S(inputs.DECODE_128K_FP8_LAT8, name="a11", wid=311, batch=3, seq_len=(500, 4000),
