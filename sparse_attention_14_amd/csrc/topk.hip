@@ -10,10 +10,10 @@
 //  1. Candidate bound.  The row is cut into G groups; each full group reports a
 //     lower bound on its ceil(k / G)-th largest key (the score kernel does this
 //     as it writes the scores; otherwise bound_kernel does, or one wavefront
-//     estimates it from strided samples).  With group bounds at least k keys of
-//     the row are >= T_lo = their minimum; a sampled estimate may miss, which
-//     only sends the row to the exact fallback below.  Rows that fit the
-//     candidate budget use T_lo = 0.
+//     estimates it from samples spread over the row).  With group bounds at
+//     least k keys of the row are >= T_lo = their minimum; a sampled estimate
+//     may miss, which only sends the row to the exact fallback below.  Rows
+//     that fit the candidate budget use T_lo = 0.
 //  2. Filter.  Workgroups scan the row in rounds of one score per thread and
 //     compact the (key, token) pairs with key >= T_lo in token order (wavefront
 //     ballots plus one prefix over the round totals).  For few long rows a
@@ -55,7 +55,7 @@ constexpr int kLocalThreads = 512;              // one workgroup per row
 constexpr int kLocalCap = 14 * kLocalThreads;   // LDS candidates of a one-workgroup row (7168)
 
 // LDS carve-up (32-bit words), the same for every kernel.
-constexpr int kTotWords = 200;                  // >= rounds * waves + 1 for every use (192 + 1)
+constexpr int kTotWords = 200;                  // >= rounds * waves for every use (192)
 constexpr int kOffHist = 0;
 constexpr int kOffScratch = kOffHist + kHistWords;
 constexpr int kOffShv = kOffScratch + 64;
@@ -113,11 +113,11 @@ __device__ __forceinline__ uint32_t lanes_below(uint64_t mask) {
 // tid < tid').  flag(m) returns 1 (counted in the low half), 1 << 16 (high half)
 // or 0.  pre[m] receives the packed count of earlier elements (both halves); the
 // packed total is returned.  Each half must stay below 65536.  tot: LDS of
-// R * waves + 1 words, not written again before one more barrier.  Two barriers.
+// R * waves words, not written again before one more barrier.  One barrier.
 template <int NT, int R, typename F>
 __device__ __forceinline__ uint32_t ordered_prefix(F &&flag, int rounds, uint32_t (&pre)[R], uint32_t *tot) {
   constexpr int W = NT / 64;
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   uint32_t totv = 0;   // lane m: packed total of round m in this wavefront
 #pragma unroll
   for (int m = 0; m < R; ++m) {
@@ -132,32 +132,34 @@ __device__ __forceinline__ uint32_t ordered_prefix(F &&flag, int rounds, uint32_
   }
   if (lane < rounds) tot[lane * W + wave] = totv;
   __syncthreads();
-  if (wave == 0) {
-    const int E = rounds * W;
-    constexpr int PL = (R * W + 63) / 64;
-    uint32_t v[PL];
-    uint32_t s = 0;
+  // every wavefront scans all round totals itself: entry e = m * W + w sits in
+  // lane e / PL, slot e % PL
+  constexpr int PL = (R * W + 63) / 64;
+  const int E = rounds * W;
+  uint32_t v[PL];
+  uint32_t s = 0;
 #pragma unroll
-    for (int i = 0; i < PL; ++i) {
-      const int e = lane * PL + i;
-      v[i] = e < E ? tot[e] : 0u;
-      s += v[i];
-    }
-    const uint32_t incl = wave_inclusive_scan(s);
-    uint32_t run = incl - s;
-#pragma unroll
-    for (int i = 0; i < PL; ++i) {
-      const int e = lane * PL + i;
-      if (e < E) tot[e] = run;
-      run += v[i];
-    }
-    if (lane == 63) tot[R * W] = incl;
+  for (int i = 0; i < PL; ++i) {
+    const int e = lane * PL + i;
+    v[i] = e < E ? tot[e] : 0u;
+    s += v[i];
   }
-  __syncthreads();
+  const uint32_t incl = wave_inclusive_scan(s);
+  uint32_t ex[PL];
+  ex[0] = incl - s;
 #pragma unroll
-  for (int m = 0; m < R; ++m)
-    if (m < rounds) pre[m] += tot[m * W + wave];
-  return tot[R * W];
+  for (int i = 1; i < PL; ++i) ex[i] = ex[i - 1] + v[i - 1];
+#pragma unroll
+  for (int m = 0; m < R; ++m) {
+    if (m < rounds) {
+      const int e = m * W + wave;
+      uint32_t x = ex[0];
+#pragma unroll
+      for (int i = 1; i < PL; ++i) x = e % PL == i ? ex[i] : x;
+      pre[m] += (uint32_t)__builtin_amdgcn_readlane((int)x, e / PL);
+    }
+  }
+  return (uint32_t)__builtin_amdgcn_readlane((int)incl, 63);
 }
 
 template <int NT>
@@ -362,13 +364,20 @@ __device__ void finish_row(const SelectArgs &a, int qi, int n, const float *row,
   if (tid == 0 && a.counts) a.counts[qi] = a.k;
 }
 
-// Lower bound (top 16 bits) on the key of rank `need` among kSamples strided
-// samples of the row.  Called by one whole wavefront.
+// Lower bound (top 16 bits) on the key of rank `need` among kSamples samples
+// of the row: 64 runs of 16 consecutive tokens spread evenly over it.  A run
+// is one 64-byte segment, so the samples cost 4 KB of reads (one sample per
+// cache line would read half of the row).  n >= 1024.  Called by one whole
+// wavefront.
 __device__ uint32_t sample_bound_wave(const float *row, int n, uint32_t need) {
   const int lane = threadIdx.x & 63;
   uint32_t x[kSamples / 64];
 #pragma unroll
-  for (int i = 0; i < kSamples / 64; ++i) x[i] = order_key(row[(int)(((int64_t)(lane + 64 * i) * n) / kSamples)]);
+  for (int i = 0; i < kSamples / 64; ++i) {
+    const int run = 4 * i + (lane >> 4);
+    const int start = (int)(((int64_t)run * n) / 64) & ~15;
+    x[i] = order_key(row[start + (lane & 15)]);
+  }
   return wave_rank_bound(x, need, 16);
 }
 
@@ -420,7 +429,7 @@ __global__ __launch_bounds__(kLocalThreads) void select_local_kernel(SelectArgs 
   const uint32_t cap = (uint32_t)a.local_cap;
 
   float v[kPassRounds];
-  load_pass<NT, kPassRounds>(row, 0, n, v);
+  load_pass<NT, kPassRounds>(row, 0, n, v);   // in flight while the bound is found
   uint32_t t_lo = 0;
   if ((uint32_t)n > cap) {
     if (a.bounds) {
@@ -437,15 +446,17 @@ __global__ __launch_bounds__(kLocalThreads) void select_local_kernel(SelectArgs 
     }
   }
 
+  // The keys of a pass are formed at the end of the previous one, so the next
+  // pass's loads stay in flight across this pass's prefix and barrier.
+  uint32_t key[kPassRounds];
+#pragma unroll
+  for (int i = 0; i < kPassRounds; ++i) key[i] = order_key(v[i]);
   uint32_t found = 0, mx = 0;
   int parity = 0;
   for (int g0 = 0; g0 < n; g0 += kPass, parity ^= 1) {
     float nv[kPassRounds];
     const bool more = g0 + kPass < n;
     if (more) load_pass<NT, kPassRounds>(row, g0 + kPass, n, nv);
-    uint32_t key[kPassRounds];
-#pragma unroll
-    for (int i = 0; i < kPassRounds; ++i) key[i] = order_key(v[i]);
     uint32_t pre[kPassRounds];
     const uint32_t tot = ordered_prefix<NT, kPassRounds>(
         [&](int i) -> uint32_t { return (g0 + tid + NT * i < n && key[i] >= t_lo) ? 1u : 0u; }, kPassRounds, pre,
@@ -460,7 +471,7 @@ __global__ __launch_bounds__(kLocalThreads) void select_local_kernel(SelectArgs 
     found += tot;
     if (more) {
 #pragma unroll
-      for (int i = 0; i < kPassRounds; ++i) v[i] = nv[i];
+      for (int i = 0; i < kPassRounds; ++i) key[i] = order_key(nv[i]);
     }
   }
   mx = block_max<NT>(mx, L.scratch);   // (its barriers also publish L.cand)
