@@ -55,7 +55,7 @@ constexpr int kLocalThreads = 512;              // one workgroup per row
 constexpr int kLocalCap = 14 * kLocalThreads;   // LDS candidates of a one-workgroup row (7168)
 
 // LDS carve-up (32-bit words), the same for every kernel.
-constexpr int kTotWords = 200;                  // >= rounds * waves for every use (192)
+constexpr int kTotWords = 200;                  // >= rounds * waves + 1 for every use (192 + 1)
 constexpr int kOffHist = 0;
 constexpr int kOffScratch = kOffHist + kHistWords;
 constexpr int kOffShv = kOffScratch + 64;
@@ -113,11 +113,11 @@ __device__ __forceinline__ uint32_t lanes_below(uint64_t mask) {
 // tid < tid').  flag(m) returns 1 (counted in the low half), 1 << 16 (high half)
 // or 0.  pre[m] receives the packed count of earlier elements (both halves); the
 // packed total is returned.  Each half must stay below 65536.  tot: LDS of
-// R * waves words, not written again before one more barrier.  One barrier.
+// R * waves + 1 words, not written again before one more barrier.  Two barriers.
 template <int NT, int R, typename F>
 __device__ __forceinline__ uint32_t ordered_prefix(F &&flag, int rounds, uint32_t (&pre)[R], uint32_t *tot) {
   constexpr int W = NT / 64;
-  const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   uint32_t totv = 0;   // lane m: packed total of round m in this wavefront
 #pragma unroll
   for (int m = 0; m < R; ++m) {
@@ -132,34 +132,32 @@ __device__ __forceinline__ uint32_t ordered_prefix(F &&flag, int rounds, uint32_
   }
   if (lane < rounds) tot[lane * W + wave] = totv;
   __syncthreads();
-  // every wavefront scans all round totals itself: entry e = m * W + w sits in
-  // lane e / PL, slot e % PL
-  constexpr int PL = (R * W + 63) / 64;
-  const int E = rounds * W;
-  uint32_t v[PL];
-  uint32_t s = 0;
+  if (wave == 0) {
+    const int E = rounds * W;
+    constexpr int PL = (R * W + 63) / 64;
+    uint32_t v[PL];
+    uint32_t s = 0;
 #pragma unroll
-  for (int i = 0; i < PL; ++i) {
-    const int e = lane * PL + i;
-    v[i] = e < E ? tot[e] : 0u;
-    s += v[i];
-  }
-  const uint32_t incl = wave_inclusive_scan(s);
-  uint32_t ex[PL];
-  ex[0] = incl - s;
-#pragma unroll
-  for (int i = 1; i < PL; ++i) ex[i] = ex[i - 1] + v[i - 1];
-#pragma unroll
-  for (int m = 0; m < R; ++m) {
-    if (m < rounds) {
-      const int e = m * W + wave;
-      uint32_t x = ex[0];
-#pragma unroll
-      for (int i = 1; i < PL; ++i) x = e % PL == i ? ex[i] : x;
-      pre[m] += (uint32_t)__builtin_amdgcn_readlane((int)x, e / PL);
+    for (int i = 0; i < PL; ++i) {
+      const int e = lane * PL + i;
+      v[i] = e < E ? tot[e] : 0u;
+      s += v[i];
     }
+    const uint32_t incl = wave_inclusive_scan(s);
+    uint32_t run = incl - s;
+#pragma unroll
+    for (int i = 0; i < PL; ++i) {
+      const int e = lane * PL + i;
+      if (e < E) tot[e] = run;
+      run += v[i];
+    }
+    if (lane == 63) tot[R * W] = incl;
   }
-  return (uint32_t)__builtin_amdgcn_readlane((int)incl, 63);
+  __syncthreads();
+#pragma unroll
+  for (int m = 0; m < R; ++m)
+    if (m < rounds) pre[m] += tot[m * W + wave];
+  return tot[R * W];
 }
 
 template <int NT>
