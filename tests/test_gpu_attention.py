@@ -53,17 +53,27 @@ CASES = {
                               latent_dtype="e4m3fn"), 256),
     "fp8lat_peaky_q": (S(inputs.DECODE_128K_FP8_LAT8, name="a15", wid=315, batch=2, seq_len=(3000, 3000),
                          q_mla_sigma=20.0, tie_fraction=0.0), 2048),
+    # every visible token kept, k == n == 2048 for both queries (16 splits of 128 slots)
+    "bf16_all_2048_kept": (S(inputs.DECODE_8K, name="a18", wid=318, batch=2, seq_len=(2048, 2048)), 2048),
     "f32_tiny": (inputs.TINY_FP32, 256),
     "f32_h3_w44": (S(inputs.TINY_FP32, name="a7", wid=307, batch=3, seq_len=(10, 900), mla_heads=3, kv_lora=40,
                      rope=4), 300),
 }
 
 
-@pytest.fixture(scope="module", params=sorted(CASES))
-def case(request):
-    wl, k = CASES[request.param]
+# cases whose every visible token fits in one index list of 2048 slots
+DENSE_CASES = sorted(n for n, (wl, _) in CASES.items() if wl.seq_len[1] <= 2048)
+
+
+def _case(name):
+    wl, k = CASES[name]
     p = inputs.make_problem(wl)
     return p, device.upload(p), k
+
+
+@pytest.fixture(scope="module", params=sorted(CASES))
+def case(request):
+    return _case(request.param)
 
 
 def test_sparse_attention_matches_oracle(case):
@@ -88,10 +98,10 @@ def test_unsorted_indices_and_holes(case):
     check_attention(out.cpu().numpy(), lse.cpu().numpy(), ref_o, ref_l, TOL[p.latent.dtype])
 
 
-def test_k_at_least_n_equals_dense(case):
-    p, dp, k = case
-    if p.max_len > 2048:
-        pytest.skip("dense comparison needs every visible token to fit in k <= 2048")
+@pytest.mark.parametrize("name", DENSE_CASES)
+def test_k_at_least_n_equals_dense(name):
+    p, dp, _ = _case(name)
+    assert p.max_len <= 2048
     kk = 2048
     idx = np.full((p.n_q, kk), -1, np.int32)
     for i in range(p.n_q):

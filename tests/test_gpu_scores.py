@@ -34,10 +34,18 @@ CASES = {
 }
 
 
+PREFILL_CASES = sorted(n for n, wl in CASES.items() if wl.prefill_queries > 0)   # one sequence, many queries
+TIE_CASES = sorted(n for n, wl in CASES.items() if wl.tie_fraction > 0)
+
+
+def _case(name):
+    p = inputs.make_problem(CASES[name])
+    return p, device.upload(p)
+
+
 @pytest.fixture(scope="module", params=sorted(CASES))
 def case(request):
-    p = inputs.make_problem(CASES[request.param])
-    return p, device.upload(p)
+    return _case(request.param)
 
 
 def test_scores_match_oracle(case):
@@ -51,19 +59,19 @@ def test_scores_match_oracle(case):
         assert np.all(np.isnan(g[i, int(p.q_len[i]):])), "entries beyond q_len were written"
 
 
-def test_prefill_rows_without_q_seq(case):
-    p, dp = case
-    if p.decode:
-        pytest.skip("multi-query single-sequence case only")
+@pytest.mark.parametrize("name", PREFILL_CASES)
+def test_prefill_rows_without_q_seq(name):
+    p, dp = _case(name)
+    assert not p.decode
     g = gpu_scores(dp, use_seq=False).cpu().numpy()
     ref = oracle.index_scores(p.q_idx, p.q_idx_dtype, p.w_idx, p.keys, None, p.q_len)
     check_scores(p, g, ref)
 
 
-def test_copied_keys_score_bit_identically(case):
-    p, dp = case
-    if not p.meta["ties"]:
-        pytest.skip("no injected ties")
+@pytest.mark.parametrize("name", TIE_CASES)
+def test_copied_keys_score_bit_identically(name):
+    p, dp = _case(name)
+    assert p.meta["ties"], "the workload injects copied keys"
     g = gpu_scores(dp).cpu().numpy()
     for s, (dst, src) in p.meta["ties"].items():
         assert np.array_equal(g[s, dst].view(np.uint32), g[s, src].view(np.uint32))
