@@ -109,7 +109,7 @@ typedef struct {
  *   q_seq   [n_q] int32 or NULL (all queries in sequence 0)
  * Supported: q f32 with f32 keys, or q bf16 with bf16 or fp8 keys;
  *   width 32..128 in steps of 32 (bf16/fp8 keys: 64 or 128); 1 <= n_heads <= 64;
- *   ld_scores >= max_len.
+ *   ld_scores >= max_len; n_q <= 65535.
  */
 dsa_status dsa_index_scores(float *scores, int64_t ld_scores, const void *q, dsa_dtype q_dtype, const float *w,
                             const dsa_cache *keys, const int32_t *q_seq, const int32_t *q_len, int32_t n_q,
@@ -123,7 +123,8 @@ dsa_status dsa_index_scores(float *scores, int64_t ld_scores, const void *q, dsa
  * order followed by -1 padding; counts [n_q] (nullable) receive min(k, n).
  * Selection is integer-only on an order-preserving 32-bit image of each score,
  * so the result is exact and deterministic.
- * Supported: 1 <= k <= 2048, 1 <= max_len <= 262144, flags = DSA_TOPK_ORDER_INDEX.
+ * Supported: 1 <= k <= 2048, 1 <= max_len <= 262144, n_q <= 65535,
+ *   flags = DSA_TOPK_ORDER_INDEX.
  */
 dsa_status dsa_topk(int32_t *indices, int32_t *counts, const float *scores, int64_t ld_scores,
                     const int32_t *q_len, int32_t n_q, int32_t k, int32_t max_len, uint32_t flags,
@@ -147,7 +148,7 @@ size_t dsa_topk_workspace_size(int32_t n_q, int32_t k, int32_t max_len);
  * A100, in Vx", "INT4, FP8 and BF16"; dsa_cache_append writes it.
  * Supported: bf16 q with bf16 or fp8 latent rows, W = 576, kv_lora = 512,
  *   n_heads a multiple of 16 up to 128; f32 with W <= 1024 a multiple of 4,
- *   kv_lora <= W a multiple of 4, n_heads <= 128; 1 <= k <= 2048.
+ *   kv_lora <= W a multiple of 4, n_heads <= 128; 1 <= k <= 2048; n_q <= 2^24.
  */
 dsa_status mla_sparse_attend(float *out, float *lse, const void *q, dsa_dtype q_dtype, const dsa_cache *latent,
                              int32_t kv_lora, const int32_t *indices, int32_t k, const int32_t *q_seq, int32_t n_q,
@@ -193,7 +194,7 @@ size_t dsa_decode_step_workspace_size(int32_t batch, int32_t max_len, int32_t k,
  *   out [batch * window][mla_heads][kv_lora], lse [batch * window][mla_heads] (nullable),
  *   scores_out [batch * window][max_len], indices_out [batch * window][k] (optional).
  * max_len >= max_b seq_len[b].  1 <= window <= 64 (DSA_ERR_UNSUPPORTED above),
- * batch * window <= 2^24.  window = 1 is dsa_decode_step.  Other arguments,
+ * batch * window <= 65535.  window = 1 is dsa_decode_step.  Other arguments,
  * errors and the workspace contract as for dsa_decode_step, with the size from
  * dsa_decode_window_workspace_size (0 for invalid arguments).
  */

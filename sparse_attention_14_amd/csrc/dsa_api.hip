@@ -13,6 +13,8 @@ namespace {
 constexpr int kMaxTopk = 2048;
 constexpr int kMaxLenTopk = 262144;
 constexpr int kMaxWindow = 64;    // queries per sequence in one decode window
+constexpr int kMaxRows = 65535;   // queries per call where each query is one grid row (gridDim.y)
+constexpr int kMaxQueries = 1 << 24;   // queries per call of the attention-only entry points
 
 int elem_bytes(dsa_dtype d) { return d == DSA_F32 ? 4 : (d == DSA_BF16 ? 2 : 1); }
 
@@ -167,6 +169,7 @@ dsa_status dsa_index_scores(float *scores, int64_t ld_scores, const void *q, dsa
   if (n_q < 0 || max_len < 0) return DSA_ERR_INVALID_ARGUMENT;
   if (n_q == 0) return DSA_OK;
   if (!scores || !q_len || max_len < 1 || ld_scores < max_len) return DSA_ERR_INVALID_ARGUMENT;
+  if (n_q > kMaxRows) return DSA_ERR_UNSUPPORTED;
   dsa_status s = check_scores(q, q_dtype, w, keys, n_heads);
   if (s != DSA_OK) return s;
   return from_hip(launch_index_scores(scores, ld_scores, q, q_dtype, w, to_dev(keys), keys->dtype, q_seq, 0, q_len,
@@ -186,7 +189,7 @@ dsa_status dsa_topk(int32_t *indices, int32_t *counts, const float *scores, int6
   if (n_q == 0) return DSA_OK;
   if (!indices || !scores || !q_len || k < 1 || max_len < 1 || ld_scores < max_len) return DSA_ERR_INVALID_ARGUMENT;
   if (flags != DSA_TOPK_ORDER_INDEX) return DSA_ERR_UNSUPPORTED;
-  if (k > kMaxTopk || max_len > kMaxLenTopk) return DSA_ERR_UNSUPPORTED;
+  if (k > kMaxTopk || max_len > kMaxLenTopk || n_q > kMaxRows) return DSA_ERR_UNSUPPORTED;
   const TopkPlan p = plan_topk(n_q, k, max_len);
   if (p.total > 0 && (!workspace || workspace_bytes < p.total)) return DSA_ERR_WORKSPACE_TOO_SMALL;
   return from_hip(launch_topk(indices, counts, scores, ld_scores, q_len, p, workspace, nullptr, 0, 0,
@@ -208,7 +211,7 @@ dsa_status mla_sparse_attend(float *out, float *lse, const void *q, dsa_dtype q_
   if (!out || !indices || k < 1) return DSA_ERR_INVALID_ARGUMENT;
   dsa_status s = check_attend(q, q_dtype, latent, kv_lora, n_heads);
   if (s != DSA_OK) return s;
-  if (k > kMaxTopk) return DSA_ERR_UNSUPPORTED;
+  if (k > kMaxTopk || n_q > kMaxQueries) return DSA_ERR_UNSUPPORTED;
   const AttendPlan p = plan_attend(n_q, n_heads, kv_lora, latent->width, k, q_dtype);
   if (p.total > 0 && (!workspace || workspace_bytes < p.total)) return DSA_ERR_WORKSPACE_TOO_SMALL;
   return from_hip(launch_attend(out, lse, q, attend_dtype(q_dtype, latent), to_dev(latent), kv_lora, indices, k, q_seq, 0, n_q, n_heads,
@@ -245,7 +248,7 @@ dsa_status decode_impl(float *out, float *lse, const void *q_idx, dsa_dtype q_id
   if (window > kMaxWindow) return DSA_ERR_UNSUPPORTED;
   if (batch == 0) return DSA_OK;
   if (!out || !seq_len || k < 1 || max_len < 1) return DSA_ERR_INVALID_ARGUMENT;
-  if ((int64_t)batch * window > (int64_t)1 << 24) return DSA_ERR_UNSUPPORTED;
+  if ((int64_t)batch * window > kMaxRows) return DSA_ERR_UNSUPPORTED;
   dsa_status s = check_scores(q_idx, q_idx_dtype, w_idx, keys, idx_heads);
   if (s != DSA_OK) return s;
   s = check_attend(q_mla, q_mla_dtype, latent, kv_lora, mla_heads);
@@ -347,7 +350,7 @@ dsa_status dsa_decode_shared(float *out, float *lse, const void *q_mla, dsa_dtyp
   if (!out || !indices || k < 1) return DSA_ERR_INVALID_ARGUMENT;
   dsa_status s = check_attend(q_mla, q_mla_dtype, latent, kv_lora, mla_heads);
   if (s != DSA_OK) return s;
-  if (k > kMaxTopk || (int64_t)batch * window > (int64_t)1 << 24) return DSA_ERR_UNSUPPORTED;
+  if (k > kMaxTopk || (int64_t)batch * window > kMaxQueries) return DSA_ERR_UNSUPPORTED;
   const int32_t n_q = batch * window;
   // the size query assumes the bf16 plan (the larger one)
   const size_t need = dsa_decode_shared_workspace_size(batch, window, k, mla_heads, kv_lora);

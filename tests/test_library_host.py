@@ -76,6 +76,7 @@ def test_index_scores_validation(lib):
     assert _scores(lib, _cache(row_stride=(1 << 24) + 16, block_stride=((1 << 24) + 16) * 1024)) == 2  # > 16 MiB rows
     assert _scores(lib, _cache(table=16, max_blocks=4, block_size=48, block_stride=256 * 48)) == 2  # block % 32
     assert _scores(lib, _cache(), q_dtype=7) == 1
+    assert _scores(lib, ok, n_q=65536) == 2                           # one grid row per query
 
 
 def test_topk_validation(lib):
@@ -87,6 +88,7 @@ def test_topk_validation(lib):
     assert f(16, None, 16, 100, 16, 1, 16, 100, 1, None, 0, None) == 2        # unknown flag
     assert f(16, None, 16, 1 << 20, 16, 1, 16, 1 << 20, 0, None, 0, None) == 2  # max_len too long
     assert f(16, None, 16, 131072, 16, 4, 2048, 131072, 0, None, 0, None) == 3  # needs a workspace
+    assert f(16, None, 16, 100, 16, 65536, 2048, 100, 0, None, 0, None) == 2  # one grid row per query
 
 
 def test_attend_validation(lib):
@@ -109,6 +111,7 @@ def test_attend_validation(lib):
     assert call(q_dtype=0) == 2                                       # q dtype must match the cache
     assert call(k=4096) == 2
     assert call(n_q=4) == 3                                           # split plan needs a workspace
+    assert call(n_q=(1 << 24) + 1) == 2
 
 
 def test_decode_step_validation(lib):
@@ -141,6 +144,7 @@ def test_decode_window_validation(lib):
     assert call(window=0) == 1
     assert call(window=-2) == 1
     assert call(window=65) == 2
+    assert call(batch=16384, window=4) == 2                           # 65536 query rows
     assert call(out=None) == 1
     assert call(seq_len=None) == 1
     assert call() == 3                                                # no workspace
@@ -208,6 +212,7 @@ def test_decode_shared_validation(lib):
     assert call(batch=-1) == 1
     assert call(window=0) == 1
     assert call(window=65) == 2
+    assert call(batch=(1 << 22) + 1, window=4) == 2                   # more than 2^24 queries
     assert call(out=None) == 1
     assert call(idx=None) == 1
     assert call(k=0) == 1
