@@ -115,6 +115,36 @@ def score_kernel_bytes(p) -> int:
     return keys + p.q_idx.size * eb[p.q_idx_dtype] + p.w_idx.size * 4
 
 
+def cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as f:
+            for ln in f:
+                if ln.startswith("model name"):
+                    return ln.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def prefill_oracle_sample(oracle, n_queries):
+    """The oracle's indexer, top-k and sparse attention for the last `n_queries`
+    queries of the prefill chunk (same sequence and context), seconds per query."""
+    from sparse_attention_14_amd import inputs
+    wl = inputs.small(inputs.PREFILL_64K, prefill_queries=n_queries)
+    p = inputs.make_problem(wl)
+    t0 = time.perf_counter()
+    sc = oracle.index_scores(p.q_idx, p.q_idx_dtype, p.w_idx, p.keys, p.q_seq, p.q_len)
+    t1 = time.perf_counter()
+    idx, _ = oracle.topk(sc, p.q_len, p.topk)
+    t2 = time.perf_counter()
+    oracle.mla_attend(p.q_mla, p.q_mla_dtype, p.latent, p.kv_lora, idx, p.q_seq, p.softmax_scale)
+    t3 = time.perf_counter()
+    per = [(t1 - t0) / n_queries, (t2 - t1) / n_queries, (t3 - t2) / n_queries]
+    return {"queries": n_queries, "context": int(p.max_len), "indexer_s_per_query": round(per[0], 4),
+            "topk_s_per_query": round(per[1], 4), "sparse_mla_s_per_query": round(per[2], 4),
+            "chunk_estimate_s": round(sum(per) * inputs.PREFILL_64K.prefill_queries, 1)}
+
+
 def prefill_indexer_flops(p) -> int:
     """2 * heads * dim multiply-adds per visible (query, key) pair."""
     return 2 * p.idx_heads * p.idx_dim * int(p.q_len.astype("int64").sum())
@@ -251,6 +281,19 @@ def main():
         single[i % n_c].replay()
     torch.cuda.synchronize()
     t_single = (time.perf_counter() - t0) / n_single
+
+    # warm caches: the first copy every step (its keys and kept rows stay in the
+    # MALL), six steps per graph launch, for reference
+    warm_graph = capture(lambda: [step(0) for _ in range(n_c)])
+    warm_graph.replay()
+    torch.cuda.synchronize()
+    n_warm = max(args.steps // n_c, 10)
+    t0 = time.perf_counter()
+    for _ in range(n_warm):
+        warm_graph.replay()
+    torch.cuda.synchronize()
+    t_warm = (time.perf_counter() - t0) / (n_warm * n_c)
+    del warm_graph
 
     # eager (no graph) step time, for reference
     torch.cuda.synchronize()
@@ -532,9 +575,21 @@ def main():
             oracle.decode_step(p)
             times.append(time.perf_counter() - t0)
         t_cpu = float(np.median(times))
-        cpu = {"value": round(step_bytes / t_cpu / 1e9, 3), "unit": "GB/s", "cores": oracle.num_threads(),
+        threads = oracle.num_threads()
+        cpu = {"value": round(step_bytes / t_cpu / 1e9, 3), "unit": "GB/s", "cores": threads,
                "kind": "oracle", "sample": f"{len(times)} full decode steps of {wl.name} (4 x 131072 tokens), fp64 "
                                            f"oracle, median {t_cpu:.3f} s per step, {sum(times):.1f} s in all"}
+        # the same step on one thread (one step)
+        oracle.set_num_threads(1)
+        t0 = time.perf_counter()
+        oracle.decode_step(p)
+        t_one = time.perf_counter() - t0
+        oracle.set_num_threads(threads)
+        cpu["one_thread_s_per_step"] = round(t_one, 3)
+        cpu["gpu_over_cpu"] = round(gbs / cpu["value"], 1)
+        cpu["cpu_model"] = cpu_model()
+        if not args.no_prefill:
+            cpu["prefill_sample"] = prefill_oracle_sample(oracle, 8)
 
     line = {
         "metric": METRIC, "value": round(gbs, 1), "unit": "GB/s", "n_gpus": 1, "steps": args.steps,
@@ -545,6 +600,7 @@ def main():
                    "latent": f"{L}+{p.rope} bf16", "graph": f"{args.copies} steps per graph launch", "cache_copies": args.copies},
         "decode_us_per_step": round(t_step * 1e6, 2), "decode_us_per_step_eager": round(t_eager * 1e6, 2),
         "decode_us_per_step_one_per_launch": round(t_single * 1e6, 2), "decode_us_per_step_spread": spread,
+        "decode_us_per_step_warm": round(t_warm * 1e6, 2),
         "decode_bytes_per_step": step_bytes, "decode_hbm_frac": round(gbs / HBM_PEAK_GBS, 4),
         "roofline": roofline, "append": append, "shared": shared, "absorb": absorb, "prefill": prefill, "window": window, "latent_fp8": latent8, "cpu_baseline": cpu, "measured_peaks": measured, "device": dev_name,
         "rocm": torch.version.hip,

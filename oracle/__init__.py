@@ -71,6 +71,8 @@ def _load():
     lib.oracle_decode_step.argtypes = [P, P, P, i64, P, P, ctypes.c_int, P, P, i32, P, ctypes.c_int, P, i32, i32,
                                        P, i32, i32, dbl]
     lib.oracle_num_threads.restype = ctypes.c_int
+    lib.oracle_set_num_threads.argtypes = [ctypes.c_int]
+    lib.oracle_set_num_threads.restype = None
     lib.oracle_e4m3fn_quantize.restype = ctypes.c_uint8
     lib.oracle_e4m3fn_quantize.argtypes = [ctypes.c_float]
     lib.oracle_key_scale.restype = ctypes.c_float
@@ -109,6 +111,11 @@ def _cache_struct(cache):
 
 def num_threads() -> int:
     return int(_load().oracle_num_threads())
+
+
+def set_num_threads(n: int) -> None:
+    """Threads of the oracle's parallel loops (timing only; the results do not depend on it)."""
+    _load().oracle_set_num_threads(int(n))
 
 
 def bf16_to_double(bits: int) -> float:

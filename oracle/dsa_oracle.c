@@ -553,3 +553,13 @@ int oracle_num_threads(void) {
   return 1;
 #endif
 }
+
+/* Threads for the oracle's later parallel loops (timing only; results do not
+   depend on it). */
+void oracle_set_num_threads(int n) {
+#ifdef _OPENMP
+  if (n > 0) omp_set_num_threads(n);
+#else
+  (void)n;
+#endif
+}

@@ -133,3 +133,27 @@ def test_token_permutation_permutes_scores(oracle_mod):
     s = _scores(oracle_mod, q, w, inputs.cache_from_values(vals, "f32"), [n])[0]
     sp = _scores(oracle_mod, q, w, inputs.cache_from_values(vals[:, perm], "f32"), [n])[0]
     assert np.array_equal(sp, s[perm])
+
+
+def test_thread_count_does_not_change_results(oracle_mod):
+    """The oracle's parallel loops each own their outputs, so one thread and
+    many give the same bits (the CPU baseline also times one thread)."""
+    rng = np.random.default_rng(13)
+    n, D, H = 3000, 32, 4
+    vals = rng.standard_normal((2, n, D)).astype(np.float32)
+    q = rng.standard_normal((2, H, D)).astype(np.float32)
+    w = rng.uniform(0, 1, (2, H)).astype(np.float32)
+    c = inputs.cache_from_values(vals, "f32")
+    lens = np.array([n, n - 7], np.int32)
+    seq = np.array([0, 1], np.int32)
+    threads = oracle_mod.num_threads()
+    try:
+        oracle_mod.set_num_threads(1)
+        one = oracle_mod.index_scores(q, "f32", w, c, seq, lens)
+        one_idx, _ = oracle_mod.topk(one, lens, 256)
+    finally:
+        oracle_mod.set_num_threads(threads)
+    many = oracle_mod.index_scores(q, "f32", w, c, seq, lens)
+    many_idx, _ = oracle_mod.topk(many, lens, 256)
+    assert np.array_equal(np.nan_to_num(one, nan=-7), np.nan_to_num(many, nan=-7))
+    assert np.array_equal(one_idx, many_idx)
