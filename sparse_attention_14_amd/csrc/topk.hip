@@ -33,6 +33,8 @@
 // The per-element code is branch-free (select instead of divergent branches,
 // a dump bin for histogram entries that do not count): with few wavefronts per
 // SIMD, divergent control flow per element costs far more than the arithmetic.
+#include <atomic>
+
 #include "kernels.hpp"
 
 namespace dsa {
@@ -702,12 +704,19 @@ TopkPlan plan_topk(int n_q, int k, int max_len) {
 hipError_t launch_topk(int32_t *indices, int32_t *counts, const float *scores, int64_t ld, const int32_t *q_len,
                        const TopkPlan &plan, void *workspace, const uint32_t *bounds, int n_bounds,
                        int group_tokens, hipStream_t stream) {
-  static const bool lds_ok = [] {
-    const int most = 160 * 1024;
-    return hipFuncSetAttribute(reinterpret_cast<const void *>(&select_local_kernel),
-                               hipFuncAttributeMaxDynamicSharedMemorySize, most) == hipSuccess;
-  }();
-  if (!lds_ok) return hipErrorInvalidConfiguration;
+  // the one-workgroup-per-row kernel may use up to 160 KB of dynamic LDS; the
+  // attribute is set once per device (the current one)
+  static std::atomic<uint64_t> lds_set{0};
+  int dev = 0;
+  hipError_t de = hipGetDevice(&dev);
+  if (de != hipSuccess) return de;
+  const uint64_t bit = dev < 64 ? uint64_t(1) << dev : 0;
+  if (!bit || !(lds_set.load(std::memory_order_acquire) & bit)) {
+    de = hipFuncSetAttribute(reinterpret_cast<const void *>(&select_local_kernel),
+                             hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
+    if (de != hipSuccess) return de;
+    lds_set.fetch_or(bit, std::memory_order_acq_rel);
+  }
   if (plan.lds_bytes > 160 * 1024 || plan.chunks > kMaxChunks || (plan.chunks > 1 && plan.chunk > kPass))
     return hipErrorInvalidValue;
   uint8_t *ws = static_cast<uint8_t *>(workspace);
