@@ -138,3 +138,39 @@ def test_ties_straddle_the_boundary():
         assert (s[r] > v).sum() < k < (s[r] >= v).sum()
     print("case: 9-way ties across the k boundary, 3 x 50000", flush=True)
     _run(s, [n, n, n], k)
+
+
+def _sampled_runs(n):
+    """Token positions that the one-workgroup-per-row selector samples for its
+    candidate bound (64 runs of 16 tokens spread over the row)."""
+    pos = []
+    for run in range(64):
+        start = (run * n // 64) & ~15
+        pos.extend(range(start, start + 16))
+    return np.array(pos)
+
+
+@pytest.mark.parametrize("runs_high", [True, False])
+def test_sampled_bound_that_misses_falls_back_exactly(runs_high):
+    # Many rows (one workgroup each) longer than the LDS candidate budget: the
+    # candidate bound comes from samples.  With the sampled tokens far above
+    # (or below) the rest, the bound keeps fewer than k (or more than the
+    # budget), and the exact whole-row path must take over.
+    rng = np.random.default_rng(9 if runs_high else 10)
+    rows, n = 130, 20000
+    s = rng.standard_normal((rows, n)).astype(np.float32)
+    p = _sampled_runs(n)
+    s[:, p] = (50.0 if runs_high else -50.0) + rng.standard_normal((rows, len(p))).astype(np.float32)
+    print(f"case: {rows} x {n}, sampled runs {'high' if runs_high else 'low'}", flush=True)
+    _run(s, [n] * rows, 2048)
+
+
+def test_many_rows_with_a_positional_trend():
+    # Scores rising with position plus noise (later tokens favoured), rows of
+    # different lengths: the sampled bound sees the trend.
+    rng = np.random.default_rng(11)
+    rows, n = 160, 40000
+    trend = np.linspace(0.0, 6.0, n, dtype=np.float32)
+    s = (trend[None, :] + rng.standard_normal((rows, n)).astype(np.float32))
+    lens = rng.integers(8000, n + 1, size=rows)
+    _run(s, lens, 2048)
