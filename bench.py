@@ -47,6 +47,7 @@ def parse():
     ap.add_argument("--no-prefill", action="store_true")
     ap.add_argument("--no-window", action="store_true", help="skip the multi-token decode window leg")
     ap.add_argument("--no-latent8", action="store_true", help="skip the fp8-latent decode leg")
+    ap.add_argument("--no-configs", action="store_true", help="skip the decode steps of the other configurations")
     ap.add_argument("--copy-probe", action="store_true",
                     help="only run a plain 1 GiB device copy three times (calibrates HBM byte counters) and exit")
     return ap.parse_args()
@@ -562,6 +563,45 @@ def main():
                    "hbm_frac": round(b8 / t8 / 1e9 / HBM_PEAK_GBS, 4), "cache_copies": n8c}
         del copies8, ws8, dp8
 
+    # ------------------------------- decode steps of the other configurations ---
+    # The 1K-token fp32 case, one 8K-token bf16 sequence and 16 paged bf16
+    # sequences of 16K-32K tokens, each from HIP graphs over enough rotating
+    # cache copies that more than 512 MB is read between two uses of one copy.
+    configs = None
+    if not args.no_configs:
+        torch.cuda.empty_cache()
+        configs = {}
+        config_problems = {}
+        for wc in (inputs.TINY_FP32, inputs.DECODE_8K, inputs.PAGED_DECODE):
+            pc = inputs.make_problem(wc)
+            config_problems[wc.name] = pc
+            dpc = device.upload(pc)
+            bc = decode_algorithmic_bytes(pc)
+            ncc = int(min(64, max(2, -(-512_000_000 // bc))))
+            cc = [(dpc.keys, dpc.latent)] + [(clone_cache(dpc.keys), clone_cache(dpc.latent)) for _ in range(ncc - 1)]
+            Hc, Lc = pc.mla_heads, pc.kv_lora
+            oc = torch.empty(pc.n_q, Hc, Lc, device="cuda")
+            lc = torch.empty(pc.n_q, Hc, device="cuda")
+            wsc_bytes = dsa.dsa_decode_step_workspace_size(pc.n_q, pc.max_len, pc.topk, Hc, Lc)
+            wsc = [torch.zeros(max(wsc_bytes, 1), dtype=torch.uint8, device="cuda") for _ in cc]
+
+            def stepc(ci, pc=pc, dpc=dpc, cc=cc, oc=oc, lc=lc, wsc=wsc):
+                keys, lat = cc[ci]
+                dsa.dsa_decode_step(oc, lc, dpc.q_idx, pc.q_idx_dtype, dpc.w_idx, keys, dpc.q_mla, pc.q_mla_dtype, lat,
+                                    pc.kv_lora, dpc.q_len, pc.max_len, pc.topk, pc.softmax_scale, wsc[ci])
+
+            for i in range(3):
+                stepc(i % ncc)
+            torch.cuda.synchronize()
+            assert torch.isfinite(oc).all().item(), f"non-finite decode output ({wc.name})"
+            tc = time_graph_steps(torch, stepc, ncc, max(args.steps // 2, 2 * ncc), max(args.warmup, ncc))
+            configs[wc.name] = {"batch": pc.n_q, "context": int(pc.max_len), "paged": bool(pc.keys.paged),
+                                "us_per_step": round(tc * 1e6, 2), "bytes_per_step": bc,
+                                "GB_per_s": round(bc / tc / 1e9, 1), "hbm_frac": round(bc / tc / 1e9 / HBM_PEAK_GBS, 4),
+                                "cache_copies": ncc}
+            del cc, wsc, dpc, stepc
+            torch.cuda.empty_cache()
+
     # ------------------------------------------------------ CPU baseline ---
     cpu = None
     if not args.no_cpu:
@@ -588,6 +628,25 @@ def main():
         cpu["one_thread_s_per_step"] = round(t_one, 3)
         cpu["gpu_over_cpu"] = round(gbs / cpu["value"], 1)
         cpu["cpu_model"] = cpu_model()
+        if configs is not None:
+            # the other configurations: median of 3 steps on all threads, one step on one thread
+            per = {}
+            for name, pc in config_problems.items():
+                ts = []
+                for _ in range(3):
+                    t0 = time.perf_counter()
+                    oracle.decode_step(pc)
+                    ts.append(time.perf_counter() - t0)
+                oracle.set_num_threads(1)
+                t0 = time.perf_counter()
+                oracle.decode_step(pc)
+                t1 = time.perf_counter() - t0
+                oracle.set_num_threads(threads)
+                tm = float(np.median(ts))
+                per[name] = {"s_per_step": round(tm, 4), "one_thread_s_per_step": round(t1, 4),
+                             "GB_per_s": round(configs[name]["bytes_per_step"] / tm / 1e9, 3),
+                             "gpu_over_cpu": round(tm / (configs[name]["us_per_step"] * 1e-6), 1)}
+            cpu["configs"] = per
         if not args.no_prefill:
             cpu["prefill_sample"] = prefill_oracle_sample(oracle, 8)
 
@@ -602,7 +661,7 @@ def main():
         "decode_us_per_step_one_per_launch": round(t_single * 1e6, 2), "decode_us_per_step_spread": spread,
         "decode_us_per_step_warm": round(t_warm * 1e6, 2),
         "decode_bytes_per_step": step_bytes, "decode_hbm_frac": round(gbs / HBM_PEAK_GBS, 4),
-        "roofline": roofline, "append": append, "shared": shared, "absorb": absorb, "prefill": prefill, "window": window, "latent_fp8": latent8, "cpu_baseline": cpu, "measured_peaks": measured, "device": dev_name,
+        "roofline": roofline, "append": append, "shared": shared, "absorb": absorb, "prefill": prefill, "window": window, "latent_fp8": latent8, "configs": configs, "cpu_baseline": cpu, "measured_peaks": measured, "device": dev_name,
         "rocm": torch.version.hip,
     }
     print(json.dumps(line))

@@ -607,6 +607,7 @@ __global__ __launch_bounds__(256) void attend_f32_kernel(float *__restrict__ out
   __shared__ float lq[1024];
   __shared__ float lz[2048];
   __shared__ const float *lrow[2048];
+  __shared__ float4 pv[256];
   __shared__ float sh[8];
   const int qi = blockIdx.x / H, h = blockIdx.x - (blockIdx.x / H) * H;
   const int W = latent.width;
@@ -622,8 +623,17 @@ __global__ __launch_bounds__(256) void attend_f32_kernel(float *__restrict__ out
       int slot;
       const int64_t blk = cache_block(latent, seq, t, slot);
       rp = reinterpret_cast<const float *>(cache_row(latent, blk, slot));
+      // 16-byte loads (W is a multiple of 4, rows 16-byte aligned), summed in column order
+      const float4 *rp4 = reinterpret_cast<const float4 *>(rp);
       float dot = 0.0f;
-      for (int c = 0; c < W; ++c) dot = fmaf(lq[c], rp[c], dot);
+#pragma unroll 4
+      for (int c4 = 0; c4 < W / 4; ++c4) {
+        const float4 r = rp4[c4];
+        dot = fmaf(lq[4 * c4], r.x, dot);
+        dot = fmaf(lq[4 * c4 + 1], r.y, dot);
+        dot = fmaf(lq[4 * c4 + 2], r.z, dot);
+        dot = fmaf(lq[4 * c4 + 3], r.w, dot);
+      }
       z = dot * scale_log2;
     }
     lz[j] = z;
@@ -640,13 +650,64 @@ __global__ __launch_bounds__(256) void attend_f32_kernel(float *__restrict__ out
   }
   const float l = block_reduce_sum(sloc, sh);
   const float inv = l > 0.0f ? 1.0f / l : 0.0f;
-  for (int c = threadIdx.x; c < kv_lora; c += 256) {
-    float acc = 0.0f;
-    for (int j = 0; j < k; ++j) {
-      const float *rp = lrow[j];
-      if (rp) acc = fmaf(lz[j], rp[c], acc);
+  // PV: thread (jg, cg) sums columns c0 + 4 cg .. + 3 (one 16-byte load per
+  // row) over the slots j = jg (mod JG), four slots per round with their loads
+  // issued together; the JG partial sums are added in jg order through LDS.
+  // CG = the smallest power of two >= kv_lora / 4, at most 64; JG = 256 / CG.
+  int CG = 1;
+  while (CG < 64 && 4 * CG < kv_lora) CG *= 2;
+  const int JG = 256 / CG;
+  const int cg = threadIdx.x & (CG - 1), jg = threadIdx.x / CG;
+  for (int c0 = 0; c0 < kv_lora; c0 += 4 * CG) {
+    const int c = c0 + 4 * cg;
+    float4 acc = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+    if (c < kv_lora) {
+      const float4 zero = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+      int j = jg;
+      for (; j + 3 * JG < k; j += 4 * JG) {
+        const float *r[4] = {lrow[j], lrow[j + JG], lrow[j + 2 * JG], lrow[j + 3 * JG]};
+        float4 v[4];
+#pragma unroll
+        for (int u = 0; u < 4; ++u) v[u] = r[u] ? *reinterpret_cast<const float4 *>(r[u] + c) : zero;
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+          const float pz = lz[j + u * JG];
+          acc.x = fmaf(pz, v[u].x, acc.x);
+          acc.y = fmaf(pz, v[u].y, acc.y);
+          acc.z = fmaf(pz, v[u].z, acc.z);
+          acc.w = fmaf(pz, v[u].w, acc.w);
+        }
+      }
+      for (; j < k; j += JG) {
+        const float *r = lrow[j];
+        if (r) {
+          const float4 v = *reinterpret_cast<const float4 *>(r + c);
+          const float pz = lz[j];
+          acc.x = fmaf(pz, v.x, acc.x);
+          acc.y = fmaf(pz, v.y, acc.y);
+          acc.z = fmaf(pz, v.z, acc.z);
+          acc.w = fmaf(pz, v.w, acc.w);
+        }
+      }
     }
-    out[((int64_t)qi * H + h) * kv_lora + c] = acc * inv;
+    pv[threadIdx.x] = acc;
+    __syncthreads();
+    if (jg == 0 && c < kv_lora) {
+      float4 t = pv[cg];
+      for (int g = 1; g < JG; ++g) {
+        const float4 u = pv[g * CG + cg];
+        t.x += u.x;
+        t.y += u.y;
+        t.z += u.z;
+        t.w += u.w;
+      }
+      float *o = out + ((int64_t)qi * H + h) * kv_lora + c;
+      o[0] = t.x * inv;
+      o[1] = t.y * inv;
+      o[2] = t.z * inv;
+      o[3] = t.w * inv;
+    }
+    __syncthreads();
   }
   if (threadIdx.x == 0 && lse) lse[(int64_t)qi * H + h] = l > 0.0f ? (m + log2f(l)) * kLn2 : -INFINITY;
 }
