@@ -132,3 +132,27 @@ def test_decode_step_graph_replays_match_eager():
         assert torch.equal(out.view(torch.int32), ref[0].view(torch.int32)), f"replay {rep}: out differs"
         assert torch.equal(lse.view(torch.int32), ref[1].view(torch.int32)), f"replay {rep}: lse differs"
         gpu_decode_step(other)      # unrelated eager work between replays
+
+
+@pytest.mark.parametrize("wl", [S(inputs.DECODE_128K_FP8, name="d9", wid=409, batch=4, seq_len=(3000, 8000)),
+                                S(inputs.PAGED_DECODE, name="d10", wid=410, batch=5, seq_len=(9000, 20000))],
+                         ids=["fp8_one_workgroup_rows", "bf16_paged_spread_rows"])
+def test_empty_sequences_in_the_batch(wl):
+    """Sequences with no tokens (padding slots of a batch): no score written, no
+    kept index (-1 padding), output 0 and lse -inf; the other sequences are
+    unaffected."""
+    p = inputs.make_problem(wl)
+    p.q_len[[1, 3]] = 0
+    print(f"case {p.name}: lens {p.q_len.tolist()}", flush=True)
+    dp = device.upload(p)
+    out, lse, scores, idx, ws = gpu_decode_step(dp)
+    g_scores = scores.cpu().numpy()
+    ref_scores = oracle.index_scores(p.q_idx, p.q_idx_dtype, p.w_idx, p.keys, p.q_seq, p.q_len)
+    check_scores(p, g_scores, ref_scores)
+    g_idx = idx.cpu().numpy()
+    ref_idx, _ = oracle.topk(g_scores.astype(np.float64), p.q_len, p.topk)
+    assert np.array_equal(g_idx, ref_idx)
+    assert np.all(g_idx[[1, 3]] == -1)
+    ref_o, ref_l, _ = oracle.mla_attend(p.q_mla, p.q_mla_dtype, p.latent, p.kv_lora, g_idx, p.q_seq, p.softmax_scale)
+    check_attention(out.cpu().numpy(), lse.cpu().numpy(), ref_o, ref_l, TOL[p.latent.dtype])
+    assert torch.all(out[[1, 3]] == 0).item() and torch.all(torch.isneginf(lse[[1, 3]])).item()
