@@ -140,49 +140,60 @@ __global__ __launch_bounds__(kAttThreads) void attend_bf16_kernel(AttArgs a) {
 
   uint8_t *my_rows = lrows[team];
   uint16_t *my_p = lp[team][0];
-  // gather role: row gr = tid / 4 of the step, chunks gq + 4 j (j < 18)
-  const int gr = tid >> 2, gq = tid & 3;
-  constexpr int kPer = kChunks / 4;   // 18
-
   for (int step = 0; step < nsteps; ++step) {
     {
-      const int j = j0 + step * kStepRows + gr;
-      const int t = j < j1 ? a.indices[(int64_t)qi * a.k + j] : -1;
-      constexpr int NV = F8 ? kPer / 2 : kPer;   // fp8 rows are half as wide
-      u32x4 v[NV];
-      float sc = 0.0f;
-      if (t >= 0) {
-        int slot;
-        const int64_t blk = cache_block(a.latent, seq, t, slot);
-        const uint8_t *p = cache_row(a.latent, blk, slot) + 16 * gq;
+      // 8 lanes per row, so every load instruction covers whole 128-byte lines:
+      // rows gr8 and gr8 + kTile, 16-byte chunks gq8 + 8 i (bf16: 72 chunks,
+      // i < 9; fp8: 36 chunks, i < 5, the last only for gq8 < 4)
+      const int gr8 = tid >> 3, gq8 = tid & 7;
+      constexpr int NV8 = F8 ? 5 : kChunks / 8;
+      u32x4 w[kTeams][NV8];
+      float sc[kTeams];
+      bool ok[kTeams];
 #pragma unroll
-        for (int i = 0; i < NV; ++i) v[i] = load16(p + 64 * i);
-        if (F8) sc = a.latent.scale[blk * a.latent.scale_block_stride + slot];
-      } else {
+      for (int r = 0; r < kTeams; ++r) {
+        const int j = j0 + step * kStepRows + gr8 + kTile * r;
+        const int t = j < j1 ? a.indices[(int64_t)qi * a.k + j] : -1;
+        ok[r] = t >= 0;
+        sc[r] = 0.0f;
+        if (t >= 0) {
+          int slot;
+          const int64_t blk = cache_block(a.latent, seq, t, slot);
+          const uint8_t *p = cache_row(a.latent, blk, slot);
 #pragma unroll
-        for (int i = 0; i < NV; ++i) v[i] = u32x4{0, 0, 0, 0};
+          for (int i = 0; i < NV8; ++i) w[r][i] = load16(p + (F8 ? min(16 * gq8 + 128 * i, kW - 16) : 16 * gq8 + 128 * i));
+          if (F8) sc[r] = a.latent.scale[blk * a.latent.scale_block_stride + slot];
+        } else {
+#pragma unroll
+          for (int i = 0; i < NV8; ++i) w[r][i] = u32x4{0, 0, 0, 0};
+        }
       }
       if (step == 0) {
 #pragma unroll
         for (int ks = 0; ks < kW / 32; ++ks) qa[ks] = as_bf16x8(load16(qr + 32 * ks));
       }
-      if (gq == 0) {
-        lvalid[gr] = t >= 0 ? 1 : 0;
-        if (F8) lscale[gr] = sc;
-      }
-      uint8_t *row_base = lrows[gr / kTile] + (gr % kTile) * kRowBytes;
-      if (F8) {
-        // fp8 chunk gq + 4 i (bytes 16 (gq + 4 i) ..) -> 16 bf16 at LDS bytes 32 (gq + 4 i) ..
 #pragma unroll
-        for (int i = 0; i < NV; ++i) {
-          uint8_t *dst = row_base + 32 * gq + 128 * i;
-          *reinterpret_cast<bf16x8 *>(dst) = fp8x8_to_bf16x8(v[i][0], v[i][1]);
-          *reinterpret_cast<bf16x8 *>(dst + 16) = fp8x8_to_bf16x8(v[i][2], v[i][3]);
+      for (int r = 0; r < kTeams; ++r) {
+        if (gq8 == 0) {
+          lvalid[gr8 + kTile * r] = ok[r] ? 1 : 0;
+          if (F8) lscale[gr8 + kTile * r] = sc[r];
         }
-      } else {
-        uint8_t *dst = row_base + 16 * gq;
+        uint8_t *row_base = lrows[r] + gr8 * kRowBytes;
+        if (F8) {
+          // fp8 chunk gq8 + 8 i -> 16 bf16 at LDS bytes 32 (gq8 + 8 i) ..
 #pragma unroll
-        for (int i = 0; i < NV; ++i) *reinterpret_cast<u32x4 *>(dst + 64 * i) = v[i];
+          for (int i = 0; i < NV8; ++i) {
+            if (i < NV8 - 1 || gq8 < 4) {
+              uint8_t *dst = row_base + 32 * gq8 + 256 * i;
+              *reinterpret_cast<bf16x8 *>(dst) = fp8x8_to_bf16x8(w[r][i][0], w[r][i][1]);
+              *reinterpret_cast<bf16x8 *>(dst + 16) = fp8x8_to_bf16x8(w[r][i][2], w[r][i][3]);
+            }
+          }
+        } else {
+          uint8_t *dst = row_base + 16 * gq8;
+#pragma unroll
+          for (int i = 0; i < NV8; ++i) *reinterpret_cast<u32x4 *>(dst + 128 * i) = w[r][i];
+        }
       }
     }
     __syncthreads();
