@@ -557,15 +557,33 @@ __global__ __launch_bounds__(kFinishThreads) void select_finish_kernel(SelectArg
   // the first wavefront: chunk counts -> exclusive prefix cpre[0..chunks],
   // cmap[b] = chunk of candidate 64 b, and the largest candidate key
   if (wave == 0) {
-    constexpr int PL = kMaxChunks / 64;
+    constexpr int PL = kMaxChunks / 64;   // 4: one 16-byte load of each array per lane
+    static_assert(PL == 4, "chunk counts are loaded as one uint4 per lane");
     uint32_t cc[PL];
     uint32_t s = 0, m = 0;
+    if ((chunks & 3) == 0) {
+      // both loads of a lane in flight together (the counts and maxima of the
+      // chunk regions are 16-byte aligned when chunks is a multiple of 4)
+      uint4 c4 = make_uint4(0u, 0u, 0u, 0u), m4 = make_uint4(0u, 0u, 0u, 0u);
+      if (lane * PL < chunks) {
+        c4 = *reinterpret_cast<const uint4 *>(a.ccount + (int64_t)qi * chunks + lane * PL);
+        m4 = *reinterpret_cast<const uint4 *>(a.cmax + (int64_t)qi * chunks + lane * PL);
+      }
+      cc[0] = c4.x;
+      cc[1] = c4.y;
+      cc[2] = c4.z;
+      cc[3] = c4.w;
+      m = max(max(m4.x, m4.y), max(m4.z, m4.w));
 #pragma unroll
-    for (int i = 0; i < PL; ++i) {
-      const int ch = lane * PL + i;
-      cc[i] = ch < chunks ? a.ccount[(int64_t)qi * chunks + ch] : 0u;
-      m = max(m, ch < chunks ? a.cmax[(int64_t)qi * chunks + ch] : 0u);
-      s += cc[i];
+      for (int i = 0; i < PL; ++i) s += cc[i];
+    } else {
+#pragma unroll
+      for (int i = 0; i < PL; ++i) {
+        const int ch = lane * PL + i;
+        cc[i] = ch < chunks ? a.ccount[(int64_t)qi * chunks + ch] : 0u;
+        m = max(m, ch < chunks ? a.cmax[(int64_t)qi * chunks + ch] : 0u);
+        s += cc[i];
+      }
     }
     const uint32_t incl = wave_inclusive_scan(s);
     const bool fits = (uint32_t)__builtin_amdgcn_readlane((int)incl, 63) <= (uint32_t)kRegCap;
