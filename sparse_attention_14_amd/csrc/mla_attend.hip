@@ -150,24 +150,36 @@ __global__ __launch_bounds__(kAttThreads) void attend_bf16_kernel(AttArgs a) {
       u32x4 w[kTeams][NV8];
       float sc[kTeams];
       bool ok[kTeams];
+      // both rows' indices, then both rows' addresses, then all row loads, so
+      // the second row does not wait behind the first row's data; an empty
+      // slot loads the cache's first row and is zeroed when written to LDS
+      int tok[kTeams];
 #pragma unroll
       for (int r = 0; r < kTeams; ++r) {
         const int j = j0 + step * kStepRows + gr8 + kTile * r;
-        const int t = j < j1 ? a.indices[(int64_t)qi * a.k + j] : -1;
-        ok[r] = t >= 0;
-        sc[r] = 0.0f;
-        if (t >= 0) {
-          int slot;
-          const int64_t blk = cache_block(a.latent, seq, t, slot);
-          const uint8_t *p = cache_row(a.latent, blk, slot);
+        tok[r] = j < j1 ? a.indices[(int64_t)qi * a.k + min(j, a.k - 1)] : -1;
+      }
+      const uint8_t *src[kTeams];
+      int64_t sblk[kTeams];
+      int sslot[kTeams];
 #pragma unroll
-          for (int i = 0; i < NV8; ++i) w[r][i] = load16(p + (F8 ? min(16 * gq8 + 128 * i, kW - 16) : 16 * gq8 + 128 * i));
-          if (F8) sc[r] = a.latent.scale[blk * a.latent.scale_block_stride + slot];
-        } else {
+      for (int r = 0; r < kTeams; ++r) {
+        ok[r] = tok[r] >= 0;
+        sblk[r] = cache_block(a.latent, seq, ok[r] ? tok[r] : 0, sslot[r]);
+        src[r] = ok[r] ? cache_row(a.latent, sblk[r], sslot[r]) : a.latent.rows;
+      }
+#pragma unroll
+      for (int r = 0; r < kTeams; ++r) {
+#pragma unroll
+        for (int i = 0; i < NV8; ++i)
+          w[r][i] = load16(src[r] + (F8 ? min(16 * gq8 + 128 * i, kW - 16) : 16 * gq8 + 128 * i));
+        sc[r] = F8 && ok[r] ? a.latent.scale[sblk[r] * a.latent.scale_block_stride + sslot[r]] : 0.0f;
+      }
+#pragma unroll
+      for (int r = 0; r < kTeams; ++r)
+        if (!ok[r])
 #pragma unroll
           for (int i = 0; i < NV8; ++i) w[r][i] = u32x4{0, 0, 0, 0};
-        }
-      }
       if (step == 0) {
 #pragma unroll
         for (int ks = 0; ks < kW / 32; ++ks) qa[ks] = as_bf16x8(load16(qr + 32 * ks));
@@ -417,19 +429,22 @@ __global__ __launch_bounds__(kWideThreads) void attend_wide_kernel(AttArgs a) {
     {
       if (F8) {
         // fp8 chunk gq + 8 i -> 16 bf16 at LDS bytes 32 (gq + 8 i) ..
+        // an empty slot (the cache's first row was loaded) is written as zeros:
+        // its P is 0, but 0 times a non-finite value would not be
         uint8_t *dst = rows + gr * kRowBytes + 32 * gq;
 #pragma unroll
         for (int i = 0; i < NV; ++i) {
           if (i < NV - 1 || gq < 4) {
-            *reinterpret_cast<bf16x8 *>(dst + 256 * i) = fp8x8_to_bf16x8(v[i][0], v[i][1]);
-            *reinterpret_cast<bf16x8 *>(dst + 256 * i + 16) = fp8x8_to_bf16x8(v[i][2], v[i][3]);
+            const u32x4 x = v_ok ? v[i] : u32x4{0, 0, 0, 0};
+            *reinterpret_cast<bf16x8 *>(dst + 256 * i) = fp8x8_to_bf16x8(x[0], x[1]);
+            *reinterpret_cast<bf16x8 *>(dst + 256 * i + 16) = fp8x8_to_bf16x8(x[2], x[3]);
           }
         }
         if (gq == 0) lscale[gr] = v_sc;
       } else {
         uint8_t *dst = rows + gr * kRowBytes + 16 * gq;
 #pragma unroll
-        for (int i = 0; i < NV; ++i) *reinterpret_cast<u32x4 *>(dst + 128 * i) = v[i];
+        for (int i = 0; i < NV; ++i) *reinterpret_cast<u32x4 *>(dst + 128 * i) = v_ok ? v[i] : u32x4{0, 0, 0, 0};
       }
       if (gq == 0) lvalid[gr] = v_ok ? 1 : 0;
     }

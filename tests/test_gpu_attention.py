@@ -126,3 +126,32 @@ def test_attention_is_deterministic(case):
     b = gpu_attend(dp, idx)
     assert torch.equal(a[0].view(torch.int32), b[0].view(torch.int32))
     assert torch.equal(a[1].view(torch.int32), b[1].view(torch.int32))
+
+
+@pytest.mark.parametrize("latent_dtype", ["bf16", "e4m3fn"])
+def test_empty_slots_never_read_a_non_finite_first_row(latent_dtype):
+    """Both kernels fill empty slots (-1 holes, a split's unused tail) without
+    using the cache's data: with the cache's very first row (token 0 of
+    sequence 0) set to NaN and never kept, every output stays finite and
+    matches the oracle (64-head kernel: 20 queries; 16-head kernel: 2)."""
+    for batch in (20, 2):
+        wl = S(inputs.DECODE_8K, name="a20", wid=320 + batch, batch=batch, seq_len=(300, 3000),
+               latent_dtype=latent_dtype)
+        p = inputs.make_problem(wl)
+        row0 = p.latent.storage[0, 0]
+        if latent_dtype == "bf16":
+            row0.view(np.uint16)[:] = 0x7FC0
+        else:
+            row0[:] = 0x7F
+            p.latent.scale[0, 0] = np.nan
+        rng = np.random.default_rng(14)
+        idx = _indices(p, 2048, rng, fill=0.5)
+        for i in range(p.n_q):
+            if p.q_seq[i] == 0:
+                idx[i][idx[i] == 0] = -1           # token 0 of sequence 0 is never kept
+        dp = device.upload(p)
+        out, lse = gpu_attend(dp, torch.from_numpy(idx).cuda())
+        assert torch.isfinite(out).all().item()
+        ref_o, ref_l, _ = oracle.mla_attend(p.q_mla, p.q_mla_dtype, p.latent, p.kv_lora, idx, p.q_seq,
+                                            p.softmax_scale)
+        check_attention(out.cpu().numpy(), lse.cpu().numpy(), ref_o, ref_l, TOL[p.latent.dtype])
