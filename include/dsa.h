@@ -93,8 +93,10 @@ typedef struct {
   dsa_dtype dtype;
 } dsa_cache;
 
-/* dsa_topk flags */
-#define DSA_TOPK_ORDER_INDEX 0u  /* kept indices in ascending token order (the default) */
+/* dsa_topk flags: the order in which a row's kept indices are written */
+#define DSA_TOPK_ORDER_INDEX 0u  /* ascending token order (the default) */
+#define DSA_TOPK_ORDER_SCORE 1u  /* the stable argsort order of -scores ("GLM on an A100, in Vx", "How do we know
+                                    it is right?"): score descending, equal scores by ascending token index */
 
 /*
  * Lightning-indexer scores.  For query i of sequence seq = q_seq ? q_seq[i] : 0
@@ -119,12 +121,15 @@ dsa_status dsa_index_scores(float *scores, int64_t ld_scores, const void *q, dsa
  * Exact top-k.  For query i with n = q_len[i], keeps the first min(k, n)
  * entries of a stable descending sort of scores[i * ld_scores + s], s < n:
  * ties go to the lower token index, -0.0 equals +0.0, NaN ranks below every
- * number.  indices [n_q][k] int32 receive the kept token indices in ascending
- * order followed by -1 padding; counts [n_q] (nullable) receive min(k, n).
- * Selection is integer-only on an order-preserving 32-bit image of each score,
- * so the result is exact and deterministic.
- * Supported: 1 <= k <= 2048, 1 <= max_len <= 262144, n_q <= 65535,
- *   flags = DSA_TOPK_ORDER_INDEX.
+ * number.  indices [n_q][k] int32 receive the kept token indices followed by
+ * -1 padding, in ascending token order (flags = DSA_TOPK_ORDER_INDEX) or in the
+ * stable argsort order of -scores (DSA_TOPK_ORDER_SCORE: score descending,
+ * equal scores by ascending index; the same set, reordered by a sort of the
+ * kept entries); counts [n_q] (nullable) receive min(k, n).  Selection and
+ * ordering are integer-only on an order-preserving 32-bit image of each score,
+ * so the result is exact and deterministic.  Other flags return
+ * DSA_ERR_UNSUPPORTED.
+ * Supported: 1 <= k <= 2048, 1 <= max_len <= 262144, n_q <= 65535.
  */
 dsa_status dsa_topk(int32_t *indices, int32_t *counts, const float *scores, int64_t ld_scores,
                     const int32_t *q_len, int32_t n_q, int32_t k, int32_t max_len, uint32_t flags,
@@ -148,7 +153,9 @@ size_t dsa_topk_workspace_size(int32_t n_q, int32_t k, int32_t max_len);
  * A100, in Vx", "INT4, FP8 and BF16"; dsa_cache_append writes it.
  * Supported: bf16 q with bf16 or fp8 latent rows, W = 576, kv_lora = 512,
  *   n_heads a multiple of 16 up to 128; f32 with W <= 1024 a multiple of 4,
- *   kv_lora <= W a multiple of 4, n_heads <= 128; 1 <= k <= 2048; n_q <= 2^24.
+ *   kv_lora <= W a multiple of 4, n_heads <= 128; 1 <= k <= 2048;
+ *   n_q * n_heads < 2^24 (the launches stay below 2^32 work-items per grid
+ *   dimension; DSA_ERR_UNSUPPORTED beyond).
  */
 dsa_status mla_sparse_attend(float *out, float *lse, const void *q, dsa_dtype q_dtype, const dsa_cache *latent,
                              int32_t kv_lora, const int32_t *indices, int32_t k, const int32_t *q_seq, int32_t n_q,
@@ -222,7 +229,7 @@ size_t dsa_decode_window_workspace_size(int32_t batch, int32_t window, int32_t m
  *           query's visible count (trusted).
  *   q_mla [batch * window][mla_heads][latent->width]; out [batch * window]
  *   [mla_heads][kv_lora]; lse [batch * window][mla_heads] (nullable).
- * 1 <= window <= 64, batch * window <= 2^24; supported shapes as for
+ * 1 <= window <= 64, batch * window * mla_heads < 2^24; supported shapes as for
  * mla_sparse_attend.  The workspace needs dsa_decode_shared_workspace_size()
  * bytes (0: none, and workspace may then be NULL).
  */
@@ -293,7 +300,7 @@ dsa_status mla_absorb_out(float *out, const float *o_lat, const void *w_uv, int3
  * call leave an unspecified one of them.  Values quantized to fp8 must be finite
  * (otherwise the bytes and scale are unspecified).  seq, pos: device int32
  * [n_new], 0 <= pos[i] < the sequence's capacity (trusted).  n_new = 0 returns
- * DSA_OK.
+ * DSA_OK; n_new >= 2^26 returns DSA_ERR_UNSUPPORTED.
  * Supported: fp8 caches up to 1024 wide; copies whose row size is a multiple of
  * 16 bytes from 16-byte aligned inputs.
  */

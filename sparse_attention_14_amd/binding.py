@@ -16,6 +16,8 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libdsa.so")
 
 DTYPES = {"f32": 0, "bf16": 1, "e4m3fn": 2}
+TOPK_ORDER_INDEX = 0   # dsa_topk flags (include/dsa.h)
+TOPK_ORDER_SCORE = 1
 ELEM_BYTES = {"f32": 4, "bf16": 2, "e4m3fn": 1}
 STATUS = {0: "DSA_OK", 1: "DSA_ERR_INVALID_ARGUMENT", 2: "DSA_ERR_UNSUPPORTED", 3: "DSA_ERR_WORKSPACE_TOO_SMALL",
           4: "DSA_ERR_DEVICE"}

@@ -14,7 +14,11 @@ constexpr int kMaxTopk = 2048;
 constexpr int kMaxLenTopk = 262144;
 constexpr int kMaxWindow = 64;    // queries per sequence in one decode window
 constexpr int kMaxRows = 65535;   // queries per call where each query is one grid row (gridDim.y)
-constexpr int kMaxQueries = 1 << 24;   // queries per call of the attention-only entry points
+// (query, head) pairs per call of the attention entry points: the launches
+// stay below 2^32 work-items per grid dimension (the fp32 kernel runs 256
+// threads per pair, the others fewer)
+constexpr int64_t kMaxQueryHeads = (int64_t(1) << 24) - 1;
+constexpr int kMaxAppend = (1 << 26) - 1;   // new tokens per append call (64 threads each)
 
 int elem_bytes(dsa_dtype d) { return d == DSA_F32 ? 4 : (d == DSA_BF16 ? 2 : 1); }
 
@@ -188,12 +192,15 @@ dsa_status dsa_topk(int32_t *indices, int32_t *counts, const float *scores, int6
   if (n_q < 0 || max_len < 0) return DSA_ERR_INVALID_ARGUMENT;
   if (n_q == 0) return DSA_OK;
   if (!indices || !scores || !q_len || k < 1 || max_len < 1 || ld_scores < max_len) return DSA_ERR_INVALID_ARGUMENT;
-  if (flags != DSA_TOPK_ORDER_INDEX) return DSA_ERR_UNSUPPORTED;
+  if (flags != DSA_TOPK_ORDER_INDEX && flags != DSA_TOPK_ORDER_SCORE) return DSA_ERR_UNSUPPORTED;
   if (k > kMaxTopk || max_len > kMaxLenTopk || n_q > kMaxRows) return DSA_ERR_UNSUPPORTED;
   const TopkPlan p = plan_topk(n_q, k, max_len);
   if (p.total > 0 && (!workspace || workspace_bytes < p.total)) return DSA_ERR_WORKSPACE_TOO_SMALL;
-  return from_hip(launch_topk(indices, counts, scores, ld_scores, q_len, p, workspace, nullptr, 0, 0,
-                              static_cast<hipStream_t>(stream)));
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  hipError_t e = launch_topk(indices, counts, scores, ld_scores, q_len, p, workspace, nullptr, 0, 0, st);
+  if (e == hipSuccess && flags == DSA_TOPK_ORDER_SCORE)
+    e = launch_order_by_score(indices, scores, ld_scores, q_len, n_q, k, st);
+  return from_hip(e);
 }
 
 size_t mla_sparse_attend_workspace_size(int32_t n_q, int32_t n_heads, int32_t kv_lora, int32_t k) {
@@ -211,7 +218,7 @@ dsa_status mla_sparse_attend(float *out, float *lse, const void *q, dsa_dtype q_
   if (!out || !indices || k < 1) return DSA_ERR_INVALID_ARGUMENT;
   dsa_status s = check_attend(q, q_dtype, latent, kv_lora, n_heads);
   if (s != DSA_OK) return s;
-  if (k > kMaxTopk || n_q > kMaxQueries) return DSA_ERR_UNSUPPORTED;
+  if (k > kMaxTopk || (int64_t)n_q * n_heads > kMaxQueryHeads) return DSA_ERR_UNSUPPORTED;
   const AttendPlan p = plan_attend(n_q, n_heads, kv_lora, latent->width, k, q_dtype);
   if (p.total > 0 && (!workspace || workspace_bytes < p.total)) return DSA_ERR_WORKSPACE_TOO_SMALL;
   return from_hip(launch_attend(out, lse, q, attend_dtype(q_dtype, latent), to_dev(latent), kv_lora, indices, k, q_seq, 0, n_q, n_heads,
@@ -350,7 +357,7 @@ dsa_status dsa_decode_shared(float *out, float *lse, const void *q_mla, dsa_dtyp
   if (!out || !indices || k < 1) return DSA_ERR_INVALID_ARGUMENT;
   dsa_status s = check_attend(q_mla, q_mla_dtype, latent, kv_lora, mla_heads);
   if (s != DSA_OK) return s;
-  if (k > kMaxTopk || (int64_t)batch * window > kMaxQueries) return DSA_ERR_UNSUPPORTED;
+  if (k > kMaxTopk || (int64_t)batch * window * mla_heads > kMaxQueryHeads) return DSA_ERR_UNSUPPORTED;
   const int32_t n_q = batch * window;
   // the size query assumes the bf16 plan (the larger one)
   const size_t need = dsa_decode_shared_workspace_size(batch, window, k, mla_heads, kv_lora);
@@ -419,6 +426,7 @@ dsa_status dsa_cache_append(const dsa_cache *keys, const void *new_keys, dsa_dty
     if (s != DSA_OK) return s;
   }
   if (n_new == 0) return DSA_OK;
+  if (n_new > kMaxAppend) return DSA_ERR_UNSUPPORTED;
   return from_hip(launch_cache_append(keys ? &kd : nullptr, keys ? (int)keys->dtype : -1, new_keys,
                                       (int)new_keys_dtype, latent ? &ld : nullptr, latent ? (int)latent->dtype : -1,
                                       new_latent, (int)new_latent_dtype, seq, pos, n_new,

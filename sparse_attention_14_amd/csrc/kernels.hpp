@@ -56,6 +56,12 @@ hipError_t launch_topk(int32_t *indices, int32_t *counts, const float *scores, i
                        const TopkPlan &plan, void *workspace, const uint32_t *bounds, int n_bounds, int group_tokens,
                        hipStream_t stream);
 
+// Reorders each row's kept indices (as launch_topk writes them: ascending,
+// min(k, q_len[i]) of them, then -1) into score-descending order, equal
+// scores by ascending index.  k <= 2048.
+hipError_t launch_order_by_score(int32_t *indices, const float *scores, int64_t ld, const int32_t *q_len, int n_q,
+                                 int k, hipStream_t stream);
+
 // ---- sparse MLA attention ---------------------------------------------------
 struct AttendPlan {
   int n_q, n_heads, kv_lora, width, k;

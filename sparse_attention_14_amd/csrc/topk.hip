@@ -674,7 +674,65 @@ __global__ __launch_bounds__(256) void bound_kernel(const float *__restrict__ sc
   }
 }
 
+// Reorders each row's kept indices (ascending token order, count = min(k, n),
+// -1 padding after them) into the stable argsort order of -scores: score
+// descending, equal scores by ascending token index.  Every kept token becomes
+// the 64-bit value (order_key(score) << 32) | ~token, which orders exactly that
+// way (tokens are distinct, so no two values are equal), and a bitonic network
+// in LDS sorts the values descending; padding values are 0, below every real
+// one (~token >= 2^31).  One workgroup per row.
+constexpr int kOrderThreads = 1024;
+constexpr int kOrderMax = 2048;
+
+__global__ __launch_bounds__(kOrderThreads) void order_by_score_kernel(int32_t *__restrict__ indices,
+                                                                       const float *__restrict__ scores, int64_t ld,
+                                                                       const int32_t *__restrict__ q_len, int k) {
+  __shared__ uint64_t v[kOrderMax];
+  const int qi = blockIdx.y;
+  const int n = q_len[qi];
+  const int cnt = n < k ? n : k;
+  if (cnt <= 1) return;
+  int lg = 0;
+  while ((1 << lg) < cnt) ++lg;
+  const int P = 1 << lg;
+  int32_t *row = indices + (int64_t)qi * k;
+  const float *srow = scores + (int64_t)qi * ld;
+  for (int j = threadIdx.x; j < P; j += kOrderThreads) {
+    uint64_t c = 0;
+    if (j < cnt) {
+      const uint32_t t = (uint32_t)row[j];
+      c = ((uint64_t)order_key(srow[t]) << 32) | (uint64_t)(~t);
+    }
+    v[j] = c;
+  }
+  __syncthreads();
+  for (int ls = 1; ls <= lg; ++ls) {            // blocks of 2^ls: descending when (i & 2^ls) == 0
+    for (int lt = ls - 1; lt >= 0; --lt) {      // compare distance 2^lt
+      for (int t = threadIdx.x; t < (P >> 1); t += kOrderThreads) {
+        const int i = ((t >> lt) << (lt + 1)) | (t & ((1 << lt) - 1));
+        const int j = i | (1 << lt);
+        const uint64_t a = v[i], b = v[j];
+        const bool desc = (i & (1 << ls)) == 0;
+        if (desc ? a < b : a > b) {
+          v[i] = b;
+          v[j] = a;
+        }
+      }
+      __syncthreads();
+    }
+  }
+  for (int j = threadIdx.x; j < cnt; j += kOrderThreads) row[j] = (int32_t)(~(uint32_t)v[j]);
+}
+
 }  // namespace
+
+hipError_t launch_order_by_score(int32_t *indices, const float *scores, int64_t ld, const int32_t *q_len, int n_q,
+                                 int k, hipStream_t stream) {
+  if (k > kOrderMax || n_q > 65535) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(order_by_score_kernel, dim3(1, n_q), dim3(kOrderThreads), 0, stream, indices, scores, ld,
+                     q_len, k);
+  return hipGetLastError();
+}
 
 TopkPlan plan_topk(int n_q, int k, int max_len) {
   TopkPlan p{};

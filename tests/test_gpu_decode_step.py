@@ -11,7 +11,7 @@ import sparse_attention_14_amd as dsa
 import oracle
 from sparse_attention_14_amd import device, inputs
 
-from gpu_util import TOL, check_attention, check_scores, gpu_decode_step
+from gpu_util import TOL, check_attention, check_scores, check_selection_near_ties, fmt_scores, gpu_decode_step
 
 pytestmark = pytest.mark.gpu
 
@@ -41,25 +41,31 @@ def test_decode_step_stages(case):
     out, lse, scores, idx, ws = gpu_decode_step(dp)
     g_scores = scores.cpu().numpy()
     ref_scores = oracle.index_scores(p.q_idx, p.q_idx_dtype, p.w_idx, p.keys, p.q_seq, p.q_len)
-    check_scores(p, g_scores, ref_scores)
+    r = check_scores(p, g_scores, ref_scores)
     g_idx = idx.cpu().numpy()
     ref_idx, _ = oracle.topk(g_scores.astype(np.float64), p.q_len, p.topk)
     assert np.array_equal(g_idx, ref_idx)
     ref_o, ref_l, _ = oracle.mla_attend(p.q_mla, p.q_mla_dtype, p.latent, p.kv_lora, g_idx, p.q_seq, p.softmax_scale)
     worst = check_attention(out.cpu().numpy(), lse.cpu().numpy(), ref_o, ref_l, TOL[p.latent.dtype])
-    print(f"  attention worst relative error {worst:.3g}")
+    print(f"  {fmt_scores(r)}; attention worst relative error {worst:.3g}")
 
 
 def test_decode_step_end_to_end_oracle(case):
-    """The oracle's own chain (its scores -> its top-k -> its attention).  Index
-    lists may differ only where two scores are within tolerance of each other;
-    the count is reported, and outputs are compared where the lists agree."""
+    """The oracle's own chain (its scores -> its top-k -> its attention).  A
+    row's kept set may differ from the oracle's only by tokens whose oracle
+    score is within the fp32 accumulation bound of the row's k-th oracle score
+    (a swap the score tolerance allows); rows whose sets agree must match the
+    oracle's attention within tolerance."""
     p, dp = case
     out, lse, scores, idx, ws = gpu_decode_step(dp)
     ref = oracle.decode_step(p)
     g_idx = idx.cpu().numpy()
-    same = np.all(g_idx == ref["indices"], axis=1)
-    print(f"  rows with identical index lists: {same.sum()} / {p.n_q}")
+    sel = check_selection_near_ties(p, g_idx, ref["indices"], ref["scores"])
+    same = np.array([set(g_idx[i][g_idx[i] >= 0]) == set(ref["indices"][i][ref["indices"][i] >= 0])
+                     for i in range(p.n_q)])
+    print(f"  rows whose kept set differs from the oracle's own chain: {sel['rows_differing']} / {p.n_q} "
+          f"(worst gap {sel['worst_gap_over_bound']:.3g} x bound)")
+    assert same.sum() == p.n_q - sel["rows_differing"]
     if same.any():
         check_attention(out.cpu().numpy()[same], lse.cpu().numpy()[same], ref["out"][same], ref["lse"][same],
                         TOL[p.latent.dtype])

@@ -6,7 +6,7 @@ import torch
 import oracle
 from sparse_attention_14_amd import device, inputs
 
-from gpu_util import check_scores, gpu_scores
+from gpu_util import check_scores, fmt_scores, gpu_scores
 
 pytestmark = pytest.mark.gpu
 
@@ -53,8 +53,8 @@ def test_scores_match_oracle(case):
     print(f"case {p.name}: n_q={p.n_q} max_len={p.max_len} keys={p.keys.dtype} paged={p.keys.paged}", flush=True)
     g = gpu_scores(dp).cpu().numpy()
     ref = oracle.index_scores(p.q_idx, p.q_idx_dtype, p.w_idx, p.keys, p.q_seq, p.q_len)
-    worst = check_scores(p, g, ref)
-    print(f"  worst scaled error {worst:.3g}")
+    r = check_scores(p, g, ref)
+    print("  " + fmt_scores(r))
     for i in range(p.n_q):
         assert np.all(np.isnan(g[i, int(p.q_len[i]):])), "entries beyond q_len were written"
 

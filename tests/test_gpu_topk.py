@@ -1,23 +1,26 @@
 """GPU parity: dsa_topk indices bit-exact against the oracle's top-k of the same
-score array (first min(k, n) of a stable argsort of -score, ascending output)."""
+score array (first min(k, n) of a stable argsort of -score), in ascending
+token order and, with DSA_TOPK_ORDER_SCORE, in the argsort order itself."""
 import numpy as np
 import pytest
 import torch
 
 import oracle
+from sparse_attention_14_amd import binding
 
 from gpu_util import gpu_topk
 
 pytestmark = pytest.mark.gpu
 
 
-def _run(scores_np: np.ndarray, lens, k: int):
+def _run(scores_np: np.ndarray, lens, k: int, order: str = "index"):
     scores_np = np.ascontiguousarray(scores_np, dtype=np.float32)
     max_len = scores_np.shape[1]
     s = torch.from_numpy(scores_np).cuda()
     ql = torch.tensor(np.asarray(lens, np.int32)).cuda()
-    idx, cnt, ws = gpu_topk(s, ql, k, max_len)
-    ref_idx, ref_cnt = oracle.topk(scores_np.astype(np.float64), np.asarray(lens, np.int32), k)
+    flags = binding.TOPK_ORDER_INDEX if order == "index" else binding.TOPK_ORDER_SCORE
+    idx, cnt, ws = gpu_topk(s, ql, k, max_len, flags=flags)
+    ref_idx, ref_cnt = oracle.topk(scores_np.astype(np.float64), np.asarray(lens, np.int32), k, order=order)
     gi, gc = idx.cpu().numpy(), cnt.cpu().numpy()
     for i in range(len(lens)):
         if not np.array_equal(gi[i], ref_idx[i]):
@@ -174,3 +177,65 @@ def test_many_rows_with_a_positional_trend():
     s = (trend[None, :] + rng.standard_normal((rows, n)).astype(np.float32))
     lens = rng.integers(8000, n + 1, size=rows)
     _run(s, lens, 2048)
+
+
+# ------------------------------------------------ DSA_TOPK_ORDER_SCORE ---
+
+def test_score_order_long_rows_with_boundary_ties():
+    """Argsort order (score descending, equal scores by ascending index) on the
+    spread (several workgroups per row) path, with 9-way ties at the boundary
+    and 1 % of scores duplicated elsewhere."""
+    rng = np.random.default_rng(21)
+    n, k = 131072, 2048
+    s = (rng.standard_normal((4, n)) * 4 + 12).astype(np.float32)
+    for r in range(4):
+        dup = rng.choice(n, n // 100, replace=False)
+        s[r, dup] = s[r, rng.choice(n, dup.size)]
+        order = np.argsort(-s[r].astype(np.float64), kind="stable")
+        t = int(order[k - 1])
+        others = order[k + 50:]
+        s[r, rng.choice(others, 8, replace=False)] = s[r, t]
+    print("case: score order, 4 x 131072 with ties", flush=True)
+    _run(s, [n, n, 100000, 4097], k, order="score")
+
+
+def test_score_order_heavy_ties_and_special_values():
+    rng = np.random.default_rng(22)
+    s = rng.integers(0, 6, size=(3, 40000)).astype(np.float32)
+    print("case: score order, six values", flush=True)
+    _run(s, [40000, 39999, 20000], 2048, order="score")
+    _run(s, [40000, 39999, 20000], 17, order="score")
+    vals = np.array([np.nan, -np.nan, np.inf, -np.inf, 0.0, -0.0, 1.0, -1.0, 1e-40, -1e-40, 3.4e38, -3.4e38],
+                    np.float32)
+    s = vals[rng.integers(0, len(vals), size=(3, 9000))]
+    print("case: score order, special values", flush=True)
+    _run(s, [9000, 5000, 8999], 2048, order="score")
+    _run(s, [9000, 5000, 8999], 5, order="score")
+
+
+@pytest.mark.parametrize("n", [0, 1, 2, 63, 64, 65, 1000, 2047, 2048, 2049])
+def test_score_order_context_at_most_k(n):
+    """n <= k keeps every token, in argsort order; padding stays -1."""
+    rng = np.random.default_rng(100 + n)
+    s = np.round(rng.standard_normal((3, 5000)) * 3).astype(np.float32)   # many exact ties
+    _run(s, [n, min(n + 1, 5000), max(n - 1, 0)], 2048, order="score")
+
+
+def test_score_order_many_rows_one_workgroup_each():
+    rng = np.random.default_rng(23)
+    s = np.round(rng.standard_normal((150, 10000)) * 8).astype(np.float32)
+    lens = rng.integers(1, 10001, size=150)
+    _run(s, lens, 2048, order="score")
+    _run(s, lens, 100, order="score")
+
+
+def test_score_order_is_a_permutation_of_index_order():
+    rng = np.random.default_rng(24)
+    a = (rng.standard_normal((4, 60000))).astype(np.float32)
+    s = torch.from_numpy(a).cuda()
+    ql = torch.full((4,), 60000, dtype=torch.int32).cuda()
+    i0, _, _ = gpu_topk(s, ql, 2048, 60000, flags=binding.TOPK_ORDER_INDEX)
+    i1, _, _ = gpu_topk(s, ql, 2048, 60000, flags=binding.TOPK_ORDER_SCORE)
+    assert torch.equal(torch.sort(i1, dim=1).values, i0)
+    v = torch.gather(s, 1, i1.long())
+    assert torch.all(v[:, 1:] <= v[:, :-1]).item()

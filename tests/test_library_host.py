@@ -85,7 +85,8 @@ def test_topk_validation(lib):
     assert f(None, None, 16, 100, 16, 1, 2048, 100, 0, None, 0, None) == 1
     assert f(16, None, 16, 100, 16, 1, 0, 100, 0, None, 0, None) == 1
     assert f(16, None, 16, 100, 16, 1, 4096, 100, 0, None, 0, None) == 2      # k > 2048
-    assert f(16, None, 16, 100, 16, 1, 16, 100, 1, None, 0, None) == 2        # unknown flag
+    assert f(16, None, 16, 100, 16, 1, 16, 100, 2, None, 0, None) == 2        # unknown flag
+    assert f(16, None, 16, 100, 16, 1, 16, 100, 7, None, 0, None) == 2
     assert f(16, None, 16, 1 << 20, 16, 1, 16, 1 << 20, 0, None, 0, None) == 2  # max_len too long
     assert f(16, None, 16, 131072, 16, 4, 2048, 131072, 0, None, 0, None) == 3  # needs a workspace
     assert f(16, None, 16, 100, 16, 65536, 2048, 100, 0, None, 0, None) == 2  # one grid row per query
@@ -112,6 +113,10 @@ def test_attend_validation(lib):
     assert call(k=4096) == 2
     assert call(n_q=4) == 3                                           # split plan needs a workspace
     assert call(n_q=(1 << 24) + 1) == 2
+    assert call(n_q=(1 << 18), heads=64) == 2                          # n_q * heads reaches 2^24
+    assert call(n_q=(1 << 20), heads=16) == 2
+    assert call(q_dtype=0, kv_lora=64, n_q=(1 << 17), heads=128,
+                cache=_cache(dtype=0, width=80, row_stride=320, block_stride=320 * 1024)) == 2
 
 
 def test_decode_step_validation(lib):
@@ -199,6 +204,7 @@ def test_cache_append_validation(lib):
     assert call(latent=odd, n=0) == 2                                 # 200-byte rows are not 16-byte chunks
     noscale = _cache(dtype=2, row_stride=128, block_stride=128 * 1024)
     assert call(keys=noscale, n=0) == 1
+    assert call(n=1 << 26) == 2                                       # 64 threads per token: 2^32 work-items
 
 
 def test_decode_shared_validation(lib):
@@ -213,6 +219,7 @@ def test_decode_shared_validation(lib):
     assert call(window=0) == 1
     assert call(window=65) == 2
     assert call(batch=(1 << 22) + 1, window=4) == 2                   # more than 2^24 queries
+    assert call(batch=(1 << 16), window=4) == 2                       # 2^18 queries x 64 heads = 2^24
     assert call(out=None) == 1
     assert call(idx=None) == 1
     assert call(k=0) == 1
