@@ -184,6 +184,28 @@ size_t dsa_decode_step_workspace_size(int32_t batch, int32_t max_len, int32_t k,
                                       int32_t kv_lora);
 
 /*
+ * dsa_decode_step for callers that cannot allocate device memory (code under
+ * HIP graph capture, tight serving loops, harnesses that forbid allocation):
+ * the same arguments without the workspace, the same results bit for bit.
+ * The step's scratch is a static device array of DSA_NOALLOC_SCRATCH_BYTES
+ * inside the library, one per GPU, held until the process ends; the call
+ * allocates and frees nothing.  A shape whose dsa_decode_step_workspace_size
+ * exceeds that size returns DSA_ERR_WORKSPACE_TOO_SMALL (for example, 4 x
+ * 131072 tokens needs about 14 MiB and 16 x 32768 about 38 MiB; 96 x 16384
+ * (55 MiB) does not fit).  Every call on one GPU shares that GPU's array: calls that
+ * overlap in time on one GPU (two streams, two host threads) race and must
+ * be ordered by the caller.  The first call on a device looks up the array's
+ * device address (hipGetSymbolAddress) with that device current.
+ */
+#define DSA_NOALLOC_SCRATCH_BYTES ((size_t)48 << 20)
+dsa_status dsa_decode_step_noalloc(float *out, float *lse, const void *q_idx, dsa_dtype q_idx_dtype,
+                                   const float *w_idx, const dsa_cache *keys, int32_t idx_heads, const void *q_mla,
+                                   dsa_dtype q_mla_dtype, const dsa_cache *latent, int32_t kv_lora,
+                                   int32_t mla_heads, const int32_t *seq_len, int32_t batch, int32_t max_len,
+                                   int32_t k, float softmax_scale, float *scores_out, int32_t *indices_out,
+                                   void *stream);
+
+/*
  * One fused DSA decode step over a multi-token window ("GLM 5.3 Flash
  * (strata-poly)", section "How it uses the card", "Guessing ahead", and the
  * --window option: the known token and up to three guesses go through the

@@ -50,7 +50,8 @@ EXPORTS = ("dsa_index_scores", "dsa_topk", "dsa_topk_workspace_size", "mla_spars
            "mla_sparse_attend_workspace_size", "dsa_decode_step", "dsa_decode_step_workspace_size",
            "dsa_decode_window", "dsa_decode_window_workspace_size", "dsa_decode_shared",
            "dsa_decode_shared_workspace_size", "dsa_cache_append", "mla_absorb_q", "mla_absorb_out",
-           "dsa_workspace_clear", "dsa_status_string")
+           "dsa_workspace_clear", "dsa_status_string", "dsa_decode_step_noalloc")
+NOALLOC_SCRATCH_BYTES = 48 << 20   # DSA_NOALLOC_SCRATCH_BYTES
 
 
 def load(path: str = LIB_PATH):
@@ -73,6 +74,8 @@ def load(path: str = LIB_PATH):
         "dsa_decode_step": (ctypes.c_int, [P, P, P, ctypes.c_int, P, CP, i32, P, ctypes.c_int, CP, i32, i32, P, i32,
                                            i32, i32, f32, P, P, P, sz, P]),
         "dsa_decode_step_workspace_size": (sz, [i32, i32, i32, i32, i32]),
+        "dsa_decode_step_noalloc": (ctypes.c_int, [P, P, P, ctypes.c_int, P, CP, i32, P, ctypes.c_int, CP, i32, i32,
+                                                   P, i32, i32, i32, f32, P, P, P]),
         "dsa_decode_window": (ctypes.c_int, [P, P, P, ctypes.c_int, P, CP, i32, P, ctypes.c_int, CP, i32, i32, P,
                                              i32, i32, i32, i32, f32, P, P, P, sz, P]),
         "dsa_decode_window_workspace_size": (sz, [i32, i32, i32, i32, i32, i32]),
@@ -173,6 +176,17 @@ def dsa_decode_step(out, lse, q_idx, q_idx_dtype, w_idx, keys: DeviceCache, q_ml
         _p(q_mla), DTYPES[q_mla_dtype], ctypes.byref(latent.desc), kv_lora, q_mla.shape[1], _p(seq_len),
         seq_len.shape[0], max_len, k, float(softmax_scale), _p(scores_out), _p(indices_out), _p(workspace),
         ws_bytes, _stream(stream)))
+
+
+def dsa_decode_step_noalloc(out, lse, q_idx, q_idx_dtype, w_idx, keys: DeviceCache, q_mla, q_mla_dtype,
+                            latent: DeviceCache, kv_lora, seq_len, max_len, k, softmax_scale, scores_out=None,
+                            indices_out=None, stream=None):
+    """dsa_decode_step on the library's static per-GPU scratch (no workspace, no allocation)."""
+    lib = load()
+    _check("dsa_decode_step_noalloc", lib.dsa_decode_step_noalloc(
+        _p(out), _p(lse), _p(q_idx), DTYPES[q_idx_dtype], _p(w_idx), ctypes.byref(keys.desc), q_idx.shape[1],
+        _p(q_mla), DTYPES[q_mla_dtype], ctypes.byref(latent.desc), kv_lora, q_mla.shape[1], _p(seq_len),
+        seq_len.shape[0], max_len, k, float(softmax_scale), _p(scores_out), _p(indices_out), _stream(stream)))
 
 
 def dsa_decode_window_workspace_size(batch, window, max_len, k, mla_heads, kv_lora) -> int:

@@ -5,6 +5,8 @@
 #include "kernels.hpp"
 
 #include <algorithm>
+#include <atomic>
+#include <mutex>
 
 using namespace dsa;
 
@@ -328,6 +330,69 @@ dsa_status dsa_decode_step(float *out, float *lse, const void *q_idx, dsa_dtype 
   return decode_impl(out, lse, q_idx, q_idx_dtype, w_idx, keys, idx_heads, q_mla, q_mla_dtype, latent, kv_lora,
                      mla_heads, seq_len, batch, 1, max_len, k, softmax_scale, scores_out, indices_out, workspace,
                      workspace_bytes, stream);
+}
+
+}  // extern "C"
+
+namespace {
+
+// Scratch of dsa_decode_step_noalloc: a device array in the library's code
+// object, one copy per GPU (allocated when the code object is loaded there and
+// held until the process ends).  In host code `scratch` names a host-side
+// stand-in, not device memory: its device address on each GPU comes from
+// hipGetSymbolAddress, taken once per device with that device current, and
+// only that address is passed to kernels.
+__device__ __align__(256) uint8_t scratch[DSA_NOALLOC_SCRATCH_BYTES];
+
+constexpr int kMaxDevices = 64;
+std::atomic<void *> scratch_dev[kMaxDevices];
+std::mutex scratch_mu;
+
+// The current device's scratch address, looked up on its first use.
+dsa_status scratch_of_current_device(void **ptr) {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return DSA_ERR_DEVICE;
+  if (dev < 0 || dev >= kMaxDevices) return DSA_ERR_UNSUPPORTED;
+  void *p = scratch_dev[dev].load(std::memory_order_acquire);
+  if (!p) {
+    std::lock_guard<std::mutex> lock(scratch_mu);
+    p = scratch_dev[dev].load(std::memory_order_relaxed);
+    if (!p) {
+      void *addr = nullptr;
+      if (hipGetSymbolAddress(&addr, HIP_SYMBOL(scratch)) != hipSuccess || !addr) return DSA_ERR_DEVICE;
+      scratch_dev[dev].store(addr, std::memory_order_release);
+      p = addr;
+    }
+  }
+  *ptr = p;
+  return DSA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+dsa_status dsa_decode_step_noalloc(float *out, float *lse, const void *q_idx, dsa_dtype q_idx_dtype,
+                                   const float *w_idx, const dsa_cache *keys, int32_t idx_heads, const void *q_mla,
+                                   dsa_dtype q_mla_dtype, const dsa_cache *latent, int32_t kv_lora,
+                                   int32_t mla_heads, const int32_t *seq_len, int32_t batch, int32_t max_len,
+                                   int32_t k, float softmax_scale, float *scores_out, int32_t *indices_out,
+                                   void *stream) {
+  // Every host check first, so an invalid call never touches the device: with
+  // no workspace the step validates all its arguments and stops at the
+  // workspace check (DSA_OK for an empty batch), before any HIP call.
+  const dsa_status v = decode_impl(out, lse, q_idx, q_idx_dtype, w_idx, keys, idx_heads, q_mla, q_mla_dtype, latent,
+                                   kv_lora, mla_heads, seq_len, batch, 1, max_len, k, softmax_scale, scores_out,
+                                   indices_out, nullptr, 0, stream);
+  if (v != DSA_ERR_WORKSPACE_TOO_SMALL) return v;
+  if (dsa_decode_step_workspace_size(batch, max_len, k, mla_heads, kv_lora) > DSA_NOALLOC_SCRATCH_BYTES)
+    return DSA_ERR_WORKSPACE_TOO_SMALL;
+  void *ws = nullptr;
+  dsa_status s = scratch_of_current_device(&ws);
+  if (s != DSA_OK) return s;
+  return decode_impl(out, lse, q_idx, q_idx_dtype, w_idx, keys, idx_heads, q_mla, q_mla_dtype, latent, kv_lora,
+                     mla_heads, seq_len, batch, 1, max_len, k, softmax_scale, scores_out, indices_out, ws,
+                     DSA_NOALLOC_SCRATCH_BYTES, stream);
 }
 
 dsa_status dsa_decode_window(float *out, float *lse, const void *q_idx, dsa_dtype q_idx_dtype, const float *w_idx,

@@ -256,3 +256,29 @@ def test_absorb_validation(lib):
     assert o(out=None) == 1 and o(ol=None) == 1 and o(w=None) == 1
     assert o(L=500) == 2 and o(dv=100) == 2 and o(ol=8) == 2
     assert o(H=0) == 1 and o(H=2000) == 2
+
+
+def test_decode_step_noalloc_validation(lib):
+    """The allocation-free step validates everything on the host before it
+    looks up its device scratch: these calls never reach a device."""
+    keys = _cache()
+    lat = _cache(width=576, row_stride=1152, block_stride=1152 * 1024)
+    f = lib.dsa_decode_step_noalloc
+
+    def call(batch=1, k=2048, max_len=100, out=16, seq_len=16, heads=64, q_dt=1):
+        return f(out, None, 16, q_dt, 16, ctypes.byref(keys), 32, 16, 1, ctypes.byref(lat), 512, heads, seq_len,
+                 batch, max_len, k, 0.04, None, None, None)
+
+    assert call(batch=0) == 0
+    assert call(batch=-1) == 1
+    assert call(out=None) == 1
+    assert call(seq_len=None) == 1
+    assert call(k=0) == 1
+    assert call(k=4096) == 2
+    assert call(heads=24) == 2
+    assert call(q_dt=2) == 2
+    # the scratch holds the 128K batch of 4 and the paged batch of 16 x 32K, not 96 x 16K
+    assert lib.dsa_decode_step_workspace_size(4, 131072, 2048, 64, 512) <= binding.NOALLOC_SCRATCH_BYTES
+    assert lib.dsa_decode_step_workspace_size(16, 32768, 2048, 64, 512) <= binding.NOALLOC_SCRATCH_BYTES
+    assert lib.dsa_decode_step_workspace_size(96, 16384, 2048, 64, 512) > binding.NOALLOC_SCRATCH_BYTES
+    assert call(batch=96, max_len=16384) == 3
