@@ -159,23 +159,27 @@ def clone_cache(c):
                        block_table=None if c.block_table is None else c.block_table.clone())
 
 
-def read_traffic(kernel_tag: str):
-    """HBM traffic per launch from the committed PMC summary, if it was taken on
-    the current kernel source (its hash matches); else None."""
+def score_source_hash() -> str:
     import hashlib
-    path = os.path.join(ROOT, "profiles", f"pmc_{kernel_tag}.txt")
+    src = open(os.path.join(ROOT, "sparse_attention_14_amd", "csrc", "index_scores.hip"), "rb").read()
+    return hashlib.sha256(src).hexdigest()[:16]
+
+
+def read_profile_value(name: str, key: str):
+    """A value from a committed profile summary (profiles/<name>), if that
+    summary was taken on the current score-kernel source (its hash matches);
+    else None."""
+    path = os.path.join(ROOT, "profiles", name)
     if not os.path.exists(path):
         return None
-    src = open(os.path.join(ROOT, "sparse_attention_14_amd", "csrc", "index_scores.hip"), "rb").read()
-    h = hashlib.sha256(src).hexdigest()[:16]
     vals = {}
     for line in open(path):
         if ":" in line:
             k, v = line.split(":", 1)
             vals[k.strip()] = v.strip()
-    if vals.get("source_sha256_16") != h or "traffic_bytes_per_launch" not in vals:
+    if vals.get("source_sha256_16") != score_source_hash() or key not in vals:
         return None
-    return float(vals["traffic_bytes_per_launch"])
+    return float(vals[key])
 
 
 def main():
@@ -328,14 +332,20 @@ def main():
                                  q_seq=dp.q_seq)
         e1.record(kstream)
     e1.synchronize()
+    # back-to-back launches between two events: the same per-dispatch duration a
+    # kernel trace of this command reports for these launches (an event pair
+    # around every single launch would add the events' own overhead)
     t_kernel = e0.elapsed_time(e1) / 1e3 / n_k
     kbytes = score_kernel_bytes(p)
     k_gbs = kbytes / t_kernel / 1e9
-    traffic = read_traffic("scores_decode_128k_fp8")
+    traffic = read_profile_value("pmc_scores_decode_128k_fp8.txt", "traffic_bytes_per_launch")
+    trace_us = read_profile_value("kernel_trace_scores_decode_128k_fp8.txt", "avg_us_standalone")
     roofline = {"bound": "hbm", "achieved": round(k_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                 "frac": round(k_gbs / HBM_PEAK_GBS, 4), "traffic": traffic,
                 "kernel": "scores_mfma_kernel (fp8 keys, 128-wide, 32 heads)", "bytes_per_launch": kbytes,
-                "avg_launch_us": round(t_kernel * 1e6, 3)}
+                "avg_launch_us": round(t_kernel * 1e6, 3), "launches": n_k,
+                "trace_avg_us": trace_us,
+                "frac_from_trace": None if trace_us is None else round(kbytes / (trace_us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4)}
 
     # ------------------------------------------------- measured peaks ---
     # What this GPU reaches on plain work, as context for the fractions of the
@@ -661,6 +671,9 @@ def main():
         "decode_us_per_step_one_per_launch": round(t_single * 1e6, 2), "decode_us_per_step_spread": spread,
         "decode_us_per_step_warm": round(t_warm * 1e6, 2),
         "decode_bytes_per_step": step_bytes, "decode_hbm_frac": round(gbs / HBM_PEAK_GBS, 4),
+        "decode_step_roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                                 "frac": round(gbs / HBM_PEAK_GBS, 4), "bytes_per_step": step_bytes,
+                                 "what": "algorithmic bytes of the whole step / step time"},
         "roofline": roofline, "append": append, "shared": shared, "absorb": absorb, "prefill": prefill, "window": window, "latent_fp8": latent8, "configs": configs, "cpu_baseline": cpu, "measured_peaks": measured, "device": dev_name,
         "rocm": torch.version.hip,
     }

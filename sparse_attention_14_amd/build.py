@@ -17,10 +17,11 @@ OUT = os.path.join(HERE, "libdsa.so")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
 
-# Per-file code-generation options.  index_scores.hip: MFMA results in ordinary
-# VGPRs (not accumulation registers), so the score epilogue reads them without a
-# v_accvgpr_read copy per element.
-FILE_FLAGS = {"index_scores.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
+# Per-file code-generation options.  index_scores.hip, prefill_scores.hip: MFMA
+# results in ordinary VGPRs (not accumulation registers), so the score epilogue
+# reads them without a v_accvgpr_read copy per element.
+FILE_FLAGS = {"index_scores.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
+              "prefill_scores.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
 
 
 def sources():

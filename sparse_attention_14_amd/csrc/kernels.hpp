@@ -33,6 +33,11 @@ hipError_t launch_index_scores(float *scores, int64_t ld, const void *q, int q_d
                                const CacheDev &keys, int key_dt, const int32_t *q_seq, int seq_ident,
                                const int32_t *q_len, int n_q, int n_heads, int max_len, const ScoreBounds &sb,
                                hipStream_t stream, int qw = 1, int window = 0, int32_t *row_len_out = nullptr);
+// The GEMM-shaped score kernel for many queries (bf16 q and keys, 128 wide, up
+// to 32 heads); paged caches need block_size = 1 << block_shift.
+hipError_t launch_prefill_scores(float *scores, int64_t ld, const uint16_t *q, const float *w, const CacheDev &keys,
+                                 const int32_t *q_seq, const int32_t *q_len, int n_q, int n_heads, int max_len,
+                                 int block_shift, hipStream_t stream);
 int score_tiles_per_wave(int rows, int max_len);
 int score_groups_per_row(int rows, int max_len);
 int score_group_tokens(int rows, int max_len);
