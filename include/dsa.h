@@ -128,7 +128,9 @@ dsa_status dsa_index_scores(float *scores, int64_t ld_scores, const void *q, dsa
  * kept entries); counts [n_q] (nullable) receive min(k, n).  Selection and
  * ordering are integer-only on an order-preserving 32-bit image of each score,
  * so the result is exact and deterministic.  Other flags return
- * DSA_ERR_UNSUPPORTED.
+ * DSA_ERR_UNSUPPORTED.  Every row of scores must be readable up to max_len
+ * floats (the kernels may read past a row's visible count, never past
+ * max_len).
  * Supported: 1 <= k <= 2048, 1 <= max_len <= 262144, n_q <= 65535.
  */
 dsa_status dsa_topk(int32_t *indices, int32_t *counts, const float *scores, int64_t ld_scores,

@@ -139,13 +139,15 @@ __device__ __forceinline__ uint32_t wave_max_u32(uint32_t x) {
 // bound on the need-th largest key.  Called by a whole wavefront.
 template <int N>
 __device__ __forceinline__ uint32_t wave_rank_bound(const uint32_t (&x)[N], uint32_t need, int bits) {
+  // one bit per step from the top; the count of keys >= the trial prefix is a
+  // sum of ballot population counts (scalar), not a cross-lane reduction
   uint32_t T = 0;
   for (int b = 31; b >= 32 - bits; --b) {
     const uint32_t c = T | (1u << b);
     uint32_t m = 0;
 #pragma unroll
-    for (int i = 0; i < N; ++i) m += x[i] >= c ? 1u : 0u;
-    if (wave_sum(m) >= need) T = c;
+    for (int i = 0; i < N; ++i) m += (uint32_t)__popcll(__ballot(x[i] >= c));
+    if (m >= need) T = c;
   }
   return T;
 }

@@ -57,6 +57,21 @@ struct AttArgs {
 
 typedef __attribute__((__vector_size__(4 * sizeof(short)))) short i16x4;
 
+// Fetches every argument in one round trip: the returned zero depends on all of
+// them, so code indexed by it waits for one batch of argument loads instead of
+// one dependent scalar round trip per argument at its first use.
+__device__ __forceinline__ int args_together(const AttArgs &a) {
+  int zero;
+  asm("s_mov_b32 %0, 0"
+      : "=s"(zero)
+      : "s"(a.out), "s"(a.lse), "s"(a.q), "s"(a.latent.rows), "s"(a.latent.scale), "s"(a.latent.row_stride),
+        "s"(a.latent.block_stride), "s"(a.latent.scale_block_stride), "s"(a.latent.table), "s"(a.latent.block_size),
+        "s"(a.latent.max_blocks), "s"(a.indices), "s"(a.q_seq), "s"(a.part_o), "s"(a.part_ml), "s"(a.k),
+        "s"(a.n_q), "s"(a.n_heads), "s"(a.splits), "s"(a.rows_per_split), "s"(a.n_hg), "s"(a.pairs),
+        "s"(a.seq_per), "s"(a.scale_log2));
+  return zero;
+}
+
 // Allreduce over the 16 lanes of a DPP row (row_ror 8, 4, 2, 1).
 __device__ __forceinline__ float row16_max(float x) {
   x = fmaxf(x, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x128, 0xF, 0xF, false)));
@@ -102,7 +117,7 @@ __global__ __launch_bounds__(kAttThreads) void attend_bf16_kernel(AttArgs a) {
 
   // XCD-aware mapping: workgroup ids i, i+8, i+16, ... run on one XCD; give the
   // n_hg head groups of a (query, split) pair ids 8 apart.
-  const int lin = blockIdx.x;
+  const int lin = blockIdx.x + args_together(a);
   const int group = lin / (8 * a.n_hg);
   const int rem = lin - group * 8 * a.n_hg;
   const int hg = rem >> 3;

@@ -42,9 +42,9 @@ namespace {
 
 constexpr int kRegCap = 12288;                  // candidates per row held in registers
 constexpr int kBins = kHistBins;                // 4096 (12-bit digits)
-constexpr int kCoarse = kBins + 64;             // 64 super-bins of 64 bins each; before them, per-lane
-                                                // dump slots for elements that do not count, after
-                                                // them the same for the super-bins
+constexpr int kCoarse = kBins + 64;             // 64 super-bins of 64 bins each (summed from the bins);
+                                                // before them, per-lane dump slots for elements that
+                                                // do not count
 constexpr int kHistWords = kCoarse + 128;
 constexpr int kGroup = 1024;                    // tokens per bound group (bound_kernel)
 constexpr int kSamples = 1024;
@@ -99,16 +99,36 @@ struct SelectArgs {
   int local_cap;    // LDS candidate capacity (one workgroup per row)
   int group_tokens; // tokens per bound group
   int bound_most;   // largest rank a bound group can report
+  int max_len;      // allocated row length bound: every row holds at least this many scores
   uint32_t *ccount; // [n_q][chunks] candidates per chunk
   uint32_t *cmax;   // [n_q][chunks] largest candidate key per chunk
   uint32_t *tlo;    // [n_q] the row's candidate bound
   uint2 *cand;      // [n_q][chunks][chunk] (key, token) per chunk
 };
 
+// Fetches every argument in one round trip: the returned zero depends on all of
+// them, so code indexed by it (the row, the chunk) waits for one batch of
+// argument loads instead of one dependent scalar round trip per argument at
+// its first use.
+__device__ __forceinline__ int args_together(const SelectArgs &a) {
+  int zero;
+  asm("s_mov_b32 %0, 0"
+      : "=s"(zero)
+      : "s"(a.indices), "s"(a.counts), "s"(a.scores), "s"(a.ld), "s"(a.q_len), "s"(a.bounds), "s"(a.n_bounds),
+        "s"(a.k), "s"(a.chunk), "s"(a.chunks), "s"(a.local_cap), "s"(a.group_tokens), "s"(a.bound_most),
+        "s"(a.ccount), "s"(a.cmax), "s"(a.tlo), "s"(a.cand), "s"(a.max_len));
+  return zero;
+}
+
 // Number of set bits of `mask` below this lane.
 __device__ __forceinline__ uint32_t lanes_below(uint64_t mask) {
   return __builtin_amdgcn_mbcnt_hi((uint32_t)(mask >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)mask, 0u));
 }
+
+// Waits for every outstanding memory operation of the wavefront: taken before
+// an early return past loads issued ahead of the row-length check, so no load
+// is still in flight when the wavefront ends.
+__device__ __forceinline__ void drain_loads() { __builtin_amdgcn_s_waitcnt(0); }
 
 // Order-preserving prefix over `rounds` (uniform, <= R) rounds of one element per
 // thread: element (m, tid) precedes (m', tid') when m < m' or (m == m' and
@@ -167,7 +187,29 @@ __device__ __forceinline__ void zero_hist(uint32_t *h) {
   uint4 *h4 = reinterpret_cast<uint4 *>(h);
 #pragma unroll
   for (int i = 0; i < kBins / 4 / NT; ++i) h4[threadIdx.x + NT * i] = make_uint4(0, 0, 0, 0);
-  if (threadIdx.x < 64) h[kCoarse + threadIdx.x] = 0u;
+}
+
+// Super-bin counts (64 bins each) summed from the finished fine histogram:
+// thread t adds bins [t B, t B + B) (B = kBins / NT) and the B-bin partial sums
+// of the 64 / B threads of one super-bin are added across their lanes.  Exact
+// and order-independent; it replaces one LDS atomic per key on the 64 super-bin
+// counters, which the keys just above the candidate bound all hit.  Called by
+// every thread after the fine pass and a barrier; a barrier must follow.
+template <int NT>
+__device__ __forceinline__ void coarse_from_fine(uint32_t *h) {
+  constexpr int B = kBins / NT;     // bins per thread (4 or 8)
+  constexpr int TPS = 64 / B;       // threads per super-bin (16 or 8), aligned lane groups
+  static_assert(B % 4 == 0 && TPS >= 1 && 64 % TPS == 0, "fine bins per thread");
+  const uint4 *h4 = reinterpret_cast<const uint4 *>(h) + threadIdx.x * (B / 4);
+  uint32_t s = 0;
+#pragma unroll
+  for (int i = 0; i < B / 4; ++i) {
+    const uint4 v = h4[i];
+    s += (v.x + v.y) + (v.z + v.w);
+  }
+#pragma unroll
+  for (int off = 1; off < TPS; off <<= 1) s += (uint32_t)__shfl_xor((int)s, off, 64);
+  if ((threadIdx.x & (TPS - 1)) == 0) h[kCoarse + threadIdx.x / TPS] = s;
 }
 
 // Highest bin b whose count of keys in bins >= b reaches `need` (1 <= need <=
@@ -227,6 +269,8 @@ __device__ void radix_threshold(H &&hist_pass, uint32_t lo, uint32_t mx, uint32_
     const uint32_t himask = prev >= 32 ? 0u : (0xFFFFFFFFu << prev);
     hist_pass(himask, base, sh, mask);
     __syncthreads();
+    coarse_from_fine<NT>(L.hist);
+    __syncthreads();
     find_from_top(L.hist, need, L.shv);
     __syncthreads();
     base |= L.shv[0] << sh;
@@ -239,8 +283,8 @@ __device__ void radix_threshold(H &&hist_pass, uint32_t lo, uint32_t mx, uint32_
   r = need;
 }
 
-// Histogram increments of one key (branch-free): its bin and super-bin, or
-// this lane's dump slots when it does not count.
+// Histogram increment of one key (branch-free): its bin, or this lane's dump
+// slot when it does not count.
 __device__ __forceinline__ void hist_add(uint32_t *h, bool valid, uint32_t key, uint32_t lo, uint32_t himask,
                                          uint32_t base, int sh, uint32_t mask) {
   const uint32_t off = key - lo;
@@ -248,7 +292,6 @@ __device__ __forceinline__ void hist_add(uint32_t *h, bool valid, uint32_t key, 
   const uint32_t bin = (off >> sh) & mask;
   const uint32_t lane = threadIdx.x & 63;
   atomicAdd(&h[in ? bin : kBins + lane], 1u);
-  atomicAdd(&h[in ? kCoarse + (bin >> 6) : kCoarse + 64 + lane], 1u);
 }
 
 // Rows with n <= k keep every token.
@@ -296,6 +339,19 @@ __device__ void finish_regs(const SelectArgs &a, int qi, uint32_t C, uint32_t lo
     }
   }
   if (tid == 0 && a.counts) a.counts[qi] = a.k;
+}
+
+// Loads the rounds of scores of the pass at g0: token g0 + tid + NT i, clamped
+// to the row's allocated length (a row holds at least max_len scores), so
+// every load is unconditional and none waits for the row's visible count;
+// scores past the visible count are masked by the caller.
+template <int NT, int RP>
+__device__ __forceinline__ void load_pass_clamped(const float *row, int g0, int max_len, float (&v)[RP]) {
+#pragma unroll
+  for (int i = 0; i < RP; ++i) {
+    const int t = g0 + (int)threadIdx.x + NT * i;
+    v[i] = row[t < max_len ? t : max_len - 1];
+  }
 }
 
 // Loads the rounds of scores of the pass at g0: token g0 + tid + NT i (< n).
@@ -397,6 +453,37 @@ __device__ __forceinline__ uint32_t report_quantile(const uint32_t *b, int nb, u
   return wave_rank_bound(x, need, 16);
 }
 
+// The first wavefront's share of a row's bound reports, loaded before the row
+// length is known (lane l holds reports l + 64 i; reports past n_bounds read
+// as 0).  N = 8 covers up to 512 reports, N = 32 up to 2048.
+template <int N>
+__device__ __forceinline__ void load_reports(const SelectArgs &a, int qi, uint32_t (&x)[N]) {
+  const int lane = threadIdx.x & 63;
+  const uint32_t *b = a.bounds + (int64_t)qi * a.n_bounds;
+  const int last = a.n_bounds - 1;
+#pragma unroll
+  for (int i = 0; i < N; ++i) {
+    const int g = lane + 64 * i;
+    x[i] = b[g < last ? g : last];
+  }
+#pragma unroll
+  for (int i = 0; i < N; ++i) x[i] = lane + 64 * i < a.n_bounds ? x[i] : 0u;
+}
+
+// row_bound from reports already loaded by the first wavefront (load_reports).
+template <int N>
+__device__ uint32_t row_bound_from(const SelectArgs &a, int n, const uint32_t (&x)[N], const Lds &L) {
+  const int r = bound_rank(a.k, n / a.group_tokens, a.bound_most);
+  if (r == 0) return 0u;
+  const uint32_t need = (uint32_t)((a.k + r - 1) / r);
+  if (threadIdx.x < 64) {
+    const uint32_t t = wave_rank_bound(x, need, 16);
+    if (threadIdx.x == 0) L.shv[6] = t;
+  }
+  __syncthreads();
+  return L.shv[6];
+}
+
 __device__ uint32_t row_bound(const SelectArgs &a, int qi, int n, const Lds &L) {
   const int r = bound_rank(a.k, n / a.group_tokens, a.bound_most);
   if (r == 0) return 0u;
@@ -417,19 +504,21 @@ __global__ __launch_bounds__(kLocalThreads) void select_local_kernel(SelectArgs 
   constexpr int NT = kLocalThreads;
   extern __shared__ __align__(16) uint32_t lds[];
   const Lds L = carve(lds);
-  const int qi = blockIdx.y;
+  const int zero = args_together(a);
+  const int qi = blockIdx.y + zero;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const float *row = a.scores + (int64_t)qi * a.ld;
+  float v[kPassRounds];
+  load_pass_clamped<NT, kPassRounds>(row, 0, a.max_len, v);   // in flight while the length and bound arrive
   const int n = a.q_len[qi];
   const int k = a.k;
   if (n <= k) {
     emit_all<NT>(a, qi, n);
+    drain_loads();
     return;
   }
-  const float *row = a.scores + (int64_t)qi * a.ld;
   const uint32_t cap = (uint32_t)a.local_cap;
 
-  float v[kPassRounds];
-  load_pass<NT, kPassRounds>(row, 0, n, v);   // in flight while the bound is found
   uint32_t t_lo = 0;
   if ((uint32_t)n > cap) {
     if (a.bounds) {
@@ -497,20 +586,33 @@ __global__ __launch_bounds__(kFilterThreads) void select_filter_kernel(SelectArg
   constexpr int NT = kFilterThreads;
   extern __shared__ __align__(16) uint32_t lds[];
   const Lds L = carve(lds);
-  const int qi = blockIdx.y, c = blockIdx.x;
+  const int zero = args_together(a);
+  const int qi = blockIdx.y + zero, c = blockIdx.x;
   const int tid = threadIdx.x;
+  const float *row = a.scores + (int64_t)qi * a.ld;
+  const int c0 = c * a.chunk;
+  // in flight while the row length arrives: the chunk's scores and, in the
+  // first wavefront, the row's bound reports
+  float v[kPassRounds];
+  load_pass_clamped<NT, kPassRounds>(row, c0, a.max_len, v);
+  const bool few_reports = a.n_bounds <= 512;
+  uint32_t rep8[8], rep32[32];
+  if (a.bounds && tid < 64) {
+    if (few_reports) load_reports<8>(a, qi, rep8);
+    else load_reports<32>(a, qi, rep32);
+  }
   const int n = a.q_len[qi];
   const int k = a.k;
   if (n <= k) {
     if (c == 0) emit_all<NT>(a, qi, n);
+    drain_loads();
     return;
   }
-  const float *row = a.scores + (int64_t)qi * a.ld;
-  const int c0 = c * a.chunk;
   const int c1 = min(c0 + a.chunk, n);
-  float v[kPassRounds];
-  load_pass<NT, kPassRounds>(row, c0, c1, v);   // in flight while the bound is read
-  const uint32_t t_lo = n > kRegCap ? row_bound(a, qi, n, L) : 0u;
+  uint32_t t_lo = 0u;
+  if (n > kRegCap)
+    t_lo = a.bounds ? (few_reports ? row_bound_from<8>(a, n, rep8, L) : row_bound_from<32>(a, n, rep32, L))
+                    : row_bound(a, qi, n, L);
   if (c == 0 && tid == 0) a.tlo[qi] = t_lo;
   uint32_t key[kPassRounds];
   uint32_t mx = 0;
@@ -547,27 +649,42 @@ __global__ __launch_bounds__(kFinishThreads) void select_finish_kernel(SelectArg
   constexpr int R = kRegCap / NT;
   extern __shared__ __align__(16) uint32_t lds[];
   const Lds L = carve(lds);
-  const int qi = blockIdx.y;
+  const int zero = args_together(a);
+  const int qi = blockIdx.y + zero;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int n = a.q_len[qi];
-  if (n <= a.k) return;   // the filter kernel emitted the row
   const float *row = a.scores + (int64_t)qi * a.ld;
   const int chunks = a.chunks;
+  // the row length, the row's bound and the chunk counts and maxima are all in
+  // flight together (every row has its regions; rows the filter emitted whole
+  // are not finished, so what they hold does not matter)
+  const int n = a.q_len[qi];
+  const uint32_t tlo_v = a.tlo[qi];
+  constexpr int PL = kMaxChunks / 64;   // 4: one 16-byte load of each array per lane
+  static_assert(PL == 4, "chunk counts are loaded as one uint4 per lane");
+  uint4 c4 = make_uint4(0u, 0u, 0u, 0u), m4 = make_uint4(0u, 0u, 0u, 0u);
+  if (wave == 0 && (chunks & 3) == 0) {
+    // both loads of a lane in flight together (the counts and maxima of the
+    // chunk regions are 16-byte aligned when chunks is a multiple of 4)
+    const int cl = min(lane * PL, chunks - PL);
+    c4 = *reinterpret_cast<const uint4 *>(a.ccount + (int64_t)qi * chunks + cl);
+    m4 = *reinterpret_cast<const uint4 *>(a.cmax + (int64_t)qi * chunks + cl);
+  }
+  if (n <= a.k) {   // the filter kernel emitted the row
+    drain_loads();
+    return;
+  }
 
   // the first wavefront: chunk counts -> exclusive prefix cpre[0..chunks],
   // cmap[b] = chunk of candidate 64 b, and the largest candidate key
   if (wave == 0) {
-    constexpr int PL = kMaxChunks / 64;   // 4: one 16-byte load of each array per lane
-    static_assert(PL == 4, "chunk counts are loaded as one uint4 per lane");
     uint32_t cc[PL];
     uint32_t s = 0, m = 0;
     if ((chunks & 3) == 0) {
       // both loads of a lane in flight together (the counts and maxima of the
       // chunk regions are 16-byte aligned when chunks is a multiple of 4)
-      uint4 c4 = make_uint4(0u, 0u, 0u, 0u), m4 = make_uint4(0u, 0u, 0u, 0u);
-      if (lane * PL < chunks) {
-        c4 = *reinterpret_cast<const uint4 *>(a.ccount + (int64_t)qi * chunks + lane * PL);
-        m4 = *reinterpret_cast<const uint4 *>(a.cmax + (int64_t)qi * chunks + lane * PL);
+      if (lane * PL >= chunks) {   // lanes past the last chunk loaded a clamped copy: they count nothing
+        c4 = make_uint4(0u, 0u, 0u, 0u);
+        m4 = make_uint4(0u, 0u, 0u, 0u);
       }
       cc[0] = c4.x;
       cc[1] = c4.y;
@@ -603,7 +720,7 @@ __global__ __launch_bounds__(kFinishThreads) void select_finish_kernel(SelectArg
       L.cpre[chunks] = incl;
       if (fits) L.cmap[(incl + 63u) >> 6] = (uint32_t)(chunks - 1);
       L.shv[1] = incl;
-      L.shv[2] = a.tlo[qi];
+      L.shv[2] = tlo_v;
       L.shv[3] = m;
     }
   }
@@ -810,6 +927,7 @@ hipError_t launch_topk(int32_t *indices, int32_t *counts, const float *scores, i
   a.n_bounds = n_bounds;
   a.group_tokens = group_tokens > 0 ? group_tokens : 1;
   a.bound_most = 32;
+  a.max_len = plan.max_len;
   if (plan.chunks > 1) {
     a.tlo = reinterpret_cast<uint32_t *>(ws + plan.off_tlo);
     a.ccount = reinterpret_cast<uint32_t *>(ws + plan.off_count);

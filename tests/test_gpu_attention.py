@@ -30,6 +30,10 @@ def _indices(p, k, rng, fill=0.7, pad=True):
 CASES = {
     "bf16_h64": (S(inputs.DECODE_8K, name="a1", wid=301, batch=3, seq_len=(500, 4000)), 2048),
     "bf16_paged_h16": (S(inputs.PAGED_DECODE, name="a2", wid=302, batch=2, seq_len=(2000, 3000), mla_heads=16), 2048),
+    # 48 heads do not pair into 32-head workgroups: the 16-head kernel (two teams over two row halves)
+    "bf16_h48": (S(inputs.DECODE_8K, name="a19", wid=319, batch=3, seq_len=(700, 5000), mla_heads=48), 2048),
+    "fp8lat_h48_k300": (S(inputs.DECODE_128K_FP8_LAT8, name="a20", wid=320, batch=2, seq_len=(200, 3000),
+                          mla_heads=48, tie_fraction=0.0), 300),
     "bf16_h128_k17": (S(inputs.DECODE_8K, name="a3", wid=303, batch=2, seq_len=(40, 300), mla_heads=128), 17),
     "bf16_peaky_q": (S(inputs.DECODE_8K, name="a4", wid=304, batch=2, seq_len=(3000, 3000), q_mla_sigma=20.0), 2048),
     "bf16_one_query_many_splits": (S(inputs.DECODE_8K, name="a5", wid=305, batch=1, seq_len=(8192, 8192)), 2048),
