@@ -499,28 +499,47 @@ __device__ uint32_t row_bound(const SelectArgs &a, int qi, int n, const Lds &L) 
   return L.shv[6];
 }
 
-// One workgroup per row: filter into LDS, then finish.
+// One workgroup per row.  Each wavefront filters a contiguous slice of the
+// row into a region of LDS of its own, in token order, so the stream of
+// scores needs no workgroup barrier and every wavefront keeps two batches of
+// loads in flight; the regions taken in wavefront order hold the candidates
+// in token order.  Then the exact finish on the candidates.
+constexpr int kLocalWaves = kLocalThreads / 64;
+constexpr int kWaveCap = kLocalCap / kLocalWaves;   // candidates per wavefront region (896)
+constexpr int kWaveRounds = 16;                      // 64-token rounds per load batch (4 KB per wavefront)
+static_assert(kWaveCap % 64 == 0, "a row of at most kLocalCap tokens fits the regions without a bound");
+
 __global__ __launch_bounds__(kLocalThreads) void select_local_kernel(SelectArgs a) {
-  constexpr int NT = kLocalThreads;
+  constexpr int NT = kLocalThreads, W = kLocalWaves, RW = kWaveRounds;
   extern __shared__ __align__(16) uint32_t lds[];
   const Lds L = carve(lds);
   const int zero = args_together(a);
   const int qi = blockIdx.y + zero;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const float *row = a.scores + (int64_t)qi * a.ld;
-  float v[kPassRounds];
-  load_pass_clamped<NT, kPassRounds>(row, 0, a.max_len, v);   // in flight while the length and bound arrive
   const int n = a.q_len[qi];
   const int k = a.k;
   if (n <= k) {
     emit_all<NT>(a, qi, n);
-    drain_loads();
     return;
   }
-  const uint32_t cap = (uint32_t)a.local_cap;
+
+  // this wavefront's slice [t0, t1) (64-token multiples; t1 >= 1 since n > k >= 1),
+  // read in batches of RW rounds; loads past the slice read its last score
+  const int span = ((n + W - 1) / W + 63) / 64 * 64;
+  const int t0 = min(wave * span, n), t1 = min(t0 + span, n);
+  const int last = t1 - 1;
+  const int pairs = (t1 - t0 + 2 * 64 * RW - 1) / (2 * 64 * RW);
+  auto load_batch = [&](int b, float (&v)[RW]) {
+#pragma unroll
+    for (int i = 0; i < RW; ++i) v[i] = row[min(t0 + 64 * (RW * b + i) + lane, last)];
+  };
+  float va[RW], vb[RW];
+  load_batch(0, va);   // in flight while the bound is found
 
   uint32_t t_lo = 0;
-  if ((uint32_t)n > cap) {
+  if (n > a.local_cap) {
     if (a.bounds) {
       t_lo = row_bound(a, qi, n, L);
     } else {
@@ -535,49 +554,69 @@ __global__ __launch_bounds__(kLocalThreads) void select_local_kernel(SelectArgs 
     }
   }
 
-  // The keys of a pass are formed at the end of the previous one, so the next
-  // pass's loads stay in flight across this pass's prefix and barrier.
-  uint32_t key[kPassRounds];
+  uint2 *region = L.cand + wave * kWaveCap;
+  uint32_t cnt = 0, mx = 0;   // candidates of this wavefront (uniform); largest key seen by this lane
+  auto filter_batch = [&](int b, const float (&v)[RW]) {
 #pragma unroll
-  for (int i = 0; i < kPassRounds; ++i) key[i] = order_key(v[i]);
-  uint32_t found = 0, mx = 0;
-  int parity = 0;
-  for (int g0 = 0; g0 < n; g0 += kPass, parity ^= 1) {
-    float nv[kPassRounds];
-    const bool more = g0 + kPass < n;
-    if (more) load_pass<NT, kPassRounds>(row, g0 + kPass, n, nv);
-    uint32_t pre[kPassRounds];
-    const uint32_t tot = ordered_prefix<NT, kPassRounds>(
-        [&](int i) -> uint32_t { return (g0 + tid + NT * i < n && key[i] >= t_lo) ? 1u : 0u; }, kPassRounds, pre,
-        parity ? L.tot1 : L.tot0);
-#pragma unroll
-    for (int i = 0; i < kPassRounds; ++i) {
-      const int t = g0 + tid + NT * i;
-      const uint32_t p = found + pre[i];
-      if (t < n && key[i] >= t_lo && p < cap) L.cand[p] = make_uint2(key[i], (uint32_t)t);
-      mx = max(mx, t < n ? key[i] : 0u);
+    for (int i = 0; i < RW; ++i) {
+      const int t = t0 + 64 * (RW * b + i) + lane;
+      const uint32_t key = order_key(v[i]);
+      const bool live = t < t1;
+      const bool in = live && key >= t_lo;
+      const uint64_t m = __ballot(in);
+      const uint32_t pos = cnt + lanes_below(m);
+      if (in && pos < (uint32_t)kWaveCap) region[pos] = make_uint2(key, (uint32_t)t);
+      cnt += (uint32_t)__popcll(m);
+      mx = max(mx, live ? key : 0u);
     }
-    found += tot;
-    if (more) {
-#pragma unroll
-      for (int i = 0; i < kPassRounds; ++i) key[i] = order_key(nv[i]);
-    }
+  };
+  // two batches per iteration in alternating buffers: while one is filtered the
+  // other is in flight (the batch after the slice's last is loaded and dropped)
+  for (int p = 0; p < pairs; ++p) {
+    load_batch(2 * p + 1, vb);
+    filter_batch(2 * p, va);
+    load_batch(2 * p + 2, va);
+    filter_batch(2 * p + 1, vb);
   }
-  mx = block_max<NT>(mx, L.scratch);   // (its barriers also publish L.cand)
-  if (found < (uint32_t)k || found > cap) {
+  drain_loads();
+  mx = wave_max_u32(mx);
+  if (lane == 0) {
+    L.scratch[wave] = cnt;
+    L.scratch[W + wave] = mx;
+  }
+  __syncthreads();   // (also publishes the regions)
+  uint32_t off[W + 1];
+  off[0] = 0;
+  bool overflow = false;
+  mx = 0;
+#pragma unroll
+  for (int w = 0; w < W; ++w) {
+    const uint32_t c = L.scratch[w];
+    overflow |= c > (uint32_t)kWaveCap;
+    off[w + 1] = off[w] + c;
+    mx = max(mx, L.scratch[W + w]);
+  }
+  const uint32_t C = off[W];
+  if (overflow || C < (uint32_t)k) {
+    __syncthreads();   // every thread has read the counts before finish_row reuses the scratch words
     finish_row<NT>(a, qi, n, row, L);
     return;
   }
+  // candidate j (token order) is entry j - off[w] of region w, off[w] <= j < off[w + 1]
   constexpr int R = kRegCap / NT;
+  static_assert(kLocalCap <= kRegCap, "every candidate of the regions fits the registers");
   uint32_t ck[R], ct[R];
 #pragma unroll
   for (int m = 0; m < R; ++m) {
     const uint32_t j = tid + NT * m;
-    const uint2 c = j < found ? L.cand[j] : make_uint2(0u, 0u);
+    uint32_t at = j;   // LDS entry: the last region whose offset is <= j (empty regions are skipped over)
+#pragma unroll
+    for (int i = 1; i < W; ++i) at = j >= off[i] ? (uint32_t)(i * kWaveCap) + (j - off[i]) : at;
+    const uint2 c = j < C ? L.cand[at] : make_uint2(0u, 0u);
     ck[m] = c.x;
     ct[m] = c.y;
   }
-  finish_regs<NT, R>(a, qi, found, t_lo, mx, ck, ct, L);
+  finish_regs<NT, R>(a, qi, C, t_lo, mx, ck, ct, L);
 }
 
 // Few long rows, step 2: workgroup (chunk c, row) filters its chunk and writes
