@@ -525,15 +525,19 @@ __global__ __launch_bounds__(kLocalThreads) void select_local_kernel(SelectArgs 
     return;
   }
 
-  // this wavefront's slice [t0, t1) (64-token multiples; t1 >= 1 since n > k >= 1),
-  // read in batches of RW rounds; loads past the slice read its last score
+  // this wavefront's slice [t0, t1) (64-token multiples), read in batches of RW
+  // rounds through a buffer resource over the row's n scores: loads past the
+  // row read 0 and are dropped (tokens past t1 are not live)
   const int span = ((n + W - 1) / W + 63) / 64 * 64;
   const int t0 = min(wave * span, n), t1 = min(t0 + span, n);
-  const int last = t1 - 1;
   const int pairs = (t1 - t0 + 2 * 64 * RW - 1) / (2 * 64 * RW);
+  const __amdgpu_buffer_rsrc_t rrow =
+      __builtin_amdgcn_make_buffer_rsrc(const_cast<float *>(row), (short)0, n * 4, 0x00020000);
   auto load_batch = [&](int b, float (&v)[RW]) {
+    const uint32_t off = (uint32_t)(t0 + 64 * RW * b + lane) * 4u;
 #pragma unroll
-    for (int i = 0; i < RW; ++i) v[i] = row[min(t0 + 64 * (RW * b + i) + lane, last)];
+    for (int i = 0; i < RW; ++i)
+      v[i] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rrow, off + 256u * i, 0, 0));
   };
   float va[RW], vb[RW];
   load_batch(0, va);   // in flight while the bound is found
@@ -553,21 +557,27 @@ __global__ __launch_bounds__(kLocalThreads) void select_local_kernel(SelectArgs 
       t_lo = L.shv[4];
     }
   }
+  // order_key(x) >= t_lo as one float comparison x >= f_lo (exact: fp32
+  // denormals are not flushed): t_lo 0 takes every score, NaN included; a
+  // bound at or below the key of -inf every score but NaN; a negative bound
+  // the float whose key it is; a positive one likewise (above the key of +inf
+  // that float is a NaN and nothing passes, as no key lies above it)
+  const bool take_all = t_lo == 0u;
+  const float f_lo = t_lo >= 0x80000000u ? __uint_as_float(t_lo & 0x7FFFFFFFu)
+                     : t_lo > 0x007FFFFFu ? __uint_as_float(~t_lo)
+                                         : -INFINITY;
 
   uint2 *region = L.cand + wave * kWaveCap;
-  uint32_t cnt = 0, mx = 0;   // candidates of this wavefront (uniform); largest key seen by this lane
+  uint32_t cnt = 0;   // candidates of this wavefront (uniform)
   auto filter_batch = [&](int b, const float (&v)[RW]) {
 #pragma unroll
     for (int i = 0; i < RW; ++i) {
       const int t = t0 + 64 * (RW * b + i) + lane;
-      const uint32_t key = order_key(v[i]);
-      const bool live = t < t1;
-      const bool in = live && key >= t_lo;
+      const bool in = (t < t1) & ((v[i] >= f_lo) | take_all);   // (no short circuit: lane masks only)
       const uint64_t m = __ballot(in);
       const uint32_t pos = cnt + lanes_below(m);
-      if (in && pos < (uint32_t)kWaveCap) region[pos] = make_uint2(key, (uint32_t)t);
+      if (in && pos < (uint32_t)kWaveCap) region[pos] = make_uint2(__float_as_uint(v[i]), (uint32_t)t);
       cnt += (uint32_t)__popcll(m);
-      mx = max(mx, live ? key : 0u);
     }
   };
   // two batches per iteration in alternating buffers: while one is filtered the
@@ -579,22 +589,16 @@ __global__ __launch_bounds__(kLocalThreads) void select_local_kernel(SelectArgs 
     filter_batch(2 * p + 1, vb);
   }
   drain_loads();
-  mx = wave_max_u32(mx);
-  if (lane == 0) {
-    L.scratch[wave] = cnt;
-    L.scratch[W + wave] = mx;
-  }
+  if (lane == 0) L.scratch[wave] = cnt;
   __syncthreads();   // (also publishes the regions)
   uint32_t off[W + 1];
   off[0] = 0;
   bool overflow = false;
-  mx = 0;
 #pragma unroll
   for (int w = 0; w < W; ++w) {
     const uint32_t c = L.scratch[w];
     overflow |= c > (uint32_t)kWaveCap;
     off[w + 1] = off[w] + c;
-    mx = max(mx, L.scratch[W + w]);
   }
   const uint32_t C = off[W];
   if (overflow || C < (uint32_t)k) {
@@ -602,10 +606,12 @@ __global__ __launch_bounds__(kLocalThreads) void select_local_kernel(SelectArgs 
     finish_row<NT>(a, qi, n, row, L);
     return;
   }
-  // candidate j (token order) is entry j - off[w] of region w, off[w] <= j < off[w + 1]
+  // candidate j (token order) is entry j - off[w] of region w, off[w] <= j < off[w + 1];
+  // its key is formed here, once per candidate
   constexpr int R = kRegCap / NT;
   static_assert(kLocalCap <= kRegCap, "every candidate of the regions fits the registers");
   uint32_t ck[R], ct[R];
+  uint32_t mx = 0;
 #pragma unroll
   for (int m = 0; m < R; ++m) {
     const uint32_t j = tid + NT * m;
@@ -613,9 +619,11 @@ __global__ __launch_bounds__(kLocalThreads) void select_local_kernel(SelectArgs 
 #pragma unroll
     for (int i = 1; i < W; ++i) at = j >= off[i] ? (uint32_t)(i * kWaveCap) + (j - off[i]) : at;
     const uint2 c = j < C ? L.cand[at] : make_uint2(0u, 0u);
-    ck[m] = c.x;
+    ck[m] = j < C ? order_key(__uint_as_float(c.x)) : 0u;
     ct[m] = c.y;
+    mx = max(mx, ck[m]);
   }
+  mx = block_max<NT>(mx, L.scratch + 16);   // (words apart from the counts read above)
   finish_regs<NT, R>(a, qi, C, t_lo, mx, ck, ct, L);
 }
 

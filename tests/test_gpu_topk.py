@@ -105,6 +105,32 @@ def test_many_rows_one_workgroup_each():
     _run(s, lens, 2048)
 
 
+@pytest.mark.parametrize("kind", ["positive", "negative", "denormal"])
+def test_many_long_rows_special_values_with_a_bound(kind):
+    # 130 rows (one workgroup each) longer than the LDS candidate budget, so
+    # each row is filtered against a sampled bound: positive (normal scores),
+    # negative (every score below -1) or among zeros and denormals, with NaN,
+    # -NaN, +-inf, +-0, +-denormals and +-3.4e38 mixed in.
+    rng = np.random.default_rng({"positive": 31, "negative": 32, "denormal": 33}[kind])
+    rows, n = 130, 12000
+    if kind == "positive":
+        s = rng.standard_normal((rows, n))
+    elif kind == "negative":
+        s = -1.0 - np.abs(rng.standard_normal((rows, n)))
+    else:
+        tiny = np.array([0.0, -0.0, 1e-45, -1e-45, 1e-40, -1e-40, 2e-40, -2e-40, 5e-39, 1e-38], np.float64)
+        s = tiny[rng.integers(0, len(tiny), size=(rows, n))]
+    s = s.astype(np.float32)
+    special = np.array([np.nan, -np.nan, np.inf, -np.inf, 0.0, -0.0, 1e-40, -1e-40, 3.4e38, -3.4e38], np.float32)
+    hit = rng.random((rows, n)) < 0.03
+    s[hit] = special[rng.integers(0, len(special), size=int(hit.sum()))]
+    lens = rng.integers(7200, n + 1, size=rows)
+    lens[:3] = n
+    print(f"case: {rows} x {n}, {kind} bound with special values", flush=True)
+    _run(s, lens, 2048)
+    _run(s, lens, 2048, order="score")
+
+
 def test_workspace_is_reusable():
     rng = np.random.default_rng(7)
     a = rng.standard_normal((4, 60000)).astype(np.float32)
