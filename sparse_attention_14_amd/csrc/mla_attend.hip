@@ -39,6 +39,11 @@ constexpr int kW = 576, kL = 512, kTile = 64, kHG = 16;
 constexpr int kRowBytes = kW * 2 + 16;          // padded LDS row
 constexpr int kChunks = kW * 2 / 16;            // 16-byte chunks per row (72)
 constexpr int kMaxSplits = 32;
+// Lazy softmax maximum: a head's reference maximum moves only when a step's
+// maximum exceeds it by more than 2^kSlack (in the exp2 domain) or it is still
+// -inf, so the weights stay <= 2^kSlack and the running output is rescaled only
+// in the rare steps where some reference moved (alpha is exactly 1 otherwise).
+constexpr float kSlack = 8.0f;
 constexpr int kAttTargetWGs = 256;   // workgroups aimed at by the split count
 constexpr int kWideMinRows = 16;     // (query, 64-head block) pairs from which the 64-head kernel is used
 
@@ -86,6 +91,25 @@ __device__ __forceinline__ float row16_sum(float x) {
   x += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x122, 0xF, 0xF, false));
   x += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x121, 0xF, 0xF, false));
   return x;
+}
+
+// 2^x as the hardware instruction (v_exp_f32, about 1 ulp): the softmax
+// weights and rescale factors have x <= 8, and results below 2^-126 of the
+// running maximum are negligible next to it however they are rounded.
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// Two weights split into bf16 hi + lo parts (hi = rne(x), lo = rne(x - hi)),
+// packed two per word (first weight in the low half), by the packed
+// round-to-nearest-even conversion.
+typedef __bf16 bf16x2v __attribute__((ext_vector_type(2)));
+typedef float f32x2v __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ uint32_t bf16x2_rne(float a, float b) {
+  const f32x2v v = {a, b};
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2v));
+}
+__device__ __forceinline__ void split_hi_lo(float a, float b, uint32_t &hi, uint32_t &lo) {
+  hi = bf16x2_rne(a, b);
+  lo = bf16x2_rne(a - __uint_as_float(hi << 16), b - __uint_as_float(hi & 0xFFFF0000u));
 }
 
 // Transposed LDS read (ds_read_b64_tr_b16): in each 16-lane group, lane p
@@ -190,11 +214,11 @@ __global__ __launch_bounds__(kAttThreads) void attend_bf16_kernel(AttArgs a) {
           w[r][i] = load16(src[r] + (F8 ? min(16 * gq8 + 128 * i, kW - 16) : 16 * gq8 + 128 * i));
         sc[r] = F8 && ok[r] ? a.latent.scale[sblk[r] * a.latent.scale_block_stride + sslot[r]] : 0.0f;
       }
+      if (__ballot(!(ok[0] && ok[1])))   // (only a split's last step has empty slots)
 #pragma unroll
-      for (int r = 0; r < kTeams; ++r)
-        if (!ok[r])
+        for (int r = 0; r < kTeams; ++r)
 #pragma unroll
-          for (int i = 0; i < NV8; ++i) w[r][i] = u32x4{0, 0, 0, 0};
+          for (int i = 0; i < NV8; ++i) w[r][i] = ok[r] ? w[r][i] : u32x4{0, 0, 0, 0};
       if (step == 0) {
 #pragma unroll
         for (int ks = 0; ks < kW / 32; ++ks) qa[ks] = as_bf16x8(load16(qr + 32 * ks));
@@ -249,22 +273,32 @@ __global__ __launch_bounds__(kAttThreads) void attend_bf16_kernel(AttArgs a) {
       for (int i = 0; i < 4; ++i) red[team][0][tw][4 * g4 + i] = mx[i];
     __syncthreads();
 
-    float m_new[4], alpha[4], ps[4];
+    // lazy reference maximum, as in the 64-head kernel below
+    float m_new[4], alpha[4], ps[4], pv[4];
+    bool moved = false;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int h = 4 * g4 + i;
       const float tm =
           fmaxf(fmaxf(red[team][0][0][h], red[team][0][1][h]), fmaxf(red[team][0][2][h], red[team][0][3][h]));
-      m_new[i] = fmaxf(m_run[i], tm);
+      const bool grow = tm > m_run[i] + kSlack;
+      moved |= grow;
+      m_new[i] = grow ? tm : m_run[i];
       const float mu = m_new[i] == -INFINITY ? 0.0f : m_new[i];
-      alpha[i] = exp2f(m_run[i] - mu);
-      const float p = exp2f(z[i] - mu);
-      const float pv = F8 ? p * rs : p;       // weight of the decoded (unscaled) row
-      const uint16_t hi = float_to_bf16_bits(pv);
-      const uint16_t lo = float_to_bf16_bits(pv - bf16_bits_to_float(hi));
-      my_p[h * kTile + row] = hi;
-      my_p[kHG * kTile + h * kTile + row] = lo;
+      alpha[i] = grow ? fast_exp2(m_run[i] - mu) : 1.0f;
+      const float p = fast_exp2(z[i] - mu);
+      pv[i] = F8 ? p * rs : p;                // weight of the decoded (unscaled) row
       ps[i] = row16_sum(p);
+    }
+#pragma unroll
+    for (int i = 0; i < 4; i += 2) {
+      const int h = 4 * g4 + i;
+      uint32_t hi, lo;
+      split_hi_lo(pv[i], pv[i + 1], hi, lo);
+      my_p[h * kTile + row] = (uint16_t)hi;
+      my_p[(h + 1) * kTile + row] = (uint16_t)(hi >> 16);
+      my_p[kHG * kTile + h * kTile + row] = (uint16_t)lo;
+      my_p[kHG * kTile + (h + 1) * kTile + row] = (uint16_t)(lo >> 16);
     }
     if (l16 == 0)
 #pragma unroll
@@ -277,10 +311,11 @@ __global__ __launch_bounds__(kAttThreads) void attend_bf16_kernel(AttArgs a) {
       l_run[i] = l_run[i] * alpha[i] + tsum;
       m_run[i] = m_new[i];
     }
+    if (step > 0 && __ballot(moved))   // (before the first step o is 0)
 #pragma unroll
-    for (int nt = 0; nt < 8; ++nt)
+      for (int nt = 0; nt < 8; ++nt)
 #pragma unroll
-      for (int i = 0; i < 4; ++i) o[nt][i] *= alpha[i];
+        for (int i = 0; i < 4; ++i) o[nt][i] *= alpha[i];
 
     // PV: rows 32*ks2 + 8*g4 + e, columns 128*tw + 16*nt + l16; the V operand
     // comes from two transposed LDS reads of 4 rows each
@@ -327,7 +362,7 @@ __global__ __launch_bounds__(kAttThreads) void attend_bf16_kernel(AttArgs a) {
     const float m1 = xml[2 * h], l1 = xml[2 * h + 1];
     const float m = fmaxf(m_run[i], m1);
     const float mu = m == -INFINITY ? 0.0f : m;
-    const float a0 = exp2f(m_run[i] - mu), a1 = exp2f(m1 - mu);
+    const float a0 = fast_exp2(m_run[i] - mu), a1 = fast_exp2(m1 - mu);
     l_run[i] = a0 * l_run[i] + a1 * l1;
     m_run[i] = m;
 #pragma unroll
@@ -458,8 +493,11 @@ __global__ __launch_bounds__(kWideThreads) void attend_wide_kernel(AttArgs a) {
         if (gq == 0) lscale[gr] = v_sc;
       } else {
         uint8_t *dst = rows + gr * kRowBytes + 16 * gq;
+        if (__ballot(!v_ok))   // (only a split's last step has empty slots)
 #pragma unroll
-        for (int i = 0; i < NV; ++i) *reinterpret_cast<u32x4 *>(dst + 128 * i) = v_ok ? v[i] : u32x4{0, 0, 0, 0};
+          for (int i = 0; i < NV; ++i) v[i] = v_ok ? v[i] : u32x4{0, 0, 0, 0};
+#pragma unroll
+        for (int i = 0; i < NV; ++i) *reinterpret_cast<u32x4 *>(dst + 128 * i) = v[i];
       }
       if (gq == 0) lvalid[gr] = v_ok ? 1 : 0;
     }
@@ -490,27 +528,33 @@ __global__ __launch_bounds__(kWideThreads) void attend_wide_kernel(AttArgs a) {
       for (int i = 0; i < 4; ++i) red[hg][0][wr][4 * g4 + i] = mx[i];
     __syncthreads();
 
+    // lazy reference maximum (kSlack)
     float alpha[4], ps[4];
+    bool moved = false;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int h = 4 * g4 + i;
       const float tm = fmaxf(red[hg][0][0][h], red[hg][0][1][h]);
-      const float m_new = fmaxf(m_run[i], tm);
+      const bool grow = tm > m_run[i] + kSlack;
+      moved |= grow;
+      const float m_new = grow ? tm : m_run[i];
       const float mu = m_new == -INFINITY ? 0.0f : m_new;
-      alpha[i] = exp2f(m_run[i] - mu);
-      float pr[2];
+      alpha[i] = grow ? fast_exp2(m_run[i] - mu) : 1.0f;
+      float pr[2], pv[2];
 #pragma unroll
       for (int nt = 0; nt < 2; ++nt) {
         const int row = 32 * wr + 16 * nt + l16;
-        const float p = exp2f(z[nt][i] - mu);
-        const float pv = F8 ? p * lscale[row] : p;   // weight of the decoded (unscaled) row
-        const uint16_t hi = float_to_bf16_bits(pv);
-        const uint16_t lo = float_to_bf16_bits(pv - bf16_bits_to_float(hi));
-        my_p[h * kWideStep + row] = hi;
-        my_p[kHG * kWideStep + h * kWideStep + row] = lo;
-        pr[nt] = p;
+        pr[nt] = fast_exp2(z[nt][i] - mu);
+        pv[nt] = F8 ? pr[nt] * lscale[row] : pr[nt];   // weight of the decoded (unscaled) row
       }
-      ps[i] = row16_sum(pr[0]) + row16_sum(pr[1]);
+      uint32_t hi, lo;
+      split_hi_lo(pv[0], pv[1], hi, lo);
+      const int r0 = 32 * wr + l16;   // rows r0 and r0 + 16
+      my_p[h * kWideStep + r0] = (uint16_t)hi;
+      my_p[h * kWideStep + r0 + 16] = (uint16_t)(hi >> 16);
+      my_p[kHG * kWideStep + h * kWideStep + r0] = (uint16_t)lo;
+      my_p[kHG * kWideStep + h * kWideStep + r0 + 16] = (uint16_t)(lo >> 16);
+      ps[i] = row16_sum(pr[0] + pr[1]);
       m_run[i] = m_new;
     }
     if (l16 == 0)
@@ -522,10 +566,11 @@ __global__ __launch_bounds__(kWideThreads) void attend_wide_kernel(AttArgs a) {
       const int h = 4 * g4 + i;
       l_run[i] = l_run[i] * alpha[i] + (red[hg][1][0][h] + red[hg][1][1][h]);
     }
+    if (step > 0 && __ballot(moved))   // (before the first step o is 0)
 #pragma unroll
-    for (int nt = 0; nt < NT; ++nt)
+      for (int nt = 0; nt < NT; ++nt)
 #pragma unroll
-      for (int i = 0; i < 4; ++i) o[nt][i] *= alpha[i];
+        for (int i = 0; i < 4; ++i) o[nt][i] *= alpha[i];
 
     // PV: rows 32 ks2 + 8 g4 + e, columns 256 wr + 16 nt + l16; the V operand
     // comes from two transposed LDS reads of 4 rows each
