@@ -22,6 +22,8 @@
 // row gathers hit one L2.
 #include "kernels.hpp"
 
+#include <atomic>
+
 namespace dsa {
 namespace {
 
@@ -618,6 +620,249 @@ __global__ __launch_bounds__(kWideThreads) void attend_wide_kernel(AttArgs a) {
   }
 }
 
+// Many queries over bf16 rows (prefill chunks, decode windows): a workgroup of
+// four wavefronts owns one query, a block of 64 heads and a split of the index
+// slots, and wavefront w owns heads 16 w .. 16 w + 15 of the block for the
+// whole split, so its softmax needs no other wavefront.  Per 32-slot step the
+// kept rows are copied from memory straight into LDS (global_load_lds_dwordx4,
+// no registers), one step ahead into the other of two buffers; one barrier per
+// step and two workgroups per CU.  The 16-byte chunk c of row r sits at slot
+// c ^ g(r) of the row (g below), which keeps both operand reads free of bank
+// conflicts:
+//   QK^T : v_mfma_f32_16x16x32_bf16 with A = 16 rows (LDS) and B = q (16 heads,
+//          registers), so D leaves lane (head l16, g4) with rows 4 g4 + i of
+//          both 16-row halves: 8 rows of one head;
+//   softmax in the exp2 domain (lazy reference maximum): 8 rows in the lane,
+//          the 4 lanes of a head combined by two lane exchanges;
+//   PV   : A = P exactly as the lane holds it (K = its 8 rows, bf16 hi + lo),
+//          B = V read transposed from LDS in the same row order (two 4-row
+//          reads), 32 tiles of 16 columns.
+constexpr int kW4Step = 32;                               // rows per step
+constexpr int kW4Threads = 256;
+constexpr int kW4RowB = kW * 2;                           // 1152 bytes per row, no padding
+constexpr int kW4Chunks = kW4RowB / 16;                   // 72
+constexpr int kW4PerThread = kW4Step * kW4Chunks / kW4Threads;   // 9 chunk copies per thread and step
+constexpr int kW4BufB = kW4Step * kW4RowB;                // 36864
+constexpr size_t kW4LdsBytes = 2 * (size_t)kW4BufB;       // two buffers: 73728
+static_assert(kW4Step * kW4Chunks == kW4PerThread * kW4Threads, "whole chunk copies per thread");
+
+// Chunk swizzle of row r (bits 1 and 2 of r): rows 2 apart differ in bit 1 of
+// the slot and rows 4 apart in bit 0, so 8 consecutive rows at one chunk, and
+// 4 consecutive rows at two adjacent chunks, fall on distinct banks.
+__device__ __forceinline__ int w4_swz(int r) { return (r & 2) | ((r >> 2) & 1); }
+
+template <bool SPLIT>
+__global__ __launch_bounds__(kW4Threads, 2) void attend_w4_kernel(AttArgs a) {
+  extern __shared__ __align__(16) uint8_t w4lds[];
+  const int H = a.n_heads;
+  const int n_hb = H / kWideHeads;
+  const int wg = blockIdx.x + args_together(a);
+  const int qi = wg / (a.splits * n_hb);
+  const int rem = wg - qi * a.splits * n_hb;
+  const int hb = rem / a.splits, sp = rem - hb * a.splits;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int l16 = lane & 15, g4 = lane >> 4;
+  const int h0 = hb * kWideHeads + wave * kHG;
+  const int seq = attend_seq(a.q_seq, qi, a.seq_per);
+  const int j0 = sp * a.rows_per_split;
+  const int j1 = min(j0 + a.rows_per_split, a.k);
+  const int nsteps = (j1 - j0 + kW4Step - 1) / kW4Step;
+  const int32_t *idx_row = a.indices + (int64_t)qi * a.k;
+
+  // Step copies: this wavefront's 9 instructions write LDS bytes
+  // [1024 (9 wave + u), +1024) of a buffer; lane l's 16 bytes there are entry
+  // q = 64 (9 wave + u) + l = row q / 72, slot q % 72, i.e. chunk (q % 72) ^ g(row).
+  // (recomputed where used: hoisted out of the step loop they would not fit the registers)
+  auto fresh_lane = [&]() {
+    int l = lane;
+    asm volatile("" : "+v"(l));
+    return l;
+  };
+  auto copy_row = [&](int u, int l) { return (64 * (kW4PerThread * wave + u) + l) / kW4Chunks; };
+  auto copy_ofs = [&](int u, int l) {
+    const int q = 64 * (kW4PerThread * wave + u) + l;
+    return 16 * ((q % kW4Chunks) ^ w4_swz(q / kW4Chunks));
+  };
+  // Lanes 0..31 each hold the token of one row of a step; the rows' validity is
+  // a 32-bit mask (uniform).
+  auto step_token = [&](int st) {
+    const int j = j0 + st * kW4Step + lane;
+    return (lane < kW4Step && j < j1) ? idx_row[j] : -1;
+  };
+  auto issue_copies = [&](int tok, uint8_t *buf) {
+    int slot;
+    const int64_t blk = cache_block(a.latent, seq, tok >= 0 ? tok : 0, slot);
+    const uint8_t *rp = tok >= 0 ? cache_row(a.latent, blk, slot) : a.latent.rows;
+    const uint64_t rp64 = reinterpret_cast<uint64_t>(rp);
+    const int l = fresh_lane();
+#pragma unroll
+    for (int u = 0; u < kW4PerThread; ++u) {
+      const int r = copy_row(u, l);
+      const uint32_t lo = (uint32_t)__shfl((int)(uint32_t)rp64, r, 64);
+      const uint32_t hi = (uint32_t)__shfl((int)(uint32_t)(rp64 >> 32), r, 64);
+      const uint8_t *src = reinterpret_cast<const uint8_t *>(((uint64_t)hi << 32) | lo) + copy_ofs(u, l);
+      __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void *)src,
+                                       (__attribute__((address_space(3))) void *)(buf + 1024 * (kW4PerThread * wave + u)),
+                                       16, 0, 0);
+    }
+  };
+  // After a wavefront's copies have landed: its entries of invalid rows become
+  // zeros (their weight is 0, but 0 times a non-finite value would not be).
+  auto clear_invalid = [&](uint32_t valid, uint8_t *buf) {
+    const int l = fresh_lane();
+#pragma unroll
+    for (int u = 0; u < kW4PerThread; ++u)
+      if (!((valid >> copy_row(u, l)) & 1u))
+        *reinterpret_cast<u32x4 *>(buf + 1024 * (kW4PerThread * wave + u) + 16 * lane) = u32x4{0, 0, 0, 0};
+  };
+
+  // first step's copies, then q (head h0 + l16, dims 8 g4 + 32 ks + [0, 8))
+  int tok = step_token(0);
+  uint32_t valid = (uint32_t)__ballot(tok >= 0);
+  if (nsteps > 0) issue_copies(tok, w4lds);
+  bf16x8 qa[kW / 32];
+  {
+    const uint16_t *qr = a.q + ((int64_t)qi * H + h0 + l16) * kW + 8 * g4;
+#pragma unroll
+    for (int ks = 0; ks < kW / 32; ++ks) qa[ks] = as_bf16x8(load16(qr + 32 * ks));
+  }
+  int tok_next = step_token(1);
+  __builtin_amdgcn_s_waitcnt(0);
+  if (valid != 0xFFFFFFFFu) clear_invalid(valid, w4lds);
+  __syncthreads();
+
+  float m_run = -INFINITY, l_run = 0.0f;   // head l16: reference maximum, this lane's partial sum
+  f32x4 o[kL / 16];                        // column tile nt: heads 4 g4 + i, column 16 nt + l16
+#pragma unroll
+  for (int nt = 0; nt < kL / 16; ++nt) o[nt] = f32x4{0, 0, 0, 0};
+
+  // per-lane LDS offsets: QK rows 16 t + l16 at chunk g4 + 4 ks; PV transposed
+  // reads of rows 4 g4 + l16 / 4 (+ 16) at columns 16 nt + 4 (l16 % 4), whose
+  // slot depends on nt's parity
+  const int qk_off = kW4RowB * l16 + 16 * (g4 ^ w4_swz(l16));
+  const int pr = 4 * g4 + (l16 >> 2);
+  int pv_off[2];
+#pragma unroll
+  for (int par = 0; par < 2; ++par)
+    pv_off[par] = kW4RowB * pr + 16 * ((2 * par + ((l16 & 3) >> 1)) ^ w4_swz(pr)) + 8 * (l16 & 1);
+
+  for (int st = 0; st < nsteps; ++st) {
+    uint8_t *cur = w4lds + (st & 1) * kW4BufB;
+    uint8_t *nxt = w4lds + ((st + 1) & 1) * kW4BufB;
+    // next step's copies into the other buffer (read by no one since the barrier)
+    const uint32_t valid_next = (uint32_t)__ballot(tok_next >= 0);
+    const bool more = st + 1 < nsteps;
+    if (more) issue_copies(tok_next, nxt);
+    const int tok_after = step_token(st + 2);
+
+    // QK^T: D[row 16 t + 4 g4 + i][head l16]
+    f32x4 acc[2];
+#pragma unroll
+    for (int t = 0; t < 2; ++t) {
+      const uint8_t *rp = cur + kW4RowB * 16 * t + qk_off;
+      acc[t] = f32x4{0, 0, 0, 0};
+#pragma unroll
+      for (int ks = 0; ks < kW / 32; ++ks)
+        acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(*reinterpret_cast<const u32x4 *>(rp + 64 * ks)),
+                                                         qa[ks], acc[t], 0, 0, 0);
+    }
+    float z[2][4];
+    float mx = -INFINITY;
+#pragma unroll
+    for (int t = 0; t < 2; ++t)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int r = 16 * t + 4 * g4 + i;
+        z[t][i] = ((valid >> r) & 1u) ? acc[t][i] * a.scale_log2 : -INFINITY;
+        mx = fmaxf(mx, z[t][i]);
+      }
+    mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
+    mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+    // lazy reference maximum (kSlack)
+    const bool grow = mx > m_run + kSlack;
+    const float m_new = grow ? mx : m_run;
+    const float mu = m_new == -INFINITY ? 0.0f : m_new;
+    const float alpha = grow ? fast_exp2(m_run - mu) : 1.0f;
+    m_run = m_new;
+    float p[2][4];
+    float ps = 0.0f;
+#pragma unroll
+    for (int t = 0; t < 2; ++t)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        p[t][i] = fast_exp2(z[t][i] - mu);
+        ps += p[t][i];
+      }
+    l_run = l_run * alpha + ps;
+    if (st > 0 && __ballot(grow)) {   // (before the first step o is 0)
+      // o's lane holds heads 4 g4 + i: their factors come from lanes 4 g4 + i
+      float ao[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) ao[i] = __shfl(alpha, 4 * g4 + i, 64);
+#pragma unroll
+      for (int nt = 0; nt < kL / 16; ++nt)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) o[nt][i] *= ao[i];
+    }
+    // P as the PV A operand: k = 8 g4 + e is row 4 g4 + e (e < 4) or 16 + 4 g4 + e - 4
+    uint32_t ph[4], pl[4];
+    split_hi_lo(p[0][0], p[0][1], ph[0], pl[0]);
+    split_hi_lo(p[0][2], p[0][3], ph[1], pl[1]);
+    split_hi_lo(p[1][0], p[1][1], ph[2], pl[2]);
+    split_hi_lo(p[1][2], p[1][3], ph[3], pl[3]);
+    const bf16x8 ahi = as_bf16x8(u32x4{ph[0], ph[1], ph[2], ph[3]});
+    const bf16x8 alo = as_bf16x8(u32x4{pl[0], pl[1], pl[2], pl[3]});
+
+    // PV: 32 column tiles
+#pragma unroll
+    for (int nt = 0; nt < kL / 16; ++nt) {
+      const uint8_t *vb = cur + pv_off[nt & 1] + 64 * (nt >> 1);
+      const i16x4 v0 = lds_read_tr(vb);
+      const i16x4 v1 = lds_read_tr(vb + 16 * kW4RowB);
+      const bf16x8 b = __builtin_bit_cast(
+          bf16x8, (__attribute__((__vector_size__(8 * sizeof(short)))) short){v0[0], v0[1], v0[2], v0[3], v1[0], v1[1],
+                                                                               v1[2], v1[3]});
+      o[nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ahi, b, o[nt], 0, 0, 0);
+      o[nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(alo, b, o[nt], 0, 0, 0);
+    }
+
+    // the next step's rows have landed (this wavefront's copies), invalid ones
+    // cleared, and every wavefront is done with this buffer before it is refilled
+    __builtin_amdgcn_s_waitcnt(0);
+    if (more && valid_next != 0xFFFFFFFFu) clear_invalid(valid_next, nxt);
+    valid = valid_next;
+    tok_next = tok_after;
+    __syncthreads();
+  }
+
+  // epilogue: the head's sum over its 4 lanes; o's lane holds heads 4 g4 + i
+  l_run += __shfl_xor(l_run, 16, 64);
+  l_run += __shfl_xor(l_run, 32, 64);
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int hl = 4 * g4 + i;
+    const float li = __shfl(l_run, hl, 64), mi = __shfl(m_run, hl, 64);
+    const int head = h0 + hl;
+    if (!SPLIT) {
+      const float inv = li > 0.0f ? 1.0f / li : 0.0f;
+      float *orow = a.out + ((int64_t)qi * H + head) * kL + l16;
+#pragma unroll
+      for (int nt = 0; nt < kL / 16; ++nt) orow[16 * nt] = o[nt][i] * inv;
+      if (l16 == 0 && a.lse) a.lse[(int64_t)qi * H + head] = li > 0.0f ? (mi + log2f(li)) * kLn2 : -INFINITY;
+    } else {
+      const int64_t base = ((int64_t)(qi * a.splits + sp) * H + head);
+      float *orow = a.part_o + base * kL + l16;
+#pragma unroll
+      for (int nt = 0; nt < kL / 16; ++nt) orow[16 * nt] = o[nt][i];
+      if (l16 == 0) {
+        a.part_ml[base * 2 + 0] = mi;
+        a.part_ml[base * 2 + 1] = li;
+      }
+    }
+  }
+}
+
 // Combine split partials in split order.  One workgroup per (query, head), one
 // thread per 4 output columns.  Every thread issues all of its loads at once
 // (the splits' (max, sum) pairs and its 4 columns of every split; padding
@@ -874,6 +1119,22 @@ hipError_t launch_attend(float *out, float *lse, const void *q, int dt, const Ca
   a.pairs = n_q * plan.splits;
   a.scale_log2 = scale * kLog2e;
   uint8_t *ws = static_cast<uint8_t *>(workspace);
+  if (plan.wide && dt != kFP8) {
+    // the 64-head bf16 kernel takes 72 KB of dynamic LDS: allowed once per device (the current one)
+    static std::atomic<uint64_t> lds_set{0};
+    int dev = 0;
+    hipError_t de = hipGetDevice(&dev);
+    if (de != hipSuccess) return de;
+    const uint64_t bit = dev < 64 ? uint64_t(1) << dev : 0;
+    if (!bit || !(lds_set.load(std::memory_order_acquire) & bit)) {
+      for (const void *f : {reinterpret_cast<const void *>(&attend_w4_kernel<true>),
+                            reinterpret_cast<const void *>(&attend_w4_kernel<false>)}) {
+        de = hipFuncSetAttribute(f, hipFuncAttributeMaxDynamicSharedMemorySize, (int)kW4LdsBytes);
+        if (de != hipSuccess) return de;
+      }
+      lds_set.fetch_or(bit, std::memory_order_acq_rel);
+    }
+  }
   const int groups = (a.pairs + 7) / 8;
   const dim3 grid(groups * 8 * a.n_hg);
   const dim3 wide_grid(n_q * (n_heads / kWideHeads) * plan.splits);
@@ -882,7 +1143,7 @@ hipError_t launch_attend(float *out, float *lse, const void *q, int dt, const Ca
   do {                                                                                                        \
     if (plan.wide) {                                                                                          \
       if (f8) hipLaunchKernelGGL((attend_wide_kernel<SP, true>), wide_grid, dim3(kWideThreads), 0, stream, a); \
-      else hipLaunchKernelGGL((attend_wide_kernel<SP, false>), wide_grid, dim3(kWideThreads), 0, stream, a);   \
+      else hipLaunchKernelGGL((attend_w4_kernel<SP>), wide_grid, dim3(kW4Threads), kW4LdsBytes, stream, a);    \
     } else {                                                                                                  \
       if (f8) hipLaunchKernelGGL((attend_bf16_kernel<SP, true>), grid, dim3(kAttThreads), 0, stream, a);       \
       else hipLaunchKernelGGL((attend_bf16_kernel<SP, false>), grid, dim3(kAttThreads), 0, stream, a);         \

@@ -99,3 +99,52 @@ def test_decode_at_position_matches_prefill_row(name):
     wp = check_attention(out.cpu().numpy()[rows], lse.cpu().numpy()[rows], ref_o, ref_l, TOL[p.latent.dtype])
     wd = check_attention(d_out.cpu().numpy(), d_lse.cpu().numpy(), ref_o, ref_l, TOL[p.latent.dtype])
     print(f"  {fmt_scores(r)}; attention worst relative error prefill {wp:.3g}, decode {wd:.3g}")
+
+
+def test_many_positions_decode_equals_prefill():
+    """520 positions at once: both sides take their top-k with the many-row
+    kernel (the prefill chunk with sampled bounds, the decode step with the
+    score kernel's bounds); every row's scores and kept indices must agree bit
+    for bit, the prefill top-k must equal the oracle's top-k of its scores on
+    every row, scores must match the oracle on sampled rows and attention on a
+    few."""
+    p = inputs.make_problem(S(inputs.PREFILL_64K, name="dp3", wid=622, seq_len=(9000, 9000), prefill_queries=520))
+    dp = device.upload(p)
+    n_q, k, H, L, max_len = p.n_q, p.topk, p.mla_heads, p.kv_lora, p.max_len
+    print(f"case dp3: {n_q} queries at positions {int(p.q_len[0]) - 1}..{int(p.q_len[-1]) - 1}", flush=True)
+    sc = torch.full((n_q, max_len), float("nan"), device="cuda")
+    dsa.dsa_index_scores(sc, dp.q_idx, p.q_idx_dtype, dp.w_idx, dp.keys, dp.q_len, p.idx_heads, max_len,
+                         q_seq=dp.q_seq)
+    ix = torch.full((n_q, k), -7, dtype=torch.int32, device="cuda")
+    tws = torch.zeros(max(dsa.dsa_topk_workspace_size(n_q, k, max_len), 1), dtype=torch.uint8, device="cuda")
+    dsa.dsa_topk(ix, None, sc, dp.q_len, k, max_len, workspace=tws)
+
+    keys_b = _paged_view(dp.keys, n_q, max_len)
+    lat_b = _paged_view(dp.latent, n_q, max_len)
+    d_out = torch.full((n_q, H, L), float("nan"), device="cuda")
+    d_lse = torch.full((n_q, H), float("nan"), device="cuda")
+    d_sc = torch.full((n_q, max_len), float("nan"), device="cuda")
+    d_ix = torch.full((n_q, k), -7, dtype=torch.int32, device="cuda")
+    ws = torch.zeros(dsa.dsa_decode_step_workspace_size(n_q, max_len, k, H, L), dtype=torch.uint8, device="cuda")
+    dsa.dsa_decode_step(d_out, d_lse, dp.q_idx, p.q_idx_dtype, dp.w_idx, keys_b, dp.q_mla, p.q_mla_dtype, lat_b, L,
+                        dp.q_len, max_len, k, p.softmax_scale, ws, scores_out=d_sc, indices_out=d_ix)
+    torch.cuda.synchronize()
+
+    g_sc, g_ix = sc.cpu().numpy(), ix.cpu().numpy()
+    h_sc, h_ix = d_sc.cpu().numpy(), d_ix.cpu().numpy()
+    for r in range(n_q):
+        n = int(p.q_len[r])
+        assert np.array_equal(h_sc[r, :n].view(np.uint32), g_sc[r, :n].view(np.uint32)), \
+            f"row {r}: decode scores differ from the prefill row"
+    assert np.array_equal(h_ix, g_ix), "decode kept indices differ from the prefill rows"
+    ref_idx, _ = oracle.topk(g_sc.astype(np.float64), p.q_len, k)
+    assert np.array_equal(g_ix, ref_idx)
+    rng = np.random.default_rng(6)
+    rows = np.unique(np.concatenate([[0, n_q - 1], rng.choice(n_q, 10, replace=False)]))
+    ref_s = oracle.index_scores(p.q_idx[rows], p.q_idx_dtype, p.w_idx[rows], p.keys, p.q_seq[rows], p.q_len[rows])
+    r = check_scores(p, g_sc[rows], ref_s, rows=rows)
+    few = rows[:4]
+    ref_o, ref_l, _ = oracle.mla_attend(p.q_mla[few], p.q_mla_dtype, p.latent, L, g_ix[few], p.q_seq[few],
+                                        p.softmax_scale)
+    wd = check_attention(d_out.cpu().numpy()[few], d_lse.cpu().numpy()[few], ref_o, ref_l, TOL[p.latent.dtype])
+    print(f"  {fmt_scores(r)}; decode attention worst relative error {wd:.3g}")

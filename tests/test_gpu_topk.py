@@ -131,6 +131,70 @@ def test_many_long_rows_special_values_with_a_bound(kind):
     _run(s, lens, 2048, order="score")
 
 
+# Many rows (at least 512): the persistent kernel, one workgroup per CU taking
+# several rows, each finished by one wavefront while the next one streams.
+
+def _mixed_rows(rng, rows, n, special_frac=0.03):
+    s = rng.standard_normal((rows, n)).astype(np.float32)
+    special = np.array([np.nan, -np.nan, np.inf, -np.inf, 0.0, -0.0, 1e-40, -1e-40, 3.4e38, -3.4e38], np.float32)
+    hit = rng.random((rows, n)) < special_frac
+    s[hit] = special[rng.integers(0, len(special), size=int(hit.sum()))]
+    return s
+
+
+def test_many_rows_mixed_lengths_and_special_values():
+    rng = np.random.default_rng(41)
+    rows, n = 600, 12000
+    s = _mixed_rows(rng, rows, n)
+    lens = rng.integers(7169, n + 1, size=rows)
+    # every kind of row somewhere in the schedule: empty, n <= k, no bound needed, bounded
+    special_lens = [0, 1, 2047, 2048, 2049, 5000, 7168, 7169, 9000, n]
+    for i, L in enumerate(special_lens):
+        lens[37 * i + 3] = L
+    lens[-1] = 0
+    print(f"case: {rows} x {n}, mixed lengths, special values", flush=True)
+    _run(s, lens, 2048)
+    _run(s, lens, 2048, order="score")
+    _run(s, lens, 17)
+
+
+def test_many_rows_several_rounds_per_workgroup():
+    # 1100 rows: each persistent workgroup takes 4-5 of them; every third row
+    # keeps all its tokens (n <= k), so finishing and emitting rows interleave
+    rng = np.random.default_rng(42)
+    rows, n = 1100, 9000
+    s = (rng.standard_normal((rows, n)) * 2).astype(np.float32)
+    lens = rng.integers(7169, n + 1, size=rows)
+    lens[::3] = rng.integers(0, 2049, size=len(lens[::3]))
+    print(f"case: {rows} x {n}, several rows per workgroup", flush=True)
+    _run(s, lens, 2048)
+
+
+def test_many_rows_heavy_ties_take_the_exact_fallback():
+    # six distinct values: the sampled bound keeps far more than a region holds,
+    # so those rows take the whole-workgroup exact path between streamed rows
+    rng = np.random.default_rng(43)
+    rows, n = 520, 10000
+    s = rng.integers(0, 6, size=(rows, n)).astype(np.float32)
+    s[1::2] = rng.standard_normal((rows // 2, n)).astype(np.float32)   # alternate with ordinary rows
+    lens = rng.integers(7169, n + 1, size=rows)
+    print(f"case: {rows} x {n}, heavy ties alternating with ordinary rows", flush=True)
+    _run(s, lens, 2048)
+    _run(s, lens, 2048, order="score")
+
+
+def test_many_rows_with_a_positional_trend():
+    # later tokens favoured: the last wavefront slices hold most candidates and
+    # may overflow their regions (exact fallback) while other rows do not
+    rng = np.random.default_rng(44)
+    rows, n = 520, 20000
+    trend = np.linspace(0.0, 3.0, n, dtype=np.float32)
+    s = (trend[None, :] * rng.random((rows, 1)).astype(np.float32) + rng.standard_normal((rows, n)).astype(np.float32))
+    lens = rng.integers(8000, n + 1, size=rows)
+    print(f"case: {rows} x {n}, positional trend", flush=True)
+    _run(s, lens, 2048)
+
+
 def test_workspace_is_reusable():
     rng = np.random.default_rng(7)
     a = rng.standard_normal((4, 60000)).astype(np.float32)
