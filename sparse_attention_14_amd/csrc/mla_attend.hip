@@ -646,10 +646,17 @@ constexpr int kW4BufB = kW4Step * kW4RowB;                // 36864
 constexpr size_t kW4LdsBytes = 2 * (size_t)kW4BufB;       // two buffers: 73728
 static_assert(kW4Step * kW4Chunks == kW4PerThread * kW4Threads, "whole chunk copies per thread");
 
-// Chunk swizzle of row r (bits 1 and 2 of r): rows 2 apart differ in bit 1 of
-// the slot and rows 4 apart in bit 0, so 8 consecutive rows at one chunk, and
-// 4 consecutive rows at two adjacent chunks, fall on distinct banks.
-__device__ __forceinline__ int w4_swz(int r) { return (r & 2) | ((r >> 2) & 1); }
+// Chunk swizzle of row r: slot = chunk ^ h(r % 16), h a 3-bit value per row.
+// The row stride (1152 bytes) is a multiple of the bank width, so only h
+// separates rows: h is distinct over any 8 aligned rows and over the even and
+// the odd rows of 16 (16-byte reads, 8 or 16 lanes per cycle), and h >> 1 is
+// distinct over any 4 aligned rows and over the same-parity rows of 8 (the
+// transposed reads: 4 or 8 rows at 2 adjacent chunks), so both operand reads
+// are free of bank conflicts with 32 or with 64 banks.
+__device__ __forceinline__ int w4_swz(int r) {
+  constexpr uint64_t kH = 0x4602753157136420ull;   // h(i) in nibble i: 0 2 4 6 3 1 7 5 1 3 5 7 2 0 6 4
+  return (int)((kH >> (4 * (r & 15))) & 7u);
+}
 
 template <bool SPLIT>
 __global__ __launch_bounds__(kW4Threads, 2) void attend_w4_kernel(AttArgs a) {
@@ -737,15 +744,20 @@ __global__ __launch_bounds__(kW4Threads, 2) void attend_w4_kernel(AttArgs a) {
 #pragma unroll
   for (int nt = 0; nt < kL / 16; ++nt) o[nt] = f32x4{0, 0, 0, 0};
 
-  // per-lane LDS offsets: QK rows 16 t + l16 at chunk g4 + 4 ks; PV transposed
-  // reads of rows 4 g4 + l16 / 4 (+ 16) at columns 16 nt + 4 (l16 % 4), whose
-  // slot depends on nt's parity
-  const int qk_off = kW4RowB * l16 + 16 * (g4 ^ w4_swz(l16));
-  const int pr = 4 * g4 + (l16 >> 2);
-  int pv_off[2];
+  // per-lane LDS offsets (h(r + 16) = h(r)): QK reads rows 16 t + l16 at chunk
+  // 4 ks + g4, slot 8 (ks >> 1) + ((4 (ks & 1) + g4) ^ h), by ks's parity; PV's
+  // transposed reads take rows 4 g4 + l16 / 4 (+ 16) at columns 16 nt + 4 (l16 % 4),
+  // chunk 2 nt + (l16 % 4) / 2, slot 8 (nt >> 2) + ((2 (nt & 3) + (l16 % 4) / 2) ^ h), by nt % 4
+  const int hq = w4_swz(l16);
+  int qk_off[2];
 #pragma unroll
-  for (int par = 0; par < 2; ++par)
-    pv_off[par] = kW4RowB * pr + 16 * ((2 * par + ((l16 & 3) >> 1)) ^ w4_swz(pr)) + 8 * (l16 & 1);
+  for (int par = 0; par < 2; ++par) qk_off[par] = kW4RowB * l16 + 16 * ((4 * par + g4) ^ hq);
+  const int pr = 4 * g4 + (l16 >> 2);
+  const int hp = w4_swz(pr);
+  int pv_off[4];
+#pragma unroll
+  for (int m4 = 0; m4 < 4; ++m4)
+    pv_off[m4] = kW4RowB * pr + 16 * ((2 * m4 + ((l16 & 3) >> 1)) ^ hp) + 8 * (l16 & 1);
 
   for (int st = 0; st < nsteps; ++st) {
     uint8_t *cur = w4lds + (st & 1) * kW4BufB;
@@ -760,12 +772,13 @@ __global__ __launch_bounds__(kW4Threads, 2) void attend_w4_kernel(AttArgs a) {
     f32x4 acc[2];
 #pragma unroll
     for (int t = 0; t < 2; ++t) {
-      const uint8_t *rp = cur + kW4RowB * 16 * t + qk_off;
+      const uint8_t *rp = cur + kW4RowB * 16 * t;
       acc[t] = f32x4{0, 0, 0, 0};
 #pragma unroll
       for (int ks = 0; ks < kW / 32; ++ks)
-        acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(*reinterpret_cast<const u32x4 *>(rp + 64 * ks)),
-                                                         qa[ks], acc[t], 0, 0, 0);
+        acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+            as_bf16x8(*reinterpret_cast<const u32x4 *>(rp + qk_off[ks & 1] + 128 * (ks >> 1))), qa[ks], acc[t], 0, 0,
+            0);
     }
     float z[2][4];
     float mx = -INFINITY;
@@ -817,7 +830,7 @@ __global__ __launch_bounds__(kW4Threads, 2) void attend_w4_kernel(AttArgs a) {
     // PV: 32 column tiles
 #pragma unroll
     for (int nt = 0; nt < kL / 16; ++nt) {
-      const uint8_t *vb = cur + pv_off[nt & 1] + 64 * (nt >> 1);
+      const uint8_t *vb = cur + pv_off[nt & 3] + 128 * (nt >> 2);
       const i16x4 v0 = lds_read_tr(vb);
       const i16x4 v1 = lds_read_tr(vb + 16 * kW4RowB);
       const bf16x8 b = __builtin_bit_cast(
