@@ -658,6 +658,26 @@ __device__ __forceinline__ int w4_swz(int r) {
   return (int)((kH >> (4 * (r & 15))) & 7u);
 }
 
+// Lanes l and l ^ 16 (l ^ 32) combined by the VALU lane swaps (no LDS round
+// trip): v_permlane16_swap / v_permlane32_swap of x with itself leave the two
+// partners' values in the two results of every lane.
+__device__ __forceinline__ float max_xor16(float x) {
+  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float max_xor32(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float sum_xor16(float x) {
+  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+__device__ __forceinline__ float sum_xor32(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
 template <bool SPLIT>
 __global__ __launch_bounds__(kW4Threads, 2) void attend_w4_kernel(AttArgs a) {
   extern __shared__ __align__(16) uint8_t w4lds[];
@@ -790,8 +810,7 @@ __global__ __launch_bounds__(kW4Threads, 2) void attend_w4_kernel(AttArgs a) {
         z[t][i] = ((valid >> r) & 1u) ? acc[t][i] * a.scale_log2 : -INFINITY;
         mx = fmaxf(mx, z[t][i]);
       }
-    mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
-    mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+    mx = max_xor32(max_xor16(mx));
     // lazy reference maximum (kSlack)
     const bool grow = mx > m_run + kSlack;
     const float m_new = grow ? mx : m_run;
@@ -850,8 +869,7 @@ __global__ __launch_bounds__(kW4Threads, 2) void attend_w4_kernel(AttArgs a) {
   }
 
   // epilogue: the head's sum over its 4 lanes; o's lane holds heads 4 g4 + i
-  l_run += __shfl_xor(l_run, 16, 64);
-  l_run += __shfl_xor(l_run, 32, 64);
+  l_run = sum_xor32(sum_xor16(l_run));
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     const int hl = 4 * g4 + i;

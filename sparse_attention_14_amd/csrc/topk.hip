@@ -342,15 +342,15 @@ __device__ void finish_regs(const SelectArgs &a, int qi, uint32_t C, uint32_t lo
 }
 
 // Loads the rounds of scores of the pass at g0: token g0 + tid + NT i, clamped
-// to the row's allocated length (a row holds at least max_len scores), so
-// every load is unconditional and none waits for the row's visible count;
-// scores past the visible count are masked by the caller.
+// below `end` (<= the row's allocated length: a row holds at least max_len
+// scores), so every load is unconditional and none waits for the row's
+// visible count; scores past the visible count are masked by the caller.
 template <int NT, int RP>
-__device__ __forceinline__ void load_pass_clamped(const float *row, int g0, int max_len, float (&v)[RP]) {
+__device__ __forceinline__ void load_pass_clamped(const float *row, int g0, int end, float (&v)[RP]) {
 #pragma unroll
   for (int i = 0; i < RP; ++i) {
     const int t = g0 + (int)threadIdx.x + NT * i;
-    v[i] = row[t < max_len ? t : max_len - 1];
+    v[i] = row[t < end ? t : end - 1];
   }
 }
 
@@ -641,7 +641,9 @@ __global__ __launch_bounds__(kFilterThreads) void select_filter_kernel(SelectArg
   // in flight while the row length arrives: the chunk's scores and, in the
   // first wavefront, the row's bound reports
   float v[kPassRounds];
-  load_pass_clamped<NT, kPassRounds>(row, c0, a.max_len, v);
+  // (clamped to the chunk's end: a pass may be longer than the chunk, and the
+  // next chunk's scores are another workgroup's to read)
+  load_pass_clamped<NT, kPassRounds>(row, c0, min(c0 + a.chunk, a.max_len), v);
   const bool few_reports = a.n_bounds <= 512;
   uint32_t rep8[8], rep32[32];
   if (a.bounds && tid < 64) {
