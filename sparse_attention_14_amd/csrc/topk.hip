@@ -526,13 +526,14 @@ __global__ __launch_bounds__(kLocalThreads) void select_local_kernel(SelectArgs 
   }
 
   // this wavefront's slice [t0, t1) (64-token multiples), read in batches of RW
-  // rounds through a buffer resource over the row's n scores: loads past the
-  // row read 0 and are dropped (tokens past t1 are not live)
+  // rounds through a buffer resource that ends at the slice's end: loads past
+  // it (the tail of the last batch, the batch after it) read 0 without
+  // touching memory and are dropped, instead of reading the next slice
   const int span = ((n + W - 1) / W + 63) / 64 * 64;
   const int t0 = min(wave * span, n), t1 = min(t0 + span, n);
   const int pairs = (t1 - t0 + 2 * 64 * RW - 1) / (2 * 64 * RW);
   const __amdgpu_buffer_rsrc_t rrow =
-      __builtin_amdgcn_make_buffer_rsrc(const_cast<float *>(row), (short)0, n * 4, 0x00020000);
+      __builtin_amdgcn_make_buffer_rsrc(const_cast<float *>(row), (short)0, t1 * 4, 0x00020000);
   auto load_batch = [&](int b, float (&v)[RW]) {
     const uint32_t off = (uint32_t)(t0 + 64 * RW * b + lane) * 4u;
 #pragma unroll
@@ -568,7 +569,8 @@ __global__ __launch_bounds__(kLocalThreads) void select_local_kernel(SelectArgs 
                                          : -INFINITY;
 
   uint2 *region = L.cand + wave * kWaveCap;
-  uint32_t cnt = 0;   // candidates of this wavefront (uniform)
+  uint32_t cnt = 0;      // candidates of this wavefront (uniform)
+  float fmx = -INFINITY;  // largest candidate of this lane (fmaxf skips NaN; see below)
   auto filter_batch = [&](int b, const float (&v)[RW]) {
 #pragma unroll
     for (int i = 0; i < RW; ++i) {
@@ -578,6 +580,7 @@ __global__ __launch_bounds__(kLocalThreads) void select_local_kernel(SelectArgs 
       const uint32_t pos = cnt + lanes_below(m);
       if (in && pos < (uint32_t)kWaveCap) region[pos] = make_uint2(__float_as_uint(v[i]), (uint32_t)t);
       cnt += (uint32_t)__popcll(m);
+      fmx = fmaxf(fmx, in ? v[i] : -INFINITY);
     }
   };
   // two batches per iteration in alternating buffers: while one is filtered the
@@ -589,16 +592,25 @@ __global__ __launch_bounds__(kLocalThreads) void select_local_kernel(SelectArgs 
     filter_batch(2 * p + 1, vb);
   }
   drain_loads();
-  if (lane == 0) L.scratch[wave] = cnt;
+  // The window's top: the key of the largest candidate.  fmaxf skips NaN and
+  // -0 and +0 share a key, so order_key(max) is the largest key unless every
+  // candidate is NaN (key 0), when it is the key of -inf, still an upper bound.
+  const uint32_t kmx = wave_max_u32(order_key(fmx));   // (order_key is monotone; fmx is never NaN)
+  if (lane == 0) {
+    L.scratch[wave] = cnt;
+    L.scratch[W + wave] = kmx;
+  }
   __syncthreads();   // (also publishes the regions)
   uint32_t off[W + 1];
   off[0] = 0;
   bool overflow = false;
+  uint32_t mx = 0;
 #pragma unroll
   for (int w = 0; w < W; ++w) {
     const uint32_t c = L.scratch[w];
     overflow |= c > (uint32_t)kWaveCap;
     off[w + 1] = off[w] + c;
+    if (c) mx = max(mx, L.scratch[W + w]);
   }
   const uint32_t C = off[W];
   if (overflow || C < (uint32_t)k) {
@@ -608,10 +620,9 @@ __global__ __launch_bounds__(kLocalThreads) void select_local_kernel(SelectArgs 
   }
   // candidate j (token order) is entry j - off[w] of region w, off[w] <= j < off[w + 1];
   // its key is formed here, once per candidate
-  constexpr int R = kRegCap / NT;
-  static_assert(kLocalCap <= kRegCap, "every candidate of the regions fits the registers");
+  constexpr int R = kLocalCap / NT;   // 14 slots: the regions hold at most kLocalCap candidates
+  static_assert(kLocalCap % NT == 0, "whole slots");
   uint32_t ck[R], ct[R];
-  uint32_t mx = 0;
 #pragma unroll
   for (int m = 0; m < R; ++m) {
     const uint32_t j = tid + NT * m;
@@ -621,9 +632,7 @@ __global__ __launch_bounds__(kLocalThreads) void select_local_kernel(SelectArgs 
     const uint2 c = j < C ? L.cand[at] : make_uint2(0u, 0u);
     ck[m] = j < C ? order_key(__uint_as_float(c.x)) : 0u;
     ct[m] = c.y;
-    mx = max(mx, ck[m]);
   }
-  mx = block_max<NT>(mx, L.scratch + 16);   // (words apart from the counts read above)
   finish_regs<NT, R>(a, qi, C, t_lo, mx, ck, ct, L);
 }
 
