@@ -170,6 +170,23 @@ def test_many_rows_several_rounds_per_workgroup():
     _run(s, lens, 2048)
 
 
+def test_many_rows_four_per_workgroup():
+    # 2050 rows: workgroups take four rows each (the last group two); rows that
+    # keep every token, empty rows and rows that take the exact fallback are
+    # interleaved with ordinary ones inside the groups
+    rng = np.random.default_rng(45)
+    rows, n = 2050, 9000
+    s = _mixed_rows(rng, rows, n)
+    lens = rng.integers(7169, n + 1, size=rows)
+    lens[::5] = rng.integers(0, 2049, size=len(lens[::5]))
+    lens[7::97] = 0
+    s[11::53] = np.float32(2.5)                                     # all-equal rows: the exact fallback
+    lens[-1] = n
+    print(f"case: {rows} x {n}, four rows per workgroup", flush=True)
+    _run(s, lens, 2048)
+    _run(s, lens, 2048, order="score")
+
+
 def test_many_rows_heavy_ties_take_the_exact_fallback():
     # six distinct values: the sampled bound keeps far more than a region holds,
     # so those rows take the whole-workgroup exact path between streamed rows
