@@ -482,8 +482,9 @@ def main():
         plse = torch.empty(pp.n_q, pp.mla_heads, device="cuda")
         aws = torch.zeros(max(dsa.mla_sparse_attend_workspace_size(pp.n_q, pp.mla_heads, pp.kv_lora, pp.topk), 1),
                           dtype=torch.uint8, device="cuda")
-        # two untimed launches of each (first touches of freshly allocated memory
-        # and the clock ramp), then back-to-back timed launches between two events
+        # untimed launches of each first (first touches of freshly allocated memory,
+        # and the shader clock settling under sustained load, as for the indexer),
+        # then back-to-back timed launches between two events
         def ptopk():
             dsa.dsa_topk(pidx, None, ps, dpp.q_len, pp.topk, pp.max_len, workspace=tws)
 
@@ -492,7 +493,7 @@ def main():
                                   pp.softmax_scale, workspace=aws)
 
         def timed(fn, reps):
-            for _ in range(2):
+            for _ in range(10):
                 fn()
             torch.cuda.synchronize()
             e0.record()
@@ -503,7 +504,7 @@ def main():
             return e0.elapsed_time(e1) / 1e3 / reps
 
         t_pt = timed(ptopk, 10)
-        t_pa = timed(pattend, 5)
+        t_pa = timed(pattend, 10)
         mla_flops = 0
         for n in pp.q_len:
             kept = min(int(n), pp.topk)
@@ -512,7 +513,7 @@ def main():
                    "indexer_ms": round(t_pi * 1e3, 3), "indexer_tflops": round(flops / t_pi / 1e12, 1),
                    "indexer_mfma_frac": round(flops / t_pi / 1e12 / BF16_PEAK_TFLOPS, 4),
                    "topk_ms": round(t_pt * 1e3, 3), "topk_launches": 10, "sparse_mla_ms": round(t_pa * 1e3, 3),
-                   "sparse_mla_launches": 5,
+                   "sparse_mla_launches": 10,
                    "sparse_mla_tflops": round(mla_flops / t_pa / 1e12, 1)}
 
     # ------------------------------------------- multi-token decode window ---

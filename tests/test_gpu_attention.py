@@ -43,6 +43,12 @@ CASES = {
     "bf16_wide_h128": (S(inputs.DECODE_8K, name="a9", wid=309, batch=8, seq_len=(3000, 3000), mla_heads=128), 2048),
     "bf16_wide_short_rows": (S(inputs.PAGED_DECODE, name="a10", wid=310, batch=16, seq_len=(1, 300)), 2048),
     "bf16_wide_k100": (S(inputs.DECODE_8K, name="a16", wid=316, batch=20, seq_len=(50, 600)), 100),
+    # peaky logits over several 32-row steps of the 64-head kernel: the lazy reference maximum moves
+    # mid-split (rescales), split (20 queries) and unsplit (300 queries, 512 kept slots)
+    "bf16_wide_peaky_q": (S(inputs.DECODE_8K, name="a21", wid=321, batch=20, seq_len=(3000, 3000),
+                            q_mla_sigma=20.0), 2048),
+    "bf16_many_queries_peaky": (S(inputs.PREFILL_64K, name="a22", wid=322, seq_len=(2500, 2500), prefill_queries=300,
+                                  q_mla_sigma=20.0), 512),
     "fp8lat_wide_k100_h128": (S(inputs.DECODE_128K_FP8_LAT8, name="a17", wid=317, batch=9, seq_len=(50, 600),
                                 mla_heads=128, tie_fraction=0.0), 100),
     # e4m3fn latent rows with a float32 scale per token: 16-head kernel (split), 64-head kernel (split, paged;
