@@ -79,6 +79,9 @@ typedef enum {
  *   - rows, row_stride and block_stride must be multiples of 16 bytes, and
  *     row_stride >= width * element size.  A row_stride above 16 MiB returns
  *     DSA_ERR_UNSUPPORTED.
+ *   - The row at `rows` itself (and, when paged, entry 0 of every addressed
+ *     sequence's block table row) must be readable whenever a call has work:
+ *     -1 index slots load it in place of a token and discard the value.
  */
 typedef struct {
   const void *rows;

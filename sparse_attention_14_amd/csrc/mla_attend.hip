@@ -627,7 +627,7 @@ __global__ __launch_bounds__(kWideThreads) void attend_wide_kernel(AttArgs a) {
 // kept rows are copied from memory straight into LDS (global_load_lds_dwordx4,
 // no registers), one step ahead into the other of two buffers; one barrier per
 // step and two workgroups per CU.  The 16-byte chunk c of row r sits at slot
-// c ^ g(r) of the row (g below), which keeps both operand reads free of bank
+// c ^ h(r) of the row (h below), which keeps both operand reads free of bank
 // conflicts:
 //   QK^T : v_mfma_f32_16x16x32_bf16 with A = 16 rows (LDS) and B = q (16 heads,
 //          registers), so D leaves lane (head l16, g4) with rows 4 g4 + i of
@@ -699,7 +699,7 @@ __global__ __launch_bounds__(kW4Threads, 2) void attend_w4_kernel(AttArgs a) {
 
   // Step copies: this wavefront's 9 instructions write LDS bytes
   // [1024 (9 wave + u), +1024) of a buffer; lane l's 16 bytes there are entry
-  // q = 64 (9 wave + u) + l = row q / 72, slot q % 72, i.e. chunk (q % 72) ^ g(row).
+  // q = 64 (9 wave + u) + l = row q / 72, slot q % 72, i.e. chunk (q % 72) ^ h(row).
   // (recomputed where used: hoisted out of the step loop they would not fit the registers)
   auto fresh_lane = [&]() {
     int l = lane;
