@@ -251,15 +251,21 @@ __global__ __launch_bounds__(kAttThreads) void attend_bf16_kernel(AttArgs a) {
     }
     __syncthreads();
 
-    // QK^T: this wavefront's 16 rows of its team's tile
+    // QK^T: this wavefront's 16 rows of its team's tile; each row operand is
+    // read two MFMAs ahead (the scheduling barriers keep the reads from being
+    // hoisted further, which would not fit the registers)
     const int row = tw * 16 + l16;
     f32x4 sacc = {0, 0, 0, 0};
     {
       const uint8_t *rp = my_rows + row * kRowBytes + 16 * g4;
+      auto qk_read = [&](int ks) { return as_bf16x8(*reinterpret_cast<const u32x4 *>(rp + 64 * ks)); };
+      bf16x8 br[2] = {qk_read(0), qk_read(1)};
 #pragma unroll
       for (int ks = 0; ks < kW / 32; ++ks) {
-        const bf16x8 b = as_bf16x8(*reinterpret_cast<const u32x4 *>(rp + 64 * ks));
+        const bf16x8 b = br[ks & 1];
+        if (ks + 2 < kW / 32) br[ks & 1] = qk_read(ks + 2);
         sacc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qa[ks], b, sacc, 0, 0, 0);
+        __builtin_amdgcn_sched_barrier(0);
       }
     }
     const bool valid = lvalid[team * kTile + row] != 0;
@@ -327,15 +333,20 @@ __global__ __launch_bounds__(kAttThreads) void attend_bf16_kernel(AttArgs a) {
       const bf16x8 alo =
           as_bf16x8(*reinterpret_cast<const u32x4 *>(&my_p[kHG * kTile + l16 * kTile + 32 * ks2 + 8 * g4]));
       const uint8_t *vb = my_rows + (32 * ks2 + 8 * g4 + (l16 >> 2)) * kRowBytes + (128 * tw + 4 * (l16 & 3)) * 2;
-#pragma unroll
-      for (int nt = 0; nt < 8; ++nt) {
+      auto pv_read = [&](int nt) {
         const i16x4 v0 = lds_read_tr(vb + 32 * nt);
         const i16x4 v1 = lds_read_tr(vb + 4 * kRowBytes + 32 * nt);
-        const bf16x8 b = __builtin_bit_cast(
-            bf16x8, (__attribute__((__vector_size__(8 * sizeof(short)))) short){v0[0], v0[1], v0[2], v0[3], v1[0],
-                                                                                 v1[1], v1[2], v1[3]});
+        return __builtin_bit_cast(bf16x8, (__attribute__((__vector_size__(8 * sizeof(short)))) short){
+                                              v0[0], v0[1], v0[2], v0[3], v1[0], v1[1], v1[2], v1[3]});
+      };
+      bf16x8 vr[2] = {pv_read(0), pv_read(1)};   // V operands one tile ahead
+#pragma unroll
+      for (int nt = 0; nt < 8; ++nt) {
+        const bf16x8 b = vr[nt & 1];
+        if (nt + 2 < 8) vr[nt & 1] = pv_read(nt + 2);
         o[nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ahi, b, o[nt], 0, 0, 0);
         o[nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(alo, b, o[nt], 0, 0, 0);
+        __builtin_amdgcn_sched_barrier(0);
       }
     }
     __syncthreads();
@@ -645,6 +656,8 @@ constexpr int kW4PerThread = kW4Step * kW4Chunks / kW4Threads;   // 9 chunk copi
 constexpr int kW4BufB = kW4Step * kW4RowB;                // 36864
 constexpr size_t kW4LdsBytes = 2 * (size_t)kW4BufB;       // two buffers: 73728
 static_assert(kW4Step * kW4Chunks == kW4PerThread * kW4Threads, "whole chunk copies per thread");
+constexpr int kW4QkAhead = 2;   // row operands in flight ahead of the QK^T MFMAs
+constexpr int kW4PvAhead = 2;   // V operands in flight ahead of the PV MFMAs
 
 // Chunk swizzle of row r: slot = chunk ^ h(r % 16), h a 3-bit value per row.
 // The row stride (1152 bytes) is a multiple of the bank width, so only h
@@ -707,28 +720,37 @@ __global__ __launch_bounds__(kW4Threads, 2) void attend_w4_kernel(AttArgs a) {
     return l;
   };
   auto copy_row = [&](int u, int l) { return (64 * (kW4PerThread * wave + u) + l) / kW4Chunks; };
-  auto copy_ofs = [&](int u, int l) {
-    const int q = 64 * (kW4PerThread * wave + u) + l;
-    return 16 * ((q % kW4Chunks) ^ w4_swz(q / kW4Chunks));
-  };
   // Lanes 0..31 each hold the token of one row of a step; the rows' validity is
   // a 32-bit mask (uniform).
   auto step_token = [&](int st) {
     const int j = j0 + st * kW4Step + lane;
     return (lane < kW4Step && j < j1) ? idx_row[j] : -1;
   };
+  // The wavefront's entries cover its rows 8 wave .. 8 wave + 7: instruction u
+  // starts in row 8 wave + (64 u) / 72 at slot (64 u) % 72, so a lane's row is
+  // that one or the next; the eight row addresses are read from their lanes
+  // into scalar registers once per step (no lane exchange through LDS).
   auto issue_copies = [&](int tok, uint8_t *buf) {
     int slot;
     const int64_t blk = cache_block(a.latent, seq, tok >= 0 ? tok : 0, slot);
     const uint8_t *rp = tok >= 0 ? cache_row(a.latent, blk, slot) : a.latent.rows;
     const uint64_t rp64 = reinterpret_cast<uint64_t>(rp);
+    uint64_t row_addr[9];
+#pragma unroll
+    for (int k = 0; k < 8; ++k)
+      row_addr[k] = ((uint64_t)(uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(rp64 >> 32), 8 * wave + k) << 32) |
+                    (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)rp64, 8 * wave + k);
+    row_addr[8] = row_addr[7];   // (never selected: the last instruction ends with its row)
     const int l = fresh_lane();
 #pragma unroll
     for (int u = 0; u < kW4PerThread; ++u) {
-      const int r = copy_row(u, l);
-      const uint32_t lo = (uint32_t)__shfl((int)(uint32_t)rp64, r, 64);
-      const uint32_t hi = (uint32_t)__shfl((int)(uint32_t)(rp64 >> 32), r, 64);
-      const uint8_t *src = reinterpret_cast<const uint8_t *>(((uint64_t)hi << 32) | lo) + copy_ofs(u, l);
+      const int k0 = (64 * u) / kW4Chunks, b0 = (64 * u) % kW4Chunks;
+      const int t = b0 + l;
+      const bool next = t >= kW4Chunks;
+      const int slot_in_row = next ? t - kW4Chunks : t;
+      const int h = next ? w4_swz(8 * wave + k0 + 1) : w4_swz(8 * wave + k0);
+      const uint64_t base = next ? row_addr[k0 + 1] : row_addr[k0];
+      const uint8_t *src = reinterpret_cast<const uint8_t *>(base) + 16 * (slot_in_row ^ h);
       __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void *)src,
                                        (__attribute__((address_space(3))) void *)(buf + 1024 * (kW4PerThread * wave + u)),
                                        16, 0, 0);
@@ -788,17 +810,26 @@ __global__ __launch_bounds__(kW4Threads, 2) void attend_w4_kernel(AttArgs a) {
     if (more) issue_copies(tok_next, nxt);
     const int tok_after = step_token(st + 2);
 
-    // QK^T: D[row 16 t + 4 g4 + i][head l16]
-    f32x4 acc[2];
+    // QK^T: D[row 16 t + 4 g4 + i][head l16].  The two row tiles alternate
+    // (n = 2 ks + t) and each row operand is read kW4QkAhead MFMAs ahead; the
+    // scheduling barriers keep the compiler from hoisting the reads further,
+    // which would not fit the registers.
+    f32x4 acc[2] = {f32x4{0, 0, 0, 0}, f32x4{0, 0, 0, 0}};
+    {
+      auto qk_read = [&](int n) {
+        return as_bf16x8(*reinterpret_cast<const u32x4 *>(cur + kW4RowB * 16 * (n & 1) + qk_off[(n >> 1) & 1] +
+                                                          128 * (n >> 2)));
+      };
+      bf16x8 ar[kW4QkAhead];
 #pragma unroll
-    for (int t = 0; t < 2; ++t) {
-      const uint8_t *rp = cur + kW4RowB * 16 * t;
-      acc[t] = f32x4{0, 0, 0, 0};
+      for (int i = 0; i < kW4QkAhead; ++i) ar[i] = qk_read(i);
 #pragma unroll
-      for (int ks = 0; ks < kW / 32; ++ks)
-        acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-            as_bf16x8(*reinterpret_cast<const u32x4 *>(rp + qk_off[ks & 1] + 128 * (ks >> 1))), qa[ks], acc[t], 0, 0,
-            0);
+      for (int n = 0; n < 2 * (kW / 32); ++n) {
+        const bf16x8 av = ar[n % kW4QkAhead];
+        if (n + kW4QkAhead < 2 * (kW / 32)) ar[n % kW4QkAhead] = qk_read(n + kW4QkAhead);
+        acc[n & 1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, qa[n >> 1], acc[n & 1], 0, 0, 0);
+        __builtin_amdgcn_sched_barrier(0);
+      }
     }
     float z[2][4];
     float mx = -INFINITY;
@@ -846,17 +877,26 @@ __global__ __launch_bounds__(kW4Threads, 2) void attend_w4_kernel(AttArgs a) {
     const bf16x8 ahi = as_bf16x8(u32x4{ph[0], ph[1], ph[2], ph[3]});
     const bf16x8 alo = as_bf16x8(u32x4{pl[0], pl[1], pl[2], pl[3]});
 
-    // PV: 32 column tiles
+    // PV: 32 column tiles, each V operand read kW4PvAhead - 1 tiles ahead
+    {
+      auto pv_read = [&](int nt) {
+        const uint8_t *vb = cur + pv_off[nt & 3] + 128 * (nt >> 2);
+        const i16x4 v0 = lds_read_tr(vb);
+        const i16x4 v1 = lds_read_tr(vb + 16 * kW4RowB);
+        return __builtin_bit_cast(bf16x8, (__attribute__((__vector_size__(8 * sizeof(short)))) short){
+                                              v0[0], v0[1], v0[2], v0[3], v1[0], v1[1], v1[2], v1[3]});
+      };
+      bf16x8 vr[kW4PvAhead];
 #pragma unroll
-    for (int nt = 0; nt < kL / 16; ++nt) {
-      const uint8_t *vb = cur + pv_off[nt & 3] + 128 * (nt >> 2);
-      const i16x4 v0 = lds_read_tr(vb);
-      const i16x4 v1 = lds_read_tr(vb + 16 * kW4RowB);
-      const bf16x8 b = __builtin_bit_cast(
-          bf16x8, (__attribute__((__vector_size__(8 * sizeof(short)))) short){v0[0], v0[1], v0[2], v0[3], v1[0], v1[1],
-                                                                               v1[2], v1[3]});
-      o[nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ahi, b, o[nt], 0, 0, 0);
-      o[nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(alo, b, o[nt], 0, 0, 0);
+      for (int i = 0; i < kW4PvAhead; ++i) vr[i] = pv_read(i);
+#pragma unroll
+      for (int nt = 0; nt < kL / 16; ++nt) {
+        const bf16x8 b = vr[nt % kW4PvAhead];
+        if (nt + kW4PvAhead < kL / 16) vr[nt % kW4PvAhead] = pv_read(nt + kW4PvAhead);
+        o[nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ahi, b, o[nt], 0, 0, 0);
+        o[nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(alo, b, o[nt], 0, 0, 0);
+        __builtin_amdgcn_sched_barrier(0);
+      }
     }
 
     // the next step's rows have landed (this wavefront's copies), invalid ones
