@@ -524,10 +524,17 @@ __global__ __launch_bounds__(kWideThreads) void attend_wide_kernel(AttArgs a) {
       const int row = 32 * wr + 16 * nt + l16;
       const uint8_t *rp = rows + row * kRowBytes + 16 * g4;
       f32x4 sacc = {0, 0, 0, 0};
+      // row operands read two MFMAs ahead (the scheduling barriers keep the
+      // reads from being hoisted further, which would not fit the registers)
+      auto qk_read = [&](int ks) { return as_bf16x8(*reinterpret_cast<const u32x4 *>(rp + 64 * ks)); };
+      bf16x8 br[2] = {qk_read(0), qk_read(1)};
 #pragma unroll
-      for (int ks = 0; ks < kW / 32; ++ks)
-        sacc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-            qa[ks], as_bf16x8(*reinterpret_cast<const u32x4 *>(rp + 64 * ks)), sacc, 0, 0, 0);
+      for (int ks = 0; ks < kW / 32; ++ks) {
+        const bf16x8 b = br[ks & 1];
+        if (ks + 2 < kW / 32) br[ks & 1] = qk_read(ks + 2);
+        sacc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qa[ks], b, sacc, 0, 0, 0);
+        __builtin_amdgcn_sched_barrier(0);
+      }
       const bool valid = lvalid[row] != 0;
       const float rs = F8 ? lscale[row] : 1.0f;
 #pragma unroll
@@ -593,15 +600,20 @@ __global__ __launch_bounds__(kWideThreads) void attend_wide_kernel(AttArgs a) {
       const bf16x8 alo = as_bf16x8(
           *reinterpret_cast<const u32x4 *>(&my_p[kHG * kWideStep + l16 * kWideStep + 32 * ks2 + 8 * g4]));
       const uint8_t *vb = rows + (32 * ks2 + 8 * g4 + (l16 >> 2)) * kRowBytes + (256 * wr + 4 * (l16 & 3)) * 2;
-#pragma unroll
-      for (int nt = 0; nt < NT; ++nt) {
+      auto pv_read = [&](int nt) {
         const i16x4 v0 = lds_read_tr(vb + 32 * nt);
         const i16x4 v1 = lds_read_tr(vb + 4 * kRowBytes + 32 * nt);
-        const bf16x8 b = __builtin_bit_cast(
-            bf16x8, (__attribute__((__vector_size__(8 * sizeof(short)))) short){v0[0], v0[1], v0[2], v0[3], v1[0],
-                                                                                 v1[1], v1[2], v1[3]});
+        return __builtin_bit_cast(bf16x8, (__attribute__((__vector_size__(8 * sizeof(short)))) short){
+                                              v0[0], v0[1], v0[2], v0[3], v1[0], v1[1], v1[2], v1[3]});
+      };
+      bf16x8 vr[2] = {pv_read(0), pv_read(1)};   // V operands one tile ahead
+#pragma unroll
+      for (int nt = 0; nt < NT; ++nt) {
+        const bf16x8 b = vr[nt & 1];
+        if (nt + 2 < NT) vr[nt & 1] = pv_read(nt + 2);
         o[nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ahi, b, o[nt], 0, 0, 0);
         o[nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(alo, b, o[nt], 0, 0, 0);
+        __builtin_amdgcn_sched_barrier(0);
       }
     }
     __syncthreads();
