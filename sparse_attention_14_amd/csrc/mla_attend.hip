@@ -703,6 +703,17 @@ __device__ __forceinline__ float sum_xor32(float x) {
   return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 
+// One global_load_lds_dwordx4: lane l's 16 bytes at src land at lds + 16 l.
+// Issued as assembly so that the compiler does not order later LDS reads
+// behind it: it cannot tell the two step buffers apart and would otherwise
+// wait for every copy in flight (the next step's included) before the first
+// read of the current step.  The caller waits for its copies (s_waitcnt
+// vmcnt) before their buffer is read.
+__device__ __forceinline__ void copy16_to_lds(const uint8_t *src, uint8_t *lds) {
+  const uint32_t m0 = (uint32_t)reinterpret_cast<uintptr_t>((__attribute__((address_space(3))) uint8_t *)lds);
+  asm volatile("s_nop 0\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(src), "{m0}"(m0) : "memory");
+}
+
 template <bool SPLIT>
 __global__ __launch_bounds__(kW4Threads, 2) void attend_w4_kernel(AttArgs a) {
   extern __shared__ __align__(16) uint8_t w4lds[];
@@ -763,9 +774,7 @@ __global__ __launch_bounds__(kW4Threads, 2) void attend_w4_kernel(AttArgs a) {
       const int h = next ? w4_swz(8 * wave + k0 + 1) : w4_swz(8 * wave + k0);
       const uint64_t base = next ? row_addr[k0 + 1] : row_addr[k0];
       const uint8_t *src = reinterpret_cast<const uint8_t *>(base) + 16 * (slot_in_row ^ h);
-      __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void *)src,
-                                       (__attribute__((address_space(3))) void *)(buf + 1024 * (kW4PerThread * wave + u)),
-                                       16, 0, 0);
+      copy16_to_lds(src, buf + 1024 * (kW4PerThread * wave + u));
     }
   };
   // After a wavefront's copies have landed: its entries of invalid rows become
@@ -802,18 +811,24 @@ __global__ __launch_bounds__(kW4Threads, 2) void attend_w4_kernel(AttArgs a) {
   // 4 ks + g4, slot 8 (ks >> 1) + ((4 (ks & 1) + g4) ^ h), by ks's parity; PV's
   // transposed reads take rows 4 g4 + l16 / 4 (+ 16) at columns 16 nt + 4 (l16 % 4),
   // chunk 2 nt + (l16 % 4) / 2, slot 8 (nt >> 2) + ((2 (nt & 3) + (l16 % 4) / 2) ^ h), by nt % 4
-  const int hq = w4_swz(l16);
-  int qk_off[2];
+  // (formed in every step from the lane index: held across the loop they would
+  // push a value out to scratch, and its reload would wait for the copies in flight)
+  auto lds_offsets = [&](int (&qk_off)[2], int (&pv_off)[4]) {
+    const int l = fresh_lane();
+    const int lq = l & 15, gq = l >> 4;
+    const int hq = w4_swz(lq);
 #pragma unroll
-  for (int par = 0; par < 2; ++par) qk_off[par] = kW4RowB * l16 + 16 * ((4 * par + g4) ^ hq);
-  const int pr = 4 * g4 + (l16 >> 2);
-  const int hp = w4_swz(pr);
-  int pv_off[4];
+    for (int par = 0; par < 2; ++par) qk_off[par] = kW4RowB * lq + 16 * ((4 * par + gq) ^ hq);
+    const int pr = 4 * gq + (lq >> 2);
+    const int hp = w4_swz(pr);
 #pragma unroll
-  for (int m4 = 0; m4 < 4; ++m4)
-    pv_off[m4] = kW4RowB * pr + 16 * ((2 * m4 + ((l16 & 3) >> 1)) ^ hp) + 8 * (l16 & 1);
+    for (int m4 = 0; m4 < 4; ++m4)
+      pv_off[m4] = kW4RowB * pr + 16 * ((2 * m4 + ((lq & 3) >> 1)) ^ hp) + 8 * (lq & 1);
+  };
 
   for (int st = 0; st < nsteps; ++st) {
+    int qk_off[2], pv_off[4];
+    lds_offsets(qk_off, pv_off);
     uint8_t *cur = w4lds + (st & 1) * kW4BufB;
     uint8_t *nxt = w4lds + ((st + 1) & 1) * kW4BufB;
     // next step's copies into the other buffer (read by no one since the barrier)
