@@ -19,10 +19,13 @@
 // Splits write unnormalised partial outputs with their (max, sum); a merge
 // kernel combines them in split order (deterministic).  The four head groups
 // of one (query, split) are placed on the same XCD so that their identical
-// row gathers hit one L2.
+// row gathers hit one L2.  Many queries (prefill chunks, decode windows) take
+// the 64-head kernel further below, which gathers each kept row once for all
+// heads of a query.
 #include "kernels.hpp"
 
 #include <atomic>
+#include <utility>
 
 namespace dsa {
 namespace {
@@ -411,239 +414,14 @@ __global__ __launch_bounds__(kAttThreads) void attend_bf16_kernel(AttArgs a) {
 }
 
 // Many queries (decode windows, prefill): a workgroup owns one query, a block
-// of 64 heads and a split of the index slots, so each kept row is gathered
-// once for all 64 heads (the 16-head kernel above spreads few queries over
-// more workgroups, at the price of gathering every row once per head group).
-// Per 64-slot step the rows sit in LDS (8 threads per row, 128 contiguous
-// bytes per load); wavefront w takes head group w / 2 (16 heads) and half
-// w % 2 of the rows for QK^T and of the 512 value columns for PV.  The next
-// step's rows are loaded into registers while a step is computed.
+// of 64 heads and a split of whole 64-slot steps of the index list, so each
+// kept row is gathered once for all 64 heads (the 16-head kernel above spreads
+// few queries over more workgroups, at the price of gathering every row once
+// per head group).
 constexpr int kWideHeads = 64;
 constexpr int kWideStep = 64;
-constexpr int kWideThreads = 512;
-constexpr int kWidePer = kW * 2 / 16 / 8;   // 16-byte chunks per thread and row (9)
 
-template <bool SPLIT, bool F8>
-__global__ __launch_bounds__(kWideThreads) void attend_wide_kernel(AttArgs a) {
-  __shared__ __align__(16) uint8_t rows[kWideStep * kRowBytes];
-  __shared__ __align__(16) uint16_t lp[4][2][kHG * kWideStep];   // per head group: P hi / lo, [head][row]
-  __shared__ float red[4][2][2][kHG];                             // [head group][max | sum][row half][head]
-  __shared__ uint8_t lvalid[kWideStep];
-  __shared__ float lscale[F8 ? kWideStep : 1];
-
-  const int H = a.n_heads;
-  const int n_hb = H / kWideHeads;
-  const int wg = blockIdx.x;
-  const int qi = wg / (a.splits * n_hb);
-  const int rem = wg - qi * a.splits * n_hb;
-  const int hb = rem / a.splits, sp = rem - (rem / a.splits) * a.splits;
-  const int tid = threadIdx.x, lane = tid & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int hg = wave >> 1, wr = wave & 1;
-  const int l16 = lane & 15, g4 = lane >> 4;
-  const int h0 = hb * kWideHeads + hg * kHG;
-  const int seq = attend_seq(a.q_seq, qi, a.seq_per);
-  const int j0 = sp * a.rows_per_split;
-  const int j1 = min(j0 + a.rows_per_split, a.k);
-  const int nsteps = (j1 - j0 + kWideStep - 1) / kWideStep;
-
-  // gather role: row gr of a step, chunks gq + 8 i (i < 9), 128 contiguous bytes per load
-  // (fp8 rows: 36 chunks, i < 5, the last only for gq < 4)
-  const int gr = tid >> 3, gq = tid & 7;
-  constexpr int NV = F8 ? 5 : kWidePer;
-  u32x4 v[NV];
-  float v_sc = 0.0f;
-  bool v_ok;
-  auto load_rows = [&](int step) {
-    const int j = j0 + step * kWideStep + gr;
-    const int raw = a.indices[(int64_t)qi * a.k + (j < a.k ? j : a.k - 1)];
-    const int t = j < j1 ? raw : -1;
-    v_ok = t >= 0;
-    int slot;
-    const int64_t blk = cache_block(a.latent, seq, v_ok ? t : 0, slot);
-    const uint8_t *src = v_ok ? cache_row(a.latent, blk, slot) : a.latent.rows;
-#pragma unroll
-    for (int i = 0; i < NV; ++i) v[i] = load16(src + (F8 ? min(16 * gq + 128 * i, kW - 16) : 16 * gq + 128 * i));
-    if (F8) v_sc = v_ok ? a.latent.scale[blk * a.latent.scale_block_stride + slot] : 0.0f;
-  };
-  load_rows(0);
-
-  // q operand (head h0 + l16, dims 32 ks + 8 g4 + [0, 8))
-  bf16x8 qa[kW / 32];
-  {
-    const uint16_t *qr = a.q + ((int64_t)qi * H + h0 + l16) * kW + 8 * g4;
-#pragma unroll
-    for (int ks = 0; ks < kW / 32; ++ks) qa[ks] = as_bf16x8(load16(qr + 32 * ks));
-  }
-
-  float m_run[4], l_run[4];
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    m_run[i] = -INFINITY;
-    l_run[i] = 0.0f;
-  }
-  constexpr int NT = kL / 2 / 16;   // 16 value-column tiles per wavefront
-  f32x4 o[NT];
-#pragma unroll
-  for (int nt = 0; nt < NT; ++nt) o[nt] = f32x4{0, 0, 0, 0};
-  uint16_t *my_p = lp[hg][0];
-
-  for (int step = 0; step < nsteps; ++step) {
-    {
-      if (F8) {
-        // fp8 chunk gq + 8 i -> 16 bf16 at LDS bytes 32 (gq + 8 i) ..
-        // an empty slot (the cache's first row was loaded) is written as zeros:
-        // its P is 0, but 0 times a non-finite value would not be
-        uint8_t *dst = rows + gr * kRowBytes + 32 * gq;
-#pragma unroll
-        for (int i = 0; i < NV; ++i) {
-          if (i < NV - 1 || gq < 4) {
-            const u32x4 x = v_ok ? v[i] : u32x4{0, 0, 0, 0};
-            *reinterpret_cast<bf16x8 *>(dst + 256 * i) = fp8x8_to_bf16x8(x[0], x[1]);
-            *reinterpret_cast<bf16x8 *>(dst + 256 * i + 16) = fp8x8_to_bf16x8(x[2], x[3]);
-          }
-        }
-        if (gq == 0) lscale[gr] = v_sc;
-      } else {
-        uint8_t *dst = rows + gr * kRowBytes + 16 * gq;
-        if (__ballot(!v_ok))   // (only a split's last step has empty slots)
-#pragma unroll
-          for (int i = 0; i < NV; ++i) v[i] = v_ok ? v[i] : u32x4{0, 0, 0, 0};
-#pragma unroll
-        for (int i = 0; i < NV; ++i) *reinterpret_cast<u32x4 *>(dst + 128 * i) = v[i];
-      }
-      if (gq == 0) lvalid[gr] = v_ok ? 1 : 0;
-    }
-    __syncthreads();
-    load_rows(step + 1);   // past the split's end: empty slots (the cache's first row, unused)
-
-    // QK^T: 16 heads x rows 32 wr + 16 nt + l16
-    float z[2][4];
-#pragma unroll
-    for (int nt = 0; nt < 2; ++nt) {
-      const int row = 32 * wr + 16 * nt + l16;
-      const uint8_t *rp = rows + row * kRowBytes + 16 * g4;
-      f32x4 sacc = {0, 0, 0, 0};
-      // row operands read two MFMAs ahead (the scheduling barriers keep the
-      // reads from being hoisted further, which would not fit the registers)
-      auto qk_read = [&](int ks) { return as_bf16x8(*reinterpret_cast<const u32x4 *>(rp + 64 * ks)); };
-      bf16x8 br[2] = {qk_read(0), qk_read(1)};
-#pragma unroll
-      for (int ks = 0; ks < kW / 32; ++ks) {
-        const bf16x8 b = br[ks & 1];
-        if (ks + 2 < kW / 32) br[ks & 1] = qk_read(ks + 2);
-        sacc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qa[ks], b, sacc, 0, 0, 0);
-        __builtin_amdgcn_sched_barrier(0);
-      }
-      const bool valid = lvalid[row] != 0;
-      const float rs = F8 ? lscale[row] : 1.0f;
-#pragma unroll
-      for (int i = 0; i < 4; ++i) z[nt][i] = valid ? (F8 ? sacc[i] * rs : sacc[i]) * a.scale_log2 : -INFINITY;
-    }
-    float mx[4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) mx[i] = row16_max(fmaxf(z[0][i], z[1][i]));
-    if (l16 == 0)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) red[hg][0][wr][4 * g4 + i] = mx[i];
-    __syncthreads();
-
-    // lazy reference maximum (kSlack)
-    float alpha[4], ps[4];
-    bool moved = false;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int h = 4 * g4 + i;
-      const float tm = fmaxf(red[hg][0][0][h], red[hg][0][1][h]);
-      const bool grow = tm > m_run[i] + kSlack;
-      moved |= grow;
-      const float m_new = grow ? tm : m_run[i];
-      const float mu = m_new == -INFINITY ? 0.0f : m_new;
-      alpha[i] = grow ? fast_exp2(m_run[i] - mu) : 1.0f;
-      float pr[2], pv[2];
-#pragma unroll
-      for (int nt = 0; nt < 2; ++nt) {
-        const int row = 32 * wr + 16 * nt + l16;
-        pr[nt] = fast_exp2(z[nt][i] - mu);
-        pv[nt] = F8 ? pr[nt] * lscale[row] : pr[nt];   // weight of the decoded (unscaled) row
-      }
-      uint32_t hi, lo;
-      split_hi_lo(pv[0], pv[1], hi, lo);
-      const int r0 = 32 * wr + l16;   // rows r0 and r0 + 16
-      my_p[h * kWideStep + r0] = (uint16_t)hi;
-      my_p[h * kWideStep + r0 + 16] = (uint16_t)(hi >> 16);
-      my_p[kHG * kWideStep + h * kWideStep + r0] = (uint16_t)lo;
-      my_p[kHG * kWideStep + h * kWideStep + r0 + 16] = (uint16_t)(lo >> 16);
-      ps[i] = row16_sum(pr[0] + pr[1]);
-      m_run[i] = m_new;
-    }
-    if (l16 == 0)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) red[hg][1][wr][4 * g4 + i] = ps[i];
-    __syncthreads();
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int h = 4 * g4 + i;
-      l_run[i] = l_run[i] * alpha[i] + (red[hg][1][0][h] + red[hg][1][1][h]);
-    }
-    if (step > 0 && __ballot(moved))   // (before the first step o is 0)
-#pragma unroll
-      for (int nt = 0; nt < NT; ++nt)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) o[nt][i] *= alpha[i];
-
-    // PV: rows 32 ks2 + 8 g4 + e, columns 256 wr + 16 nt + l16; the V operand
-    // comes from two transposed LDS reads of 4 rows each
-#pragma unroll
-    for (int ks2 = 0; ks2 < kWideStep / 32; ++ks2) {
-      const bf16x8 ahi = as_bf16x8(*reinterpret_cast<const u32x4 *>(&my_p[l16 * kWideStep + 32 * ks2 + 8 * g4]));
-      const bf16x8 alo = as_bf16x8(
-          *reinterpret_cast<const u32x4 *>(&my_p[kHG * kWideStep + l16 * kWideStep + 32 * ks2 + 8 * g4]));
-      const uint8_t *vb = rows + (32 * ks2 + 8 * g4 + (l16 >> 2)) * kRowBytes + (256 * wr + 4 * (l16 & 3)) * 2;
-      auto pv_read = [&](int nt) {
-        const i16x4 v0 = lds_read_tr(vb + 32 * nt);
-        const i16x4 v1 = lds_read_tr(vb + 4 * kRowBytes + 32 * nt);
-        return __builtin_bit_cast(bf16x8, (__attribute__((__vector_size__(8 * sizeof(short)))) short){
-                                              v0[0], v0[1], v0[2], v0[3], v1[0], v1[1], v1[2], v1[3]});
-      };
-      bf16x8 vr[2] = {pv_read(0), pv_read(1)};   // V operands one tile ahead
-#pragma unroll
-      for (int nt = 0; nt < NT; ++nt) {
-        const bf16x8 b = vr[nt & 1];
-        if (nt + 2 < NT) vr[nt & 1] = pv_read(nt + 2);
-        o[nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ahi, b, o[nt], 0, 0, 0);
-        o[nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(alo, b, o[nt], 0, 0, 0);
-        __builtin_amdgcn_sched_barrier(0);
-      }
-    }
-    __syncthreads();
-  }
-
-  // epilogue: lane holds heads h0 + 4 g4 + i, columns 256 wr + 16 nt + l16
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int head = h0 + 4 * g4 + i;
-    if (!SPLIT) {
-      const float inv = l_run[i] > 0.0f ? 1.0f / l_run[i] : 0.0f;
-      float *orow = a.out + ((int64_t)qi * H + head) * kL + 256 * wr + l16;
-#pragma unroll
-      for (int nt = 0; nt < NT; ++nt) orow[16 * nt] = o[nt][i] * inv;
-      if (wr == 0 && l16 == 0 && a.lse)
-        a.lse[(int64_t)qi * H + head] = l_run[i] > 0.0f ? (m_run[i] + log2f(l_run[i])) * kLn2 : -INFINITY;
-    } else {
-      const int64_t base = ((int64_t)(qi * a.splits + sp) * H + head);
-      float *orow = a.part_o + base * kL + 256 * wr + l16;
-#pragma unroll
-      for (int nt = 0; nt < NT; ++nt) orow[16 * nt] = o[nt][i];
-      if (wr == 0 && l16 == 0) {
-        a.part_ml[base * 2 + 0] = m_run[i];
-        a.part_ml[base * 2 + 1] = l_run[i];
-      }
-    }
-  }
-}
-
-// Many queries over bf16 rows (prefill chunks, decode windows): a workgroup of
+// The 64-head kernel (prefill chunks, decode windows; bf16 or fp8 rows): a workgroup of
 // four wavefronts owns one query, a block of 64 heads and a split of the index
 // slots, and wavefront w owns heads 16 w .. 16 w + 15 of the block for the
 // whole split, so its softmax needs no other wavefront.  Per 32-slot step the
@@ -660,13 +438,30 @@ __global__ __launch_bounds__(kWideThreads) void attend_wide_kernel(AttArgs a) {
 //   PV   : A = P exactly as the lane holds it (K = its 8 rows, bf16 hi + lo),
 //          B = V read transposed from LDS in the same row order (two 4-row
 //          reads), 32 tiles of 16 columns.
+// fp8 rows (e4m3fn bytes and a float32 scale per token) are copied as they are
+// stored, half the bytes, into a staging area inside each wavefront's part of
+// the next step's image and converted to bf16 there at the end of the step
+// (exactly: every e4m3fn value is a bf16 value); the scales multiply the scores
+// and the weights of P instead of the rows.
 constexpr int kW4Step = 32;                               // rows per step
 constexpr int kW4Threads = 256;
 constexpr int kW4RowB = kW * 2;                           // 1152 bytes per row, no padding
 constexpr int kW4Chunks = kW4RowB / 16;                   // 72
 constexpr int kW4PerThread = kW4Step * kW4Chunks / kW4Threads;   // 9 chunk copies per thread and step
 constexpr int kW4BufB = kW4Step * kW4RowB;                // 36864
-constexpr size_t kW4LdsBytes = 2 * (size_t)kW4BufB;       // two buffers: 73728
+// fp8 rows: a step's 32 row scales follow its bf16 image in the buffer
+constexpr int kW4ScaleOfs = kW4BufB;
+template <bool F8>
+constexpr int kW4BufStride = kW4BufB + (F8 ? 4 * kW4Step : 0);
+template <bool F8>
+constexpr size_t kW4LdsBytes = 2 * (size_t)kW4BufStride<F8>;   // two buffers: 73728 (+ 256)
+// fp8 rows (576 bytes, 36 chunks): wavefront w copies its rows 8 w .. 8 w + 7
+// (288 chunks) into the second half of their bf16 image (bytes 4608 ..), five
+// instructions, the last for 32 lanes
+constexpr int kW4F8Chunks = kW / 16;                      // 36
+constexpr int kW4F8WaveChunks = 8 * kW4F8Chunks;          // 288
+constexpr int kW4F8Copies = (kW4F8WaveChunks + 63) / 64;  // 5
+constexpr int kW4F8Stage = 8 * kW4RowB / 2;               // 4608: staging offset in the wavefront's 9216 bytes
 static_assert(kW4Step * kW4Chunks == kW4PerThread * kW4Threads, "whole chunk copies per thread");
 constexpr int kW4QkAhead = 2;   // row operands in flight ahead of the QK^T MFMAs
 constexpr int kW4PvAhead = 2;   // V operands in flight ahead of the PV MFMAs
@@ -714,7 +509,7 @@ __device__ __forceinline__ void copy16_to_lds(const uint8_t *src, uint8_t *lds) 
   asm volatile("s_nop 0\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(src), "{m0}"(m0) : "memory");
 }
 
-template <bool SPLIT>
+template <bool SPLIT, bool F8>
 __global__ __launch_bounds__(kW4Threads, 2) void attend_w4_kernel(AttArgs a) {
   extern __shared__ __align__(16) uint8_t w4lds[];
   const int H = a.n_heads;
@@ -753,18 +548,34 @@ __global__ __launch_bounds__(kW4Threads, 2) void attend_w4_kernel(AttArgs a) {
   // starts in row 8 wave + (64 u) / 72 at slot (64 u) % 72, so a lane's row is
   // that one or the next; the eight row addresses are read from their lanes
   // into scalar registers once per step (no lane exchange through LDS).
+  // fp8 rows: a lane's 16 bytes are chunk e % 36 of the wavefront's row e / 36,
+  // e = 64 i + l, for instruction i; the rows' scales are loaded by lanes 0..31
+  // (returned, 0 for an empty slot) and stored with the converted rows.
   auto issue_copies = [&](int tok, uint8_t *buf) {
     int slot;
     const int64_t blk = cache_block(a.latent, seq, tok >= 0 ? tok : 0, slot);
     const uint8_t *rp = tok >= 0 ? cache_row(a.latent, blk, slot) : a.latent.rows;
     const uint64_t rp64 = reinterpret_cast<uint64_t>(rp);
-    uint64_t row_addr[9];
+    uint64_t row_addr[10];
 #pragma unroll
     for (int k = 0; k < 8; ++k)
       row_addr[k] = ((uint64_t)(uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(rp64 >> 32), 8 * wave + k) << 32) |
                     (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)rp64, 8 * wave + k);
-    row_addr[8] = row_addr[7];   // (never selected: the last instruction ends with its row)
+    row_addr[8] = row_addr[9] = row_addr[7];   // (never selected: past the wavefront's last row)
     const int l = fresh_lane();
+    if (F8) {
+#pragma unroll
+      for (int i = 0; i < kW4F8Copies; ++i) {
+        const int e = 64 * i + l;
+        const int k0 = (64 * i) / kW4F8Chunks;
+        const int k = e / kW4F8Chunks, c = e - kW4F8Chunks * k;
+        const uint64_t base = k == k0 ? row_addr[k0] : k == k0 + 1 ? row_addr[k0 + 1] : row_addr[k0 + 2];
+        if (e < kW4F8WaveChunks)
+          copy16_to_lds(reinterpret_cast<const uint8_t *>(base) + 16 * c,
+                        buf + 8 * kW4RowB * wave + kW4F8Stage + 1024 * i);
+      }
+      return (tok >= 0 && lane < kW4Step) ? a.latent.scale[blk * a.latent.scale_block_stride + slot] : 0.0f;
+    }
 #pragma unroll
     for (int u = 0; u < kW4PerThread; ++u) {
       const int k0 = (64 * u) / kW4Chunks, b0 = (64 * u) % kW4Chunks;
@@ -776,6 +587,36 @@ __global__ __launch_bounds__(kW4Threads, 2) void attend_w4_kernel(AttArgs a) {
       const uint8_t *src = reinterpret_cast<const uint8_t *>(base) + 16 * (slot_in_row ^ h);
       copy16_to_lds(src, buf + 1024 * (kW4PerThread * wave + u));
     }
+    return 0.0f;
+  };
+  // fp8 rows, after the wavefront's copies have landed: its eight rows are read
+  // from the staging area into registers, then written as bf16 (exact) into the
+  // swizzled image (empty rows as zeros); lanes 0..31 of wavefront 0 store the
+  // step's row scales.
+  auto convert_rows = [&](uint32_t valid, float rscale, uint8_t *buf) {
+    const int l = fresh_lane();
+    u32x4 raw[kW4F8Copies];
+#pragma unroll
+    for (int i = 0; i < kW4F8Copies; ++i)
+      raw[i] = 64 * i + l < kW4F8WaveChunks
+                   ? *reinterpret_cast<const u32x4 *>(buf + 8 * kW4RowB * wave + kW4F8Stage + 1024 * i + 16 * l)
+                   : u32x4{0, 0, 0, 0};
+    __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0): every staging read done before the image is written
+#pragma unroll
+    for (int i = 0; i < kW4F8Copies; ++i) {
+      const int e = 64 * i + l;
+      if (e < kW4F8WaveChunks) {
+        const int k = e / kW4F8Chunks, c = e - kW4F8Chunks * k;
+        const int r = 8 * wave + k;
+        const bool ok = (valid >> r) & 1u;
+        const u32x4 x = ok ? raw[i] : u32x4{0, 0, 0, 0};
+        const int h = w4_swz(r);
+        uint8_t *row = buf + kW4RowB * r;
+        *reinterpret_cast<bf16x8 *>(row + 16 * ((2 * c) ^ h)) = fp8x8_to_bf16x8(x[0], x[1]);
+        *reinterpret_cast<bf16x8 *>(row + 16 * ((2 * c + 1) ^ h)) = fp8x8_to_bf16x8(x[2], x[3]);
+      }
+    }
+    if (wave == 0 && l < kW4Step) reinterpret_cast<float *>(buf + kW4ScaleOfs)[l] = rscale;
   };
   // After a wavefront's copies have landed: its entries of invalid rows become
   // zeros (their weight is 0, but 0 times a non-finite value would not be).
@@ -790,7 +631,8 @@ __global__ __launch_bounds__(kW4Threads, 2) void attend_w4_kernel(AttArgs a) {
   // first step's copies, then q (head h0 + l16, dims 8 g4 + 32 ks + [0, 8))
   int tok = step_token(0);
   uint32_t valid = (uint32_t)__ballot(tok >= 0);
-  if (nsteps > 0) issue_copies(tok, w4lds);
+  float rs_first = 0.0f;
+  if (nsteps > 0) rs_first = issue_copies(tok, w4lds);
   bf16x8 qa[kW / 32];
   {
     const uint16_t *qr = a.q + ((int64_t)qi * H + h0 + l16) * kW + 8 * g4;
@@ -799,7 +641,11 @@ __global__ __launch_bounds__(kW4Threads, 2) void attend_w4_kernel(AttArgs a) {
   }
   int tok_next = step_token(1);
   __builtin_amdgcn_s_waitcnt(0);
-  if (valid != 0xFFFFFFFFu) clear_invalid(valid, w4lds);
+  if (F8) {
+    if (nsteps > 0) convert_rows(valid, rs_first, w4lds);
+  } else if (valid != 0xFFFFFFFFu) {
+    clear_invalid(valid, w4lds);
+  }
   __syncthreads();
 
   float m_run = -INFINITY, l_run = 0.0f;   // head l16: reference maximum, this lane's partial sum
@@ -829,12 +675,13 @@ __global__ __launch_bounds__(kW4Threads, 2) void attend_w4_kernel(AttArgs a) {
   for (int st = 0; st < nsteps; ++st) {
     int qk_off[2], pv_off[4];
     lds_offsets(qk_off, pv_off);
-    uint8_t *cur = w4lds + (st & 1) * kW4BufB;
-    uint8_t *nxt = w4lds + ((st + 1) & 1) * kW4BufB;
+    uint8_t *cur = w4lds + (st & 1) * kW4BufStride<F8>;
+    uint8_t *nxt = w4lds + ((st + 1) & 1) * kW4BufStride<F8>;
     // next step's copies into the other buffer (read by no one since the barrier)
     const uint32_t valid_next = (uint32_t)__ballot(tok_next >= 0);
     const bool more = st + 1 < nsteps;
-    if (more) issue_copies(tok_next, nxt);
+    float rs_next = 0.0f;
+    if (more) rs_next = issue_copies(tok_next, nxt);
     const int tok_after = step_token(st + 2);
 
     // QK^T: D[row 16 t + 4 g4 + i][head l16].  The two row tiles alternate
@@ -858,6 +705,13 @@ __global__ __launch_bounds__(kW4Threads, 2) void attend_w4_kernel(AttArgs a) {
         __builtin_amdgcn_sched_barrier(0);
       }
     }
+    // fp8 rows: the score of the decoded row is its scale times the product with
+    // the stored bytes (row scales of rows 16 t + 4 g4 + i)
+    f32x4 rsc[2] = {f32x4{1, 1, 1, 1}, f32x4{1, 1, 1, 1}};
+    if (F8) {
+#pragma unroll
+      for (int t = 0; t < 2; ++t) rsc[t] = *reinterpret_cast<const f32x4 *>(cur + kW4ScaleOfs + 4 * (16 * t + 4 * g4));
+    }
     float z[2][4];
     float mx = -INFINITY;
 #pragma unroll
@@ -865,7 +719,7 @@ __global__ __launch_bounds__(kW4Threads, 2) void attend_w4_kernel(AttArgs a) {
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int r = 16 * t + 4 * g4 + i;
-        z[t][i] = ((valid >> r) & 1u) ? acc[t][i] * a.scale_log2 : -INFINITY;
+        z[t][i] = ((valid >> r) & 1u) ? (F8 ? acc[t][i] * rsc[t][i] : acc[t][i]) * a.scale_log2 : -INFINITY;
         mx = fmaxf(mx, z[t][i]);
       }
     mx = max_xor32(max_xor16(mx));
@@ -895,7 +749,14 @@ __global__ __launch_bounds__(kW4Threads, 2) void attend_w4_kernel(AttArgs a) {
 #pragma unroll
         for (int i = 0; i < 4; ++i) o[nt][i] *= ao[i];
     }
-    // P as the PV A operand: k = 8 g4 + e is row 4 g4 + e (e < 4) or 16 + 4 g4 + e - 4
+    // P as the PV A operand: k = 8 g4 + e is row 4 g4 + e (e < 4) or 16 + 4 g4 + e - 4;
+    // fp8 rows weigh the stored bytes by P times the row scale
+    if (F8) {
+#pragma unroll
+      for (int t = 0; t < 2; ++t)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) p[t][i] *= rsc[t][i];
+    }
     uint32_t ph[4], pl[4];
     split_hi_lo(p[0][0], p[0][1], ph[0], pl[0]);
     split_hi_lo(p[0][2], p[0][3], ph[1], pl[1]);
@@ -929,7 +790,11 @@ __global__ __launch_bounds__(kW4Threads, 2) void attend_w4_kernel(AttArgs a) {
     // the next step's rows have landed (this wavefront's copies), invalid ones
     // cleared, and every wavefront is done with this buffer before it is refilled
     __builtin_amdgcn_s_waitcnt(0);
-    if (more && valid_next != 0xFFFFFFFFu) clear_invalid(valid_next, nxt);
+    if (F8) {
+      if (more) convert_rows(valid_next, rs_next, nxt);
+    } else if (more && valid_next != 0xFFFFFFFFu) {
+      clear_invalid(valid_next, nxt);
+    }
     valid = valid_next;
     tok_next = tok_after;
     __syncthreads();
@@ -1217,17 +1082,21 @@ hipError_t launch_attend(float *out, float *lse, const void *q, int dt, const Ca
   a.pairs = n_q * plan.splits;
   a.scale_log2 = scale * kLog2e;
   uint8_t *ws = static_cast<uint8_t *>(workspace);
-  if (plan.wide && dt != kFP8) {
-    // the 64-head bf16 kernel takes 72 KB of dynamic LDS: allowed once per device (the current one)
+  if (plan.wide) {
+    // the 64-head kernel takes 72 KB of dynamic LDS: allowed once per device (the current one)
     static std::atomic<uint64_t> lds_set{0};
     int dev = 0;
     hipError_t de = hipGetDevice(&dev);
     if (de != hipSuccess) return de;
     const uint64_t bit = dev < 64 ? uint64_t(1) << dev : 0;
     if (!bit || !(lds_set.load(std::memory_order_acquire) & bit)) {
-      for (const void *f : {reinterpret_cast<const void *>(&attend_w4_kernel<true>),
-                            reinterpret_cast<const void *>(&attend_w4_kernel<false>)}) {
-        de = hipFuncSetAttribute(f, hipFuncAttributeMaxDynamicSharedMemorySize, (int)kW4LdsBytes);
+      const std::pair<const void *, size_t> fs[] = {
+          {reinterpret_cast<const void *>(&attend_w4_kernel<true, false>), kW4LdsBytes<false>},
+          {reinterpret_cast<const void *>(&attend_w4_kernel<false, false>), kW4LdsBytes<false>},
+          {reinterpret_cast<const void *>(&attend_w4_kernel<true, true>), kW4LdsBytes<true>},
+          {reinterpret_cast<const void *>(&attend_w4_kernel<false, true>), kW4LdsBytes<true>}};
+      for (const auto &f : fs) {
+        de = hipFuncSetAttribute(f.first, hipFuncAttributeMaxDynamicSharedMemorySize, (int)f.second);
         if (de != hipSuccess) return de;
       }
       lds_set.fetch_or(bit, std::memory_order_acq_rel);
@@ -1240,8 +1109,10 @@ hipError_t launch_attend(float *out, float *lse, const void *q, int dt, const Ca
 #define DSA_ATTEND(SP)                                                                                        \
   do {                                                                                                        \
     if (plan.wide) {                                                                                          \
-      if (f8) hipLaunchKernelGGL((attend_wide_kernel<SP, true>), wide_grid, dim3(kWideThreads), 0, stream, a); \
-      else hipLaunchKernelGGL((attend_w4_kernel<SP>), wide_grid, dim3(kW4Threads), kW4LdsBytes, stream, a);    \
+      if (f8) hipLaunchKernelGGL((attend_w4_kernel<SP, true>), wide_grid, dim3(kW4Threads), kW4LdsBytes<true>,   \
+                                 stream, a);                                                                  \
+      else hipLaunchKernelGGL((attend_w4_kernel<SP, false>), wide_grid, dim3(kW4Threads), kW4LdsBytes<false>,   \
+                              stream, a);                                                                     \
     } else {                                                                                                  \
       if (f8) hipLaunchKernelGGL((attend_bf16_kernel<SP, true>), grid, dim3(kAttThreads), 0, stream, a);       \
       else hipLaunchKernelGGL((attend_bf16_kernel<SP, false>), grid, dim3(kAttThreads), 0, stream, a);         \
