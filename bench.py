@@ -21,6 +21,7 @@ Prints one JSON line.
 from __future__ import annotations
 
 import argparse
+import dataclasses
 import json
 import os
 import sys
@@ -505,6 +506,18 @@ def main():
 
         t_pt = timed(ptopk, 10)
         t_pa = timed(pattend, 10)
+        # the same chunk over an fp8 latent cache (e4m3fn rows of the same bf16
+        # rows, one float32 scale per token), same kept indices
+        pp8 = inputs.make_problem(dataclasses.replace(wp, latent_dtype="e4m3fn"))
+        lat8 = device.upload(pp8).latent
+        del pp8
+
+        def pattend8():
+            dsa.mla_sparse_attend(pout, plse, dpp.q_mla, pp.q_mla_dtype, lat8, pp.kv_lora, pidx,
+                                  pp.softmax_scale, workspace=aws)
+
+        t_pa8 = timed(pattend8, 10)
+        del lat8
         mla_flops = 0
         for n in pp.q_len:
             kept = min(int(n), pp.topk)
@@ -514,7 +527,8 @@ def main():
                    "indexer_mfma_frac": round(flops / t_pi / 1e12 / BF16_PEAK_TFLOPS, 4),
                    "topk_ms": round(t_pt * 1e3, 3), "topk_launches": 10, "sparse_mla_ms": round(t_pa * 1e3, 3),
                    "sparse_mla_launches": 10,
-                   "sparse_mla_tflops": round(mla_flops / t_pa / 1e12, 1)}
+                   "sparse_mla_tflops": round(mla_flops / t_pa / 1e12, 1),
+                   "sparse_mla_fp8_latent_ms": round(t_pa8 * 1e3, 3)}
 
     # ------------------------------------------- multi-token decode window ---
     window = None
