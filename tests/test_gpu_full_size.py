@@ -7,6 +7,8 @@ index, every attention row).  The prefill chunk is too large for the fp64
 oracle to score every row in seconds, so sampled rows are checked against the
 oracle one by one, and properties that hold at any size are checked on every row.
 """
+import dataclasses
+
 import numpy as np
 import pytest
 import torch
@@ -109,6 +111,38 @@ def test_prefill_chunk_full_size_sampled():
                                         p.q_seq[srows], p.softmax_scale)
     worst = check_attention(out.cpu().numpy()[srows], lse.cpu().numpy()[srows], ref_o, ref_l, TOL[p.latent.dtype])
     print(f"  sampled rows {len(rows)} (indices), {len(srows)} (scores, attention); attention worst {worst:.3g}")
+
+
+def test_prefill_chunk_fp8_latent_attention_sampled():
+    """The 2048-query chunk's sparse MLA over an fp8 latent cache (the 64-head
+    kernel with fp8 rows, 64 steps per query): sampled rows against the oracle."""
+    wl = dataclasses.replace(inputs.PREFILL_64K, latent_dtype="e4m3fn")
+    print("case prefill_chunk_2048_at_64k, fp8 latent: full size, sampled rows", flush=True)
+    p = inputs.make_problem(wl)
+    dp = device.upload(p)
+    n_q, max_len, k = p.n_q, p.max_len, p.topk
+    scores = torch.empty(n_q, max_len, device="cuda")
+    dsa.dsa_index_scores(scores, dp.q_idx, p.q_idx_dtype, dp.w_idx, dp.keys, dp.q_len, p.idx_heads, max_len,
+                         q_seq=dp.q_seq)
+    idx = torch.empty(n_q, k, dtype=torch.int32, device="cuda")
+    ws = torch.zeros(dsa.dsa_topk_workspace_size(n_q, k, max_len), dtype=torch.uint8, device="cuda")
+    dsa.dsa_topk(idx, None, scores, dp.q_len, k, max_len, workspace=ws)
+    del scores
+    out = torch.empty(n_q, p.mla_heads, p.kv_lora, device="cuda")
+    lse = torch.empty(n_q, p.mla_heads, device="cuda")
+    wa = torch.zeros(max(dsa.mla_sparse_attend_workspace_size(n_q, p.mla_heads, p.kv_lora, k), 1),
+                     dtype=torch.uint8, device="cuda")
+    dsa.mla_sparse_attend(out, lse, dp.q_mla, p.q_mla_dtype, dp.latent, p.kv_lora, idx, p.softmax_scale,
+                          q_seq=dp.q_seq, workspace=wa)
+    torch.cuda.synchronize()
+    assert torch.isfinite(out).all().item() and torch.isfinite(lse).all().item()
+    g_idx = idx.cpu().numpy()
+    rng = np.random.default_rng(1)
+    rows = np.unique(np.concatenate([[0, n_q - 1], rng.choice(n_q, 14, replace=False)]))
+    ref_o, ref_l, _ = oracle.mla_attend(p.q_mla[rows], p.q_mla_dtype, p.latent, p.kv_lora, g_idx[rows],
+                                        p.q_seq[rows], p.softmax_scale)
+    worst = check_attention(out.cpu().numpy()[rows], lse.cpu().numpy()[rows], ref_o, ref_l, TOL[p.latent.dtype])
+    print(f"  sampled rows {len(rows)}; attention worst {worst:.3g}")
 
 
 @pytest.mark.parametrize("name", ["decode_128k_fp8_window4", "paged_decode_16x16k_32k_window4"])
