@@ -441,8 +441,17 @@ def main():
             K, N = (aw.d_nope, aw.kv_lora) if name == "q" else (aw.kv_lora, aw.d_v)
             flops = 2 * aw.n_q * aw.heads * K * N
             wbytes = aw.heads * K * N * 2
+            rows = aw.n_q * aw.heads
+            # algorithmic bytes: every operand read once, the result written once
+            # (q: bf16 q_nope and q_rope in, the bf16 576-wide query out; out: the
+            # fp32 attention output in, the fp32 projection out)
+            if name == "q":
+                abytes = wbytes + rows * (aw.d_nope + aw.rope) * 2 + rows * (aw.kv_lora + aw.rope) * 2
+            else:
+                abytes = wbytes + rows * aw.kv_lora * 4 + rows * aw.d_v * 4
             res[name] = {"us": round(t * 1e6, 2), "tflops": round(flops / t / 1e12, 1),
-                         "weight_GB_per_s": round(wbytes / t / 1e9, 1)}
+                         "weight_GB_per_s": round(wbytes / t / 1e9, 1), "bytes": int(abytes),
+                         "GB_per_s": round(abytes / t / 1e9, 1), "hbm_frac": round(abytes / t / 1e9 / HBM_PEAK_GBS, 4)}
         return {"queries": aw.n_q, "heads": aw.heads, "d_nope": aw.d_nope, "kv_lora": aw.kv_lora, "d_v": aw.d_v,
                 "q_absorb": res["q"], "out_proj": res["out"]}
 
