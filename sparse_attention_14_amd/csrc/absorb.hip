@@ -353,9 +353,15 @@ __global__ __launch_bounds__(256) void absorb_gemm_kernel(AbsorbArgs a) {
   typedef uint8_t BTile[kGmBK * kGmBS];
   ATile *la = reinterpret_cast<ATile *>(smem);
   BTile *lb = reinterpret_cast<BTile *>(smem + 2 * sizeof(ATile));
+  // When the (row block, head) pairs come in whole groups of 8, the nblk column
+  // blocks of one pair are workgroups b, b + 8, b + 16, ...: dispatched together
+  // on one XCD, so the A tile they share is read from memory once and then from
+  // that XCD's L2.  Otherwise consecutive workgroups take its column blocks.
   const int nblk = a.N / kGmBN;
-  const int nb = blockIdx.x % nblk;
-  const int rest = blockIdx.x / nblk;
+  const bool by_xcd = ((a.M + kGmBM - 1) / kGmBM) * a.H % 8 == 0;
+  const int b8 = blockIdx.x % 8, bq = blockIdx.x / 8;
+  const int nb = by_xcd ? bq % nblk : blockIdx.x % nblk;
+  const int rest = by_xcd ? b8 + 8 * (bq / nblk) : blockIdx.x / nblk;
   const int h = rest % a.H;
   const int m0 = (rest / a.H) * kGmBM;
   const int n0 = nb * kGmBN;
