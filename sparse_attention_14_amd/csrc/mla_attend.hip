@@ -504,6 +504,13 @@ __device__ __forceinline__ float sum_xor32(float x) {
 // wait for every copy in flight (the next step's included) before the first
 // read of the current step.  The caller waits for its copies (s_waitcnt
 // vmcnt) before their buffer is read.
+// Waits for every vector-memory operation of the wavefront (its copies
+// included), and keeps the compiler from moving memory accesses across the wait.
+__device__ __forceinline__ void wait_copies() {
+  __builtin_amdgcn_s_waitcnt(0);
+  asm volatile("" ::: "memory");
+}
+
 __device__ __forceinline__ void copy16_to_lds(const uint8_t *src, uint8_t *lds) {
   const uint32_t m0 = (uint32_t)reinterpret_cast<uintptr_t>((__attribute__((address_space(3))) uint8_t *)lds);
   asm volatile("s_nop 0\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(src), "{m0}"(m0) : "memory");
@@ -602,6 +609,7 @@ __global__ __launch_bounds__(kW4Threads, 2) void attend_w4_kernel(AttArgs a) {
                    ? *reinterpret_cast<const u32x4 *>(buf + 8 * kW4RowB * wave + kW4F8Stage + 1024 * i + 16 * l)
                    : u32x4{0, 0, 0, 0};
     __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0): every staging read done before the image is written
+    asm volatile("" ::: "memory");
 #pragma unroll
     for (int i = 0; i < kW4F8Copies; ++i) {
       const int e = 64 * i + l;
@@ -640,7 +648,7 @@ __global__ __launch_bounds__(kW4Threads, 2) void attend_w4_kernel(AttArgs a) {
     for (int ks = 0; ks < kW / 32; ++ks) qa[ks] = as_bf16x8(load16(qr + 32 * ks));
   }
   int tok_next = step_token(1);
-  __builtin_amdgcn_s_waitcnt(0);
+  wait_copies();
   if (F8) {
     if (nsteps > 0) convert_rows(valid, rs_first, w4lds);
   } else if (valid != 0xFFFFFFFFu) {
@@ -789,7 +797,7 @@ __global__ __launch_bounds__(kW4Threads, 2) void attend_w4_kernel(AttArgs a) {
 
     // the next step's rows have landed (this wavefront's copies), invalid ones
     // cleared, and every wavefront is done with this buffer before it is refilled
-    __builtin_amdgcn_s_waitcnt(0);
+    wait_copies();
     if (F8) {
       if (more) convert_rows(valid_next, rs_next, nxt);
     } else if (more && valid_next != 0xFFFFFFFFu) {
