@@ -88,6 +88,48 @@ __device__ __forceinline__ u32x4 load16_nt(const void *p) {
   return __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(p));
 }
 
+// Direct-to-LDS copies (global_load_lds): the bytes go from memory into LDS
+// without passing through registers.  One instruction: lane l's 16 (or 4) bytes
+// land at lds + 16 l (4 l).  Issued as assembly so that the compiler does not
+// order later LDS reads behind them: it cannot tell which LDS bytes a copy
+// writes and would otherwise make every LDS read wait for every copy in flight
+// (the next step's included).  The caller waits for its copies itself
+// (wait_copies, wait_vm) before their bytes are read.
+__device__ __forceinline__ uint32_t lds_address(const void *lds) {
+  return (uint32_t)reinterpret_cast<uintptr_t>((__attribute__((address_space(3))) const uint8_t *)lds);
+}
+__device__ __forceinline__ void copy16_to_lds(const uint8_t *src, uint8_t *lds) {
+  asm volatile("s_nop 0\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(src), "{m0}"(lds_address(lds)) : "memory");
+}
+// The same from a wavefront-uniform base plus a 32-bit lane offset.
+__device__ __forceinline__ void copy16_to_lds(const uint8_t *base, uint32_t off, uint8_t *lds) {
+  asm volatile("s_nop 0\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(off), "s"(base), "{m0}"(lds_address(lds))
+               : "memory");
+}
+__device__ __forceinline__ void copy4_to_lds(const uint8_t *base, uint32_t off, uint8_t *lds) {
+  asm volatile("s_nop 0\n\tglobal_load_lds_dword %0, %1" ::"v"(off), "s"(base), "{m0}"(lds_address(lds))
+               : "memory");
+}
+
+// Waits for every vector-memory operation of the wavefront (its copies
+// included), and keeps the compiler from moving memory accesses across the wait.
+__device__ __forceinline__ void wait_copies() {
+  __builtin_amdgcn_s_waitcnt(0);
+  asm volatile("" ::: "memory");
+}
+
+// Waits until at most N vector-memory operations of the wavefront are in
+// flight, also as a compiler memory barrier.  Loads and copies complete in the
+// order they were issued, so the copies issued more than N such operations ago
+// are then in LDS; stores may complete in any order and are not counted by
+// callers (a store in flight only makes the wait longer).
+template <int N>
+__device__ __forceinline__ void wait_vm() {
+  static_assert(N >= 0 && N < 64, "vmcnt is six bits");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+  asm volatile("" ::: "memory");
+}
+
 // Agent-scope release/acquire around the "last workgroup finishes" handshake.
 __device__ __forceinline__ void fence_release_agent() { __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent"); }
 __device__ __forceinline__ void fence_acquire_agent() { __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent"); }

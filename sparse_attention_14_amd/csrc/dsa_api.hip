@@ -123,7 +123,7 @@ struct StepLayout {
 // grid (batch, or batch / 2 when pairs of queries share key loads); the bound
 // area is sized for either, so the total does not depend on it.
 StepLayout step_layout(int32_t batch, int32_t max_len, int32_t k, int32_t mla_heads, int32_t kv_lora,
-                       int latent_dt, int width, int32_t window = 1, int32_t score_rows = 0) {
+                       int latent_dt, int width, int32_t window = 1, int32_t score_rows = 0, bool pair = false) {
   StepLayout L{};
   L.ld = ((int64_t)max_len + 63) / 64 * 64;
   L.tp = plan_topk(batch, k, max_len);
@@ -133,9 +133,9 @@ StepLayout step_layout(int32_t batch, int32_t max_len, int32_t k, int32_t mla_he
   off += round256((size_t)batch * L.ld * 4);
   L.off_idx = off;
   off += round256((size_t)batch * k * 4);
-  L.n_bounds = score_groups_per_row(score_rows > 0 ? score_rows : batch, max_len);
+  L.n_bounds = score_groups_per_row(score_rows > 0 ? score_rows : batch, max_len, pair);
   int most = score_groups_per_row(batch, max_len);
-  if (window % 2 == 0) most = std::max(most, score_groups_per_row(batch / 2, max_len));
+  if (window % 2 == 0) most = std::max(most, score_groups_per_row(batch / 2, max_len, true));
   L.off_bounds = off;
   off += round256((size_t)batch * most * 4);
   L.off_topk = off;
@@ -274,9 +274,10 @@ dsa_status decode_impl(float *out, float *lse, const void *q_idx, dsa_dtype q_id
   // lengths itself and hands their visible counts on; f32: a separate kernel
   const bool rows_in_scores = window > 1 && q_idx_dtype != DSA_F32;
   // The workspace size query assumes the bf16 latent plan, which is the larger one.
-  const StepLayout L = step_layout(n_q, max_len, k, mla_heads, kv_lora, kBF16, 576, window, score_rows);
+  const bool pair = qw == 2;
+  const StepLayout L = step_layout(n_q, max_len, k, mla_heads, kv_lora, kBF16, 576, window, score_rows, pair);
   const StepLayout A = step_layout(n_q, max_len, k, mla_heads, kv_lora, q_mla_dtype, latent->width, window,
-                                   score_rows);
+                                   score_rows, pair);
   if (!workspace || workspace_bytes < L.total) return DSA_ERR_WORKSPACE_TOO_SMALL;
   hipStream_t st = static_cast<hipStream_t>(stream);
   uint8_t *ws = static_cast<uint8_t *>(workspace);
@@ -311,7 +312,7 @@ dsa_status decode_impl(float *out, float *lse, const void *q_idx, dsa_dtype q_id
                                 q_len, n_q, idx_heads, max_len, ScoreBounds{bounds, k}, st, qw);
   if (e != hipSuccess) return DSA_ERR_DEVICE;
   e = launch_topk(idx, nullptr, scores, ld, q_len, L.tp, ws_topk, bounds, L.n_bounds,
-                  score_group_tokens(score_rows, max_len), st);
+                  score_group_tokens(score_rows, max_len, pair), st);
   if (e != hipSuccess) return DSA_ERR_DEVICE;
   e = launch_attend(out, lse, q_mla, attend_dtype(q_mla_dtype, latent), to_dev(latent), kv_lora, idx, k, q_seq,
                     window > 1 ? (q_seq ? 0 : window) : seq_ident, n_q, mla_heads, softmax_scale, A.ap, ws_att, st);

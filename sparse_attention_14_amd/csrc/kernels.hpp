@@ -19,11 +19,11 @@ struct ScoreBounds {
   uint32_t *bounds;  // [n_q][score_groups_per_row()] or nullptr
   int topk;
 };
-// qw (1 or 2): rows 2 y and 2 y + 1 belong to one sequence when qw = 2 (bf16/fp8
-// keys, 128 wide, <= 32 heads): each key tile is read once for both (decode
-// windows).  n_q must be a multiple of qw.  Bound groups are then laid
-// out for a grid of n_q / qw workgroup rows: score_groups_per_row /
-// score_group_tokens take that row count.
+// qw (1 or 2): rows 2 y and 2 y + 1 belong to one sequence when qw = 2 (decode
+// windows only: window > 0; bf16/fp8 keys, 128 wide, <= 32 heads): each key
+// tile is read once for both.  n_q must be a multiple of qw.  Bound groups are
+// then laid out for a grid of n_q / qw workgroup rows: score_groups_per_row /
+// score_group_tokens take that row count and pair = true.
 // window > 0 (bf16 q, q_seq null, n_q a multiple of window, window a multiple
 // of qw): row i is query i % window of sequence i / window, q_len holds the
 // sequence lengths [n_q / window] and the row's visible count is
@@ -38,9 +38,10 @@ hipError_t launch_index_scores(float *scores, int64_t ld, const void *q, int q_d
 hipError_t launch_prefill_scores(float *scores, int64_t ld, const uint16_t *q, const float *w, const CacheDev &keys,
                                  const int32_t *q_seq, const int32_t *q_len, int n_q, int n_heads, int max_len,
                                  int block_shift, hipStream_t stream);
-int score_tiles_per_wave(int rows, int max_len);
-int score_groups_per_row(int rows, int max_len);
-int score_group_tokens(int rows, int max_len);
+// pair: the grid of the query-pair kernel (decode windows, qw = 2)
+int score_tiles_per_wave(int rows, int max_len, bool pair = false);
+int score_groups_per_row(int rows, int max_len, bool pair = false);
+int score_group_tokens(int rows, int max_len, bool pair = false);
 
 // ---- top-k ------------------------------------------------------------------
 struct TopkPlan {

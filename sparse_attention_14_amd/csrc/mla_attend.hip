@@ -498,24 +498,6 @@ __device__ __forceinline__ float sum_xor32(float x) {
   return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 
-// Waits for every vector-memory operation of the wavefront (its copies
-// included), and keeps the compiler from moving memory accesses across the wait.
-__device__ __forceinline__ void wait_copies() {
-  __builtin_amdgcn_s_waitcnt(0);
-  asm volatile("" ::: "memory");
-}
-
-// One global_load_lds_dwordx4: lane l's 16 bytes at src land at lds + 16 l.
-// Issued as assembly so that the compiler does not order later LDS reads
-// behind it: it cannot tell the two step buffers apart and would otherwise
-// wait for every copy in flight (the next step's included) before the first
-// read of the current step.  The caller waits for its copies (wait_copies)
-// before their buffer is read.
-__device__ __forceinline__ void copy16_to_lds(const uint8_t *src, uint8_t *lds) {
-  const uint32_t m0 = (uint32_t)reinterpret_cast<uintptr_t>((__attribute__((address_space(3))) uint8_t *)lds);
-  asm volatile("s_nop 0\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(src), "{m0}"(m0) : "memory");
-}
-
 template <bool SPLIT, bool F8>
 __global__ __launch_bounds__(kW4Threads, 2) void attend_w4_kernel(AttArgs a) {
   extern __shared__ __align__(16) uint8_t w4lds[];
