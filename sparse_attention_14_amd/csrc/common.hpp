@@ -129,6 +129,14 @@ __device__ __forceinline__ void wait_vm() {
   __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
   asm volatile("" ::: "memory");
 }
+// The same, and every LDS access of the wavefront done (so that a buffer it
+// has read can be handed to new copies).
+template <int N>
+__device__ __forceinline__ void wait_vm_lds() {
+  static_assert(N >= 0 && N < 64, "vmcnt is six bits");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4));
+  asm volatile("" ::: "memory");
+}
 
 // Agent-scope release/acquire around the "last workgroup finishes" handshake.
 __device__ __forceinline__ void fence_release_agent() { __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent"); }

@@ -346,7 +346,7 @@ __global__ __launch_bounds__(256) void scores_pair_kernel(float *__restrict__ sc
       slot[it] = t0 - bi[it] * keys.block_size;
       tlast[it] = n - 1 - t0;
     }
-    int blk[TPW < 8 ? 8 : TPW] = {};
+    int blk[(TPW + 7) / 8 * 8] = {};
     if (keys.table && active) {
       const int32_t *trow = keys.table + (int64_t)seq * keys.max_blocks;
 #pragma unroll
@@ -428,9 +428,10 @@ __global__ __launch_bounds__(256) void scores_pair_kernel(float *__restrict__ sc
       // copy groups issued after tile it's: tiles it+1 .. it+P-1 (those that exist)
       static_assert(P >= 1 && P <= 3, "up to two later copy groups");
       const int later = (TPW - 1 - it) < (P - 1) ? (TPW - 1 - it) : (P - 1);
-      if (later >= 2) wait_vm<2 * OPS>();
-      else if (later == 1) wait_vm<OPS>();
-      else wait_vm<0>();
+      // (and the reads of the previous tile done: its buffer takes the copies below)
+      if (later >= 2) wait_vm_lds<2 * OPS>();
+      else if (later == 1) wait_vm_lds<OPS>();
+      else wait_vm_lds<0>();
       const uint8_t *buf = stage + (it % NB) * BUFB;
       u32x4 raw[HALFC];
 #pragma unroll

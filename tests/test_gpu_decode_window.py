@@ -34,6 +34,9 @@ CASES = {
     "bf16_w8_tiny": S(inputs.DECODE_8K, name="w6", wid=506, batch=2, seq_len=(3, 3), window=8),
     "bf16_paged_w4_bounded": S(inputs.PAGED_DECODE_W4, name="w5", wid=505, batch=2, seq_len=(13000, 26000)),
     "fp8_latent8_w4": S(inputs.DECODE_128K_FP8_LAT8, name="w7", wid=507, batch=4, seq_len=(3000, 9000), window=4),
+    # windows of 2 and 6: query pairs that do not share a workgroup with another pair
+    "fp8_w6": S(inputs.DECODE_128K_FP8_W4, name="w9", wid=509, batch=2, seq_len=(5000, 12000), window=6),
+    "bf16_paged_w2": S(inputs.PAGED_DECODE_W4, name="w10", wid=510, batch=3, seq_len=(700, 20000), window=2),
     # fp32 indexer queries: the window rows come from their own kernel
     "f32_w3": S(inputs.TINY_FP32, name="w8", wid=508, batch=3, seq_len=(2, 900), window=3),
 }
@@ -74,7 +77,7 @@ def _aliased(cache: DeviceCache, row_seq: np.ndarray) -> DeviceCache:
                        block_table=table)
 
 
-@pytest.mark.parametrize("name", ["bf16_paged_w3", "bf16_paged_w4_bounded"])
+@pytest.mark.parametrize("name", ["bf16_paged_w3", "bf16_paged_w4_bounded", "bf16_paged_w2"])
 def test_decode_window_equals_single_token_steps(name):
     p = inputs.make_problem(CASES[name])
     dp = device.upload(p)
