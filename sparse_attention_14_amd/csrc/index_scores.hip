@@ -267,12 +267,11 @@ __global__ __launch_bounds__(256) void scores_mfma_kernel(float *__restrict__ sc
 //
 // The key tiles go from memory straight into LDS (direct-to-LDS copies, no
 // registers in between): each wavefront keeps P tiles in flight in stage
-// buffers of its own (P + 1 of them), and the head weights of the pair are read
-// from LDS in the epilogue.  This keeps the kernel under 168 registers, i.e.
-// three wavefronts per SIMD, which is what hides the latency of the per-tile
-// chain (LDS read, fp8 conversion, MFMA chain, epilogue).  Each 16-byte chunk
-// of the tile is converted and multiplied in turn, so the conversion of one
-// chunk overlaps the MFMAs of the previous one.
+// buffers of its own (P + 1 of them).  The head weights of the pair are read
+// from LDS in the epilogue, or held in registers when the stage buffers already
+// limit the CU to two workgroups.  Each 16-byte chunk of the tile is converted
+// and multiplied in turn, so the conversion of one chunk overlaps the MFMAs of
+// the previous one.
 //
 // Stage layout: tile row kk at kk * ROWB, its chunk c in slot c ^ (kk % CPR)
 // (against LDS bank conflicts when 32 lanes read 32 rows).  A copy writes 64
@@ -282,9 +281,10 @@ __global__ __launch_bounds__(256) void scores_mfma_kernel(float *__restrict__ sc
 // load them again).
 //
 // Waits: a wavefront waits for the copies of tile it (its own vmcnt) with the
-// later tiles' copies still in flight; the scores of tile it are stored after
-// the wait of tile it + 1, so that no store is pending between two copy groups
-// when the wait is taken.
+// later tiles' copies still in flight, counting copies only: a store issued
+// in between can only lengthen the wait.  The scores of tile it are stored
+// after the wait of tile it + 1, a whole tile before the next wait they could
+// lengthen.
 template <bool FP8, int TPW, int P>
 __global__ __launch_bounds__(256) void scores_pair_kernel(float *__restrict__ scores, int64_t ld,
                                                           const uint16_t *__restrict__ q, const float *__restrict__ w,
