@@ -37,6 +37,8 @@ CASES = {
     # windows of 2 and 6: query pairs that do not share a workgroup with another pair
     "fp8_w6": S(inputs.DECODE_128K_FP8_W4, name="w9", wid=509, batch=2, seq_len=(5000, 12000), window=6),
     "bf16_paged_w2": S(inputs.PAGED_DECODE_W4, name="w10", wid=510, batch=3, seq_len=(700, 20000), window=2),
+    # fewer indexer heads than the MFMA's 32 rows (zero q rows and weights in the pair kernel)
+    "fp8_w4_h20": S(inputs.DECODE_128K_FP8_W4, name="w11", wid=511, batch=2, seq_len=(3000, 7000), idx_heads=20),
     # fp32 indexer queries: the window rows come from their own kernel
     "f32_w3": S(inputs.TINY_FP32, name="w8", wid=508, batch=3, seq_len=(2, 900), window=3),
 }
