@@ -45,7 +45,8 @@ __device__ __forceinline__ uint16_t to_bf16_rne(float f) {
 }
 
 // Rope columns of the MLA query for rows [m0, m0 + rows) of head h, in 16-byte
-// chunks whose loads are all issued before the stores (R is a multiple of 8).
+// chunks whose loads are all issued before the (non-temporal) stores (R is a
+// multiple of 8).
 __device__ __forceinline__ void copy_rope(const AbsorbArgs &a, int h, int m0, int rows) {
   const int cpr = a.R / 8;
   const int nch = rows * cpr;
@@ -63,8 +64,9 @@ __device__ __forceinline__ void copy_rope(const AbsorbArgs &a, int h, int m0, in
       const int ch = base + (int)threadIdx.x + 256 * j;
       const int r = ch / cpr, c = ch - r * cpr;
       if (ch < nch && m0 + r < a.M)
-        *reinterpret_cast<u32x4 *>(static_cast<uint16_t *>(a.c) + ((int64_t)(m0 + r) * a.H + h) * a.ldc + a.N +
-                                   8 * c) = v[j];
+        __builtin_nontemporal_store(
+            v[j], reinterpret_cast<u32x4 *>(static_cast<uint16_t *>(a.c) + ((int64_t)(m0 + r) * a.H + h) * a.ldc +
+                                            a.N + 8 * c));
     }
   }
 }
@@ -483,8 +485,10 @@ __global__ __launch_bounds__(256) void absorb_gemm_kernel(AbsorbArgs a) {
       const int r = ch >> 4, cc = ch & 15;
       const int m = m0 + r;
       if (m < a.M)
-        *reinterpret_cast<u32x4 *>(static_cast<uint16_t *>(a.c) + ((int64_t)m * a.H + h) * a.ldc + n0 + 8 * cc) =
-            *reinterpret_cast<const u32x4 *>(lc + r * kGmCS + 16 * cc);
+        // written once and read by a later kernel: non-temporal (8 % faster at 2048 queries)
+        __builtin_nontemporal_store(
+            *reinterpret_cast<const u32x4 *>(lc + r * kGmCS + 16 * cc),
+            reinterpret_cast<u32x4 *>(static_cast<uint16_t *>(a.c) + ((int64_t)m * a.H + h) * a.ldc + n0 + 8 * cc));
     }
   } else {
 #pragma unroll
