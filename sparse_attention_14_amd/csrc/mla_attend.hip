@@ -801,7 +801,8 @@ __global__ __launch_bounds__(kW4Threads, 2) void attend_w4_kernel(AttArgs a) {
       const float inv = li > 0.0f ? 1.0f / li : 0.0f;
       float *orow = a.out + ((int64_t)qi * H + head) * kL + l16;
 #pragma unroll
-      for (int nt = 0; nt < kL / 16; ++nt) orow[16 * nt] = o[nt][i] * inv;
+      // (written once, read by a later kernel: non-temporal)
+      for (int nt = 0; nt < kL / 16; ++nt) __builtin_nontemporal_store(o[nt][i] * inv, &orow[16 * nt]);
       if (l16 == 0 && a.lse) a.lse[(int64_t)qi * H + head] = li > 0.0f ? (mi + log2f(li)) * kLn2 : -INFINITY;
     } else {
       const int64_t base = ((int64_t)(qi * a.splits + sp) * H + head);
