@@ -381,8 +381,9 @@ __global__ __launch_bounds__(256) void absorb_gemm_kernel(AbsorbArgs a) {
       const int kk = A_F32 ? 4 * (ch & 7) : 8 * (ch & 3);
       const int64_t off = (int64_t)(m0 + r) * arow + (int64_t)h * a.K + k0 + kk;
       const bool ok = m0 + r < a.M;
-      if (A_F32)
-        ra[j] = ok ? *reinterpret_cast<const u32x4 *>(static_cast<const float *>(a.a) + off) : u32x4{};
+      if (A_F32)   // (the fp32 attention output: every element read once, non-temporal)
+        ra[j] = ok ? __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(static_cast<const float *>(a.a) + off))
+                   : u32x4{};
       else
         ra[j] = ok ? *reinterpret_cast<const u32x4 *>(static_cast<const uint16_t *>(a.a) + off) : u32x4{};
     }
@@ -499,7 +500,8 @@ __global__ __launch_bounds__(256) void absorb_gemm_kernel(AbsorbArgs a) {
         if (m < a.M) {
 #pragma unroll
           for (int ct = 0; ct < 4; ++ct)
-            static_cast<float *>(a.c)[((int64_t)m * a.H + h) * a.ldc + n0 + wc + 16 * ct + l16] = acc[rt][ct][i];
+            __builtin_nontemporal_store(
+                acc[rt][ct][i], &static_cast<float *>(a.c)[((int64_t)m * a.H + h) * a.ldc + n0 + wc + 16 * ct + l16]);
         }
       }
     }
